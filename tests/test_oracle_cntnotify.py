@@ -1,0 +1,278 @@
+"""Pins for the CntNotify half of the oracle (CPU only).
+
+The pages' mode tables (tests/golden) fix which code does what; a restatement
+in terms of sets of bit positions and Python's unbounded integers fixes the
+arithmetic; the pages' worked examples fix the life cycle.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import handles
+from cross_core_barrier_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+M32 = 0xFFFFFFFF
+
+
+def _table(name):
+    rows = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                code, label, effect = line.split()
+                rows[int(code)] = (label, effect)
+    return rows
+
+
+RECORD = _table("cntnotify_record_modes.txt")
+WAIT = _table("cntnotify_wait_modes.txt")
+
+
+def _bits(x):
+    return {i for i in range(32) if (x >> i) & 1}
+
+
+def _from_bits(s):
+    return sum(1 << i for i in s)
+
+
+def _expected_record(effect, c, v):
+    if effect == "overwrite":
+        return v
+    if effect == "add":
+        return (c + v) % (1 << 32)
+    if effect == "bit_or":
+        return _from_bits(_bits(c) | _bits(v))
+    if effect == "bit_and":
+        return _from_bits(_bits(c) & _bits(v))
+    raise AssertionError(effect)
+
+
+def _expected_wait(cond, c, v):
+    if cond == "less":
+        return c < v
+    if cond == "equal":
+        return c == v
+    if cond == "greater":
+        return c > v
+    if cond == "greater_equal":
+        return c >= v
+    if cond == "mask_subset":
+        return _bits(v) <= _bits(c)
+    raise AssertionError(cond)
+
+
+EDGE = [0, 1, 2, 3, 15, 16, 0x7FFFFFFF, 0x80000000, 0x80000001, 0xFFFFFFFE, 0xFFFFFFFF, 0xDEADBEEF]
+
+
+def test_golden_tables_shape():
+    assert sorted(RECORD) == [0, 1, 2, 4]          # no record code 3
+    assert sorted(WAIT) == [0, 1, 2, 3, 4]
+
+
+@pytest.mark.parametrize("code", [0, 1, 2, 4])
+def test_record_exhaustive_4bit_and_edges(code):
+    effect = RECORD[code][1]
+    vals = list(range(16)) + EDGE
+    for c in vals:
+        for v in vals:
+            got, rc = oracle.cnt_record(c, code, v)
+            assert rc == 0
+            assert got == _expected_record(effect, c, v), (code, c, v)
+
+
+@pytest.mark.parametrize("code", [0, 1, 2, 3, 4])
+def test_wait_exhaustive_4bit_and_edges(code):
+    cond = WAIT[code][1]
+    vals = list(range(16)) + EDGE
+    for c in vals:
+        for v in vals:
+            holds, rc = oracle.cnt_wait_holds(c, code, v)
+            assert rc == 0
+            assert bool(holds) == _expected_wait(cond, c, v), (code, c, v)
+
+
+@pytest.mark.parametrize("code", [3, 5, 6, 7, -1, 8])
+def test_record_invalid_codes(code):
+    got, rc = oracle.cnt_record(9, code, 1)
+    assert rc == oracle.INVALID_VALUE and got == 9
+
+
+@pytest.mark.parametrize("code", [5, 6, 7, -1])
+def test_wait_invalid_codes(code):
+    _, rc = oracle.cnt_wait_holds(9, code, 1)
+    assert rc == oracle.INVALID_VALUE
+
+
+def test_identities():
+    for c in EDGE:
+        assert oracle.cnt_record(c, 1, 0)[0] == c          # ADD 0
+        assert oracle.cnt_record(c, 2, 0)[0] == c          # OR 0
+        assert oracle.cnt_record(c, 4, M32)[0] == c        # AND all-ones
+        assert oracle.cnt_wait_holds(c, 3, 0)[0] == 1      # GE 0 always
+        assert oracle.cnt_wait_holds(c, 4, 0)[0] == 1      # BITMASK 0 always
+        assert oracle.cnt_wait_holds(c, 0, 0)[0] == 0      # LESS 0 never (unsigned)
+        v, _ = oracle.cnt_record(0, 0, c)                  # SET v then EQUAL v
+        assert oracle.cnt_wait_holds(v, 1, c)[0] == 1
+
+
+def test_clear_only_after_release():
+    # CntNotify §3.3/§7: isClear zeroes the count after the wait is released.
+    assert oracle.cnt_wait_apply(5, 3, 5, 1) == (0, 1, 0)
+    assert oracle.cnt_wait_apply(5, 3, 6, 1) == (5, 0, 0)   # not released: no clear
+    assert oracle.cnt_wait_apply(5, 3, 5, 0) == (5, 1, 0)
+
+
+# --- worked examples (tests/golden/cntnotify_worked_examples.txt) ------------
+
+def _examples():
+    out = []
+    with open(os.path.join(GOLDEN, "cntnotify_worked_examples.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                name, ops, expect = [s.strip() for s in line.split("|")]
+                out.append((name, ops, expect))
+    return out
+
+
+def _run_model(ops):
+    m = handles.CntNotifyModel(capacity=4)
+    rc, h = m.create(0)
+    assert rc == handles.OK
+    outcomes = []
+    n_waits = 0
+    for op in ops.split(";"):
+        parts = op.split()
+        if parts[0] == "rec":
+            assert m.record(h, (int(parts[1]), int(parts[2]))) == handles.OK
+        elif parts[0] == "wait":
+            # A later wait on the same handle observes the earlier one's result.
+            if n_waits:
+                outcomes.append(m.close(h))
+            assert m.wait(h, tuple(int(p) for p in parts[1:5])) == handles.OK
+            n_waits += 1
+        elif parts[0] == "reset":
+            if n_waits:
+                outcomes.append(m.close(h))
+                n_waits = 0
+            assert m.reset(h) == handles.OK
+    if n_waits:
+        outcomes.append(m.close(h))
+    return outcomes, m.count[h]
+
+
+@pytest.mark.parametrize("name,ops,expect", _examples(), ids=[e[0] for e in _examples()])
+def test_worked_examples_model(name, ops, expect):
+    outcomes, final = _run_model(ops)
+    want = [s.strip() for s in expect.split(";")]
+    want_final = int([w for w in want if w.startswith("final=")][0].split("=")[1])
+    want_waits = [w for w in want if not w.startswith("final=")]
+    names = {handles.OK: "rel", handles.TIMEOUT: "timeout", None: "forever"}
+    assert [names[o] for o in outcomes] == want_waits
+    assert final == want_final
+
+
+@pytest.mark.parametrize("name,ops,expect", _examples(), ids=[e[0] for e in _examples()])
+def test_worked_examples_batch(name, ops, expect):
+    """The batch interpreter gives the same final count and, for each wait
+    that the sequential model releases, the same release flag."""
+    recs = [op.split() for op in ops.split(";")]
+    if any(r[0] == "reset" for r in recs):
+        pytest.skip("reset is a stream call, not a batch op")
+    val, meta = [], []
+    for r in recs:
+        if r[0] == "rec":
+            val.append(int(r[2]))
+            meta.append(int(r[1]))
+        else:
+            val.append(int(r[2]))
+            meta.append(int(r[1]) | (int(r[4]) << 3) | 0x80)
+    val = np.array(val, dtype=np.uint32)[:, None]
+    meta = np.array(meta, dtype=np.uint8)[:, None]
+    n_waits = sum(1 for r in recs if r[0] == "wait")
+    final, rel, rc = oracle.cnt_batch(val, meta, max(n_waits, 1))
+    want = [s.strip() for s in expect.split(";")]
+    want_final = int([w for w in want if w.startswith("final=")][0].split("=")[1])
+    assert rc == 0
+    assert int(final[0]) == want_final
+    flags = [int(rel[j, 0]) for j in range(n_waits)]
+    assert flags == [1 if w == "rel" else 0 for w in want if not w.startswith("final=")]
+
+
+# --- handle life cycle (error codes) ---------------------------------------------
+
+def test_model_error_codes():
+    m = handles.CntNotifyModel(capacity=2)
+    assert m.create(1) == (handles.INVALID_VALUE, None)        # §4.1 flag must be 0
+    rc, a = m.create(0)
+    rc2, b = m.create(0)
+    assert rc == rc2 == handles.OK and a != b
+    assert m.create(0) == (handles.RESOURCE_EXHAUSTED, None)   # §4.1 resources exhausted
+    assert m.record(a, None) == handles.NULL_POINTER           # §4.2
+    assert m.wait(a, None) == handles.NULL_POINTER             # §4.3
+    assert m.get_id(a, want_out=False)[0] == handles.NULL_POINTER  # §4.5
+    assert m.record(a, (3, 1)) == handles.INVALID_VALUE        # no record code 3
+    assert m.wait(a, (5, 1, 1, 0)) == handles.INVALID_VALUE
+    assert m.destroy(a) == handles.OK
+    assert m.record(a, (1, 1)) == handles.INVALID_HANDLE       # §4.6 unusable after destroy
+    assert m.destroy(a) == handles.INVALID_HANDLE
+    assert m.create(0)[0] == handles.OK                        # the resource came back
+
+
+# --- batch interpreter vs the sequential model --------------------------------------
+
+def _model_batch(val, meta, n_rel_rows):
+    n_ops, n_c = val.shape
+    final = np.zeros(n_c, dtype=np.uint32)
+    rel = np.zeros((n_rel_rows, n_c), dtype=np.uint8)
+    for c in range(n_c):
+        count, j = 0, 0
+        for k in range(n_ops):
+            m, v = int(meta[k, c]), int(val[k, c])
+            if m & 0x80:
+                h = handles.wait_holds(count, m & 7, v)
+                rel[j, c] = 1 if h else 0
+                if h and (m >> 3) & 1:
+                    count = 0
+                j += 1
+            else:
+                count = handles.record_op(count, m & 7, v)
+        final[c] = count
+    return final, rel
+
+
+@pytest.mark.parametrize("small", [False, True])
+def test_batch_vs_model(small):
+    val, meta, rows = inputs.cnt_batch_input(3, 257, 64, small_values=small)
+    final, rel, rc = oracle.cnt_batch(val, meta, rows)
+    assert rc == 0 and rows == 8
+    f2, r2 = _model_batch(val, meta, rows)
+    np.testing.assert_array_equal(final, f2)
+    np.testing.assert_array_equal(rel, r2)
+    if small:
+        # the directed input exercises every wait code on both outcomes
+        modes = meta[7::8] & 7
+        for code in range(5):
+            flags = rel[(modes == code)]
+            assert flags.min() == 0 and flags.max() == 1, code
+
+
+def test_batch_malformed_ops():
+    val = np.array([[5], [7], [1], [1]], dtype=np.uint32)
+    meta = np.array([[0], [3], [0x80 | 3 | 0x10], [0x80 | 3]], dtype=np.uint8)
+    final, rel, rc = oracle.cnt_batch(val, meta, 2)
+    assert rc == oracle.INVALID_VALUE
+    assert int(final[0]) == 5          # record code 3 ignored
+    assert rel[:, 0].tolist() == [0, 1]  # reserved bit -> flag 0; next wait GE 1 holds
+    # more waits than rows
+    final, rel, rc = oracle.cnt_batch(np.zeros((3, 1), np.uint32), np.array([[0x83], [0x83], [0x83]], np.uint8), 2)
+    assert rc == oracle.INVALID_VALUE and rel[:, 0].tolist() == [1, 1]
+    # isClear on a record
+    final, rel, rc = oracle.cnt_batch(np.array([[5]], np.uint32), np.array([[0x08]], np.uint8), 1)
+    assert rc == oracle.INVALID_VALUE and int(final[0]) == 0
