@@ -1,0 +1,512 @@
+// ccb_api.hip -- the C entry points of libccb.so: argument validation,
+// device checks, co-residency checks, the CntNotify handle table, and the
+// launches (kernels live in ccb_kernels.hip).
+//
+// Sources: "PTO-ISA 跨核同步屏障 SYNCALL 实战指南" (PTO-ISA SYNCALL guide) §4.1
+// workspace, §4.2 usedCores, §6.3 co-residency; "CANN Runtime CntNotify（计数型
+// 通知）管理接口详解" (CANN Runtime CntNotify interfaces) §4.1-§4.6 for the handle
+// calls and their error cases, §6.1 for handle validation.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "ccb.h"
+#include "ccb_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+    bool probed = false;
+    bool gfx950 = false;
+    int numCUs = 0;
+    int ldsPerCU = 0;
+    int ldsPerBlockMax = 0;
+    int wallClockKHz = 0;
+};
+
+std::mutex g_dev_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+ccbStatus current_device(int* devOut, DeviceInfo* infoOut)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CCB_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return CCB_ERR_UNSUPPORTED_DEVICE;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DeviceInfo& d = g_dev[dev];
+    if (!d.probed) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) return CCB_ERR_HIP;
+        d.gfx950 = strncmp(p.gcnArchName, "gfx950", 6) == 0;
+        d.numCUs = p.multiProcessorCount;
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess)
+            return CCB_ERR_HIP;
+        d.ldsPerCU = v;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            return CCB_ERR_HIP;
+        d.ldsPerBlockMax = v;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+            return CCB_ERR_HIP;
+        d.wallClockKHz = v;
+        d.probed = true;
+    }
+    if (!d.gfx950) return CCB_ERR_UNSUPPORTED_DEVICE;
+    if (devOut) *devOut = dev;
+    if (infoOut) *infoOut = d;
+    return CCB_OK;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline ccbStatus from_hip(hipError_t e)
+{
+    if (e == hipSuccess) return CCB_OK;
+    if (e == hipErrorCooperativeLaunchTooLarge) return CCB_ERR_NOT_CORESIDENT;
+    return CCB_ERR_HIP;
+}
+
+inline bool valid_threads(int32_t threads)
+{
+    return threads >= 64 && threads <= 1024 && (threads % 64) == 0;
+}
+
+// Dynamic LDS that keeps at most wgsPerCu workgroups on one CU, and the check
+// that nGrid workgroups fit on the device at once (SYNCALL guide §6.3).
+inline bool valid_mode(int32_t mode) { return mode >= 0 && mode <= 3; }
+
+ccbStatus plan_persistent(ccb::KernelId id, int32_t mode, int32_t nGrid, int32_t threads,
+                          int32_t wgsPerCu, hipStream_t stream, ccb::LaunchShape* ls)
+{
+    DeviceInfo info;
+    ccbStatus st = current_device(nullptr, &info);
+    if (st != CCB_OK) return st;
+    const void* fn = ccb::kernel_ptr(id, mode);
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, fn) != hipSuccess) return CCB_ERR_HIP;
+    size_t lds = 0;
+    if (wgsPerCu > 0) {
+        long want = (long)info.ldsPerCU / wgsPerCu - (long)attr.sharedSizeBytes;
+        long cap = (long)info.ldsPerBlockMax - (long)attr.sharedSizeBytes;
+        if (want > cap) want = cap;
+        want = want / 1024 * 1024;
+        if (want < 0) want = 0;
+        lds = (size_t)want;
+        if (lds > 0 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)lds) != hipSuccess)
+            return CCB_ERR_HIP;
+    }
+    int perCU = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&perCU, fn, threads, lds) != hipSuccess)
+        return CCB_ERR_HIP;
+    if ((long)perCU * info.numCUs < nGrid) return CCB_ERR_NOT_CORESIDENT;
+    ls->fn = fn;
+    ls->nGrid = nGrid;
+    ls->threads = threads;
+    ls->lds = lds;
+    ls->stream = stream;
+    return CCB_OK;
+}
+
+inline uint32_t poll_bound(uint32_t maxPoll) { return maxPoll == 0 ? CCB_SOFT_MAX_POLL : maxPoll; }
+
+// ---------------------------------------------------------------------------
+// CntNotify handle table (CntNotify interfaces §4.1, §4.5, §4.6, §6.1).
+// A handle value encodes (generation << 20) | (index + 1); it is never
+// dereferenced, so a stale or made-up handle is detected, not followed.
+// ---------------------------------------------------------------------------
+struct CntSlot {
+    bool alive = false;
+    uint32_t gen = 0;
+    int device = -1;
+};
+
+std::mutex g_cnt_mu;
+CntSlot g_cnt[CCB_CNT_NOTIFY_POOL];
+uint32_t* g_cnt_pool[kMaxDevices] = {nullptr};
+constexpr uint32_t kLineWords = CCB_LINE_BYTES / 4;
+
+ccbCntNotify encode_handle(uint32_t idx, uint32_t gen)
+{
+    const uintptr_t v = ((uintptr_t)gen << 20) | (uintptr_t)(idx + 1);
+    return reinterpret_cast<ccbCntNotify>(v);
+}
+
+// Looks a handle up; on success *line is its device line.
+ccbStatus resolve(ccbCntNotify h, uint32_t* idxOut, uint32_t** line)
+{
+    const uintptr_t v = reinterpret_cast<uintptr_t>(h);
+    if (v == 0) return CCB_ERR_INVALID_HANDLE;
+    const uintptr_t idx1 = v & ((1u << 20) - 1);
+    const uintptr_t gen = v >> 20;
+    if (idx1 == 0 || idx1 > CCB_CNT_NOTIFY_POOL) return CCB_ERR_INVALID_HANDLE;
+    const uint32_t idx = (uint32_t)(idx1 - 1);
+    std::lock_guard<std::mutex> lk(g_cnt_mu);
+    const CntSlot& s = g_cnt[idx];
+    if (!s.alive || s.gen != gen) return CCB_ERR_INVALID_HANDLE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CCB_ERR_HIP;
+    if (dev != s.device) return CCB_ERR_INVALID_HANDLE;
+    if (idxOut) *idxOut = idx;
+    if (line) *line = g_cnt_pool[s.device] + (size_t)idx * kLineWords;
+    return CCB_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// Miscellaneous
+// ===========================================================================
+extern "C" {
+
+CCB_API const char* ccb_status_string(ccbStatus s)
+{
+    switch (s) {
+    case CCB_OK: return "CCB_OK";
+    case CCB_ERR_INVALID_VALUE: return "CCB_ERR_INVALID_VALUE";
+    case CCB_ERR_NULL_POINTER: return "CCB_ERR_NULL_POINTER";
+    case CCB_ERR_INVALID_HANDLE: return "CCB_ERR_INVALID_HANDLE";
+    case CCB_ERR_RESOURCE_EXHAUSTED: return "CCB_ERR_RESOURCE_EXHAUSTED";
+    case CCB_ERR_TIMEOUT: return "CCB_ERR_TIMEOUT";
+    case CCB_ERR_DEADLOCK: return "CCB_ERR_DEADLOCK";
+    case CCB_ERR_NOT_CORESIDENT: return "CCB_ERR_NOT_CORESIDENT";
+    case CCB_ERR_UNSUPPORTED_DEVICE: return "CCB_ERR_UNSUPPORTED_DEVICE";
+    case CCB_ERR_HIP: return "CCB_ERR_HIP";
+    case CCB_ERR_NOT_READY: return "CCB_ERR_NOT_READY";
+    default: return "CCB_ERR_UNKNOWN";
+    }
+}
+
+CCB_API int32_t ccb_version(void) { return 100; }
+
+CCB_API ccbStatus ccb_device_info(int32_t* numCUs, int32_t* ldsPerCU, int32_t* wallClockKHz)
+{
+    DeviceInfo info;
+    ccbStatus st = current_device(nullptr, &info);
+    if (st != CCB_OK) return st;
+    if (numCUs) *numCUs = info.numCUs;
+    if (ldsPerCU) *ldsPerCU = info.ldsPerCU;
+    if (wallClockKHz) *wallClockKHz = info.wallClockKHz;
+    return CCB_OK;
+}
+
+// ===========================================================================
+// Soft barrier workspace
+// ===========================================================================
+CCB_API size_t ccb_syncall_workspace_bytes(uint32_t nBarriers)
+{
+    return ((size_t)nBarriers * CCB_STRIPES + 1) * CCB_LINE_BYTES;
+}
+
+CCB_API ccbStatus ccb_syncall_workspace_reset(int32_t* ws, uint32_t nBarriers, ccbStream stream)
+{
+    if (ws == nullptr) return CCB_ERR_NULL_POINTER;
+    if (nBarriers == 0 || nBarriers > (1u << 20) || !aligned(ws, CCB_LINE_BYTES))
+        return CCB_ERR_INVALID_VALUE;
+    ccbStatus st = current_device(nullptr, nullptr);
+    if (st != CCB_OK) return st;
+    const int64_t words = ((int64_t)nBarriers * CCB_STRIPES + 1) * kLineWords;
+    return from_hip(ccb::launch_fill_zero(ws, words, (hipStream_t)stream));
+}
+
+CCB_API ccbStatus ccb_syncall_status(const int32_t* ws, uint32_t nBarriers, int32_t* arrivals,
+                                     ccbStream stream)
+{
+    if (ws == nullptr) return CCB_ERR_NULL_POINTER;
+    if (nBarriers == 0 || nBarriers > (1u << 20) || !aligned(ws, CCB_LINE_BYTES))
+        return CCB_ERR_INVALID_VALUE;
+    ccbStatus st = current_device(nullptr, nullptr);
+    if (st != CCB_OK) return st;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return CCB_ERR_HIP;
+    const size_t lines = (size_t)nBarriers * CCB_STRIPES + 1;
+    int32_t* buf = new int32_t[lines * kLineWords];
+    hipError_t e = hipMemcpy(buf, ws, lines * CCB_LINE_BYTES, hipMemcpyDeviceToHost);
+    ccbStatus rc = CCB_OK;
+    if (e != hipSuccess) {
+        rc = CCB_ERR_HIP;
+    } else {
+        if (arrivals)
+            for (uint32_t b = 0; b < nBarriers; ++b) {
+                int64_t sum = 0;
+                for (uint32_t k = 0; k < CCB_STRIPES; ++k)
+                    sum += buf[((size_t)b * CCB_STRIPES + k) * kLineWords];
+                arrivals[b] = (int32_t)sum;
+            }
+        const int32_t errWord = buf[(lines - 1) * kLineWords];
+        rc = errWord == CCB_OK ? CCB_OK : CCB_ERR_DEADLOCK;
+    }
+    delete[] buf;
+    return rc;
+}
+
+// ===========================================================================
+// Persistent workloads
+// ===========================================================================
+CCB_API ccbStatus ccb_run_barrier_only(int32_t* ws, uint32_t* placement, int32_t* wgStatus,
+                                       int32_t rounds, int32_t nGrid, int32_t threads,
+                                       int32_t usedCores, int32_t wgsPerCu, uint32_t maxPoll,
+                                       int32_t mode, ccbStream stream)
+{
+    if (ws == nullptr) return CCB_ERR_NULL_POINTER;
+    if (!aligned(ws, CCB_LINE_BYTES) || rounds < 0 || nGrid < 1 || !valid_threads(threads) ||
+        usedCores < 0 || usedCores > nGrid || wgsPerCu < 0 || !valid_mode(mode))
+        return CCB_ERR_INVALID_VALUE;
+    ccb::LaunchShape ls;
+    ccbStatus st = plan_persistent(ccb::KernelId::BarrierOnly, mode, nGrid, threads, wgsPerCu,
+                                   (hipStream_t)stream, &ls);
+    if (st != CCB_OK) return st;
+    const int32_t members = usedCores != 0 ? usedCores : nGrid;
+    return from_hip(ccb::launch_barrier_only(ls, ws, placement, wgStatus, rounds, members,
+                                             poll_bound(maxPoll)));
+}
+
+CCB_API ccbStatus ccb_run_slot_rounds(int32_t* ws, uint32_t* slots, uint32_t* out,
+                                      int32_t* wgStatus, uint64_t seed, int32_t rounds,
+                                      int32_t nGrid, int32_t threads, int32_t usedCores,
+                                      int32_t wgsPerCu, uint32_t maxPoll, int32_t mode,
+                                      ccbStream stream)
+{
+    if (ws == nullptr || (rounds > 0 && (slots == nullptr || out == nullptr)))
+        return CCB_ERR_NULL_POINTER;
+    if (!aligned(ws, CCB_LINE_BYTES) || rounds < 0 || nGrid < 1 || !valid_threads(threads) ||
+        usedCores < 0 || usedCores > nGrid || wgsPerCu < 0 || !valid_mode(mode))
+        return CCB_ERR_INVALID_VALUE;
+    ccb::LaunchShape ls;
+    ccbStatus st = plan_persistent(ccb::KernelId::SlotRounds, mode, nGrid, threads, wgsPerCu,
+                                   (hipStream_t)stream, &ls);
+    if (st != CCB_OK) return st;
+    const int32_t members = usedCores != 0 ? usedCores : nGrid;
+    return from_hip(ccb::launch_slot_rounds(ls, ws, slots, out, wgStatus, seed, rounds, members,
+                                            poll_bound(maxPoll)));
+}
+
+CCB_API ccbStatus ccb_run_grouped_rounds(int32_t* ws, uint32_t* slots, uint32_t* out,
+                                         int32_t* wgStatus, uint64_t seed, int32_t rounds,
+                                         int32_t nGrid, int32_t threads, int32_t wgsPerCu,
+                                         uint32_t maxPoll, int32_t mode, ccbStream stream)
+{
+    if (ws == nullptr || (rounds > 0 && (slots == nullptr || out == nullptr)))
+        return CCB_ERR_NULL_POINTER;
+    if (!aligned(ws, CCB_LINE_BYTES) || rounds < 0 || nGrid < 2 || (nGrid % 2) != 0 ||
+        !valid_threads(threads) || wgsPerCu < 0 || !valid_mode(mode))
+        return CCB_ERR_INVALID_VALUE;
+    ccb::LaunchShape ls;
+    ccbStatus st = plan_persistent(ccb::KernelId::GroupedRounds, mode, nGrid, threads, wgsPerCu,
+                                   (hipStream_t)stream, &ls);
+    if (st != CCB_OK) return st;
+    return from_hip(ccb::launch_grouped_rounds(ls, ws, slots, out, wgStatus, seed, rounds,
+                                               poll_bound(maxPoll)));
+}
+
+CCB_API size_t ccb_stencil_halo_bytes(int32_t nGrid, int32_t threads)
+{
+    if (nGrid < 1 || !valid_threads(threads)) return 0;
+    return (size_t)nGrid * (size_t)(threads / 64) * 4 * sizeof(int32_t);
+}
+
+CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32_t iters,
+                                  int32_t* ws, int32_t* halo, int32_t nGrid, int32_t threads,
+                                  int32_t wgsPerCu, uint32_t maxPoll, int32_t mode,
+                                  ccbStream stream)
+{
+    if (bufA == nullptr || bufB == nullptr || ws == nullptr) return CCB_ERR_NULL_POINTER;
+    if (valid_mode(mode) && (mode & CCB_VISIBILITY_FULL) == 0 && halo == nullptr)
+        return CCB_ERR_NULL_POINTER;
+    if (n < 1 || iters < 0 || !aligned(ws, CCB_LINE_BYTES) || !aligned(bufA, 16) ||
+        !aligned(bufB, 16) || nGrid < 1 || !valid_threads(threads) || wgsPerCu < 0 ||
+        !valid_mode(mode) || (halo != nullptr && !aligned(halo, 4)))
+        return CCB_ERR_INVALID_VALUE;
+    const uintptr_t a0 = (uintptr_t)bufA, a1 = a0 + (uintptr_t)n * 4;
+    const uintptr_t b0 = (uintptr_t)bufB, b1 = b0 + (uintptr_t)n * 4;
+    if (a0 < b1 && b0 < a1) return CCB_ERR_INVALID_VALUE;  // overlapping buffers
+    ccb::LaunchShape ls;
+    ccbStatus st = plan_persistent(ccb::KernelId::Stencil, mode, nGrid, threads, wgsPerCu,
+                                   (hipStream_t)stream, &ls);
+    if (st != CCB_OK) return st;
+    // equal contiguous spans per wave, a multiple of 4 elements (16 B)
+    const int64_t waves = (int64_t)nGrid * (threads / 64);
+    int64_t span = (n + waves - 1) / waves;
+    span = (span + 3) / 4 * 4;
+    return from_hip(ccb::launch_stencil(ls, bufA, bufB, n, iters, ws, halo, span,
+                                        poll_bound(maxPoll)));
+}
+
+// ===========================================================================
+// Floor microbenchmarks
+// ===========================================================================
+CCB_API ccbStatus ccb_bench_atomic_chain(int32_t* line, uint64_t* ticksOut, int32_t iters,
+                                         int32_t fenced, int32_t kind, ccbStream stream)
+{
+    if (line == nullptr || ticksOut == nullptr) return CCB_ERR_NULL_POINTER;
+    if (iters < 1 || (kind != 0 && kind != 1) || !aligned(line, CCB_LINE_BYTES))
+        return CCB_ERR_INVALID_VALUE;
+    ccbStatus st = current_device(nullptr, nullptr);
+    if (st != CCB_OK) return st;
+    return from_hip(ccb::launch_atomic_chain(line, ticksOut, iters, fenced, kind,
+                                             (hipStream_t)stream));
+}
+
+CCB_API ccbStatus ccb_bench_atomic_contended(int32_t* line, uint64_t* ticksOut, int32_t iters,
+                                             int32_t nGrid, ccbStream stream)
+{
+    if (line == nullptr || ticksOut == nullptr) return CCB_ERR_NULL_POINTER;
+    if (iters < 1 || nGrid < 1 || !aligned(line, CCB_LINE_BYTES)) return CCB_ERR_INVALID_VALUE;
+    DeviceInfo info;
+    ccbStatus st = current_device(nullptr, &info);
+    if (st != CCB_OK) return st;
+    return from_hip(ccb::launch_atomic_contended(line, ticksOut, iters, nGrid,
+                                                 (hipStream_t)stream));
+}
+
+CCB_API ccbStatus ccb_bench_copy(void* dst, const void* src, int64_t nBytes, ccbStream stream)
+{
+    if (dst == nullptr || src == nullptr) return CCB_ERR_NULL_POINTER;
+    if (nBytes < 0 || (nBytes % 16) != 0 || !aligned(dst, 16) || !aligned(src, 16))
+        return CCB_ERR_INVALID_VALUE;
+    DeviceInfo info;
+    ccbStatus st = current_device(nullptr, &info);
+    if (st != CCB_OK) return st;
+    if (nBytes == 0) return CCB_OK;
+    return from_hip(ccb::launch_copy(static_cast<int4*>(dst), static_cast<const int4*>(src),
+                                     nBytes / 16, info.numCUs * 8, (hipStream_t)stream));
+}
+
+// ===========================================================================
+// CntNotify
+// ===========================================================================
+CCB_API ccbStatus ccb_cnt_notify_create(ccbCntNotify* out, uint64_t flag)
+{
+    if (out == nullptr) return CCB_ERR_NULL_POINTER;
+    if (flag != 0) return CCB_ERR_INVALID_VALUE;  // the flag is reserved (§4.1)
+    int dev = 0;
+    ccbStatus st = current_device(&dev, nullptr);
+    if (st != CCB_OK) return st;
+    std::lock_guard<std::mutex> lk(g_cnt_mu);
+    if (g_cnt_pool[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipMalloc(&p, (size_t)CCB_CNT_NOTIFY_POOL * CCB_LINE_BYTES) != hipSuccess)
+            return CCB_ERR_HIP;
+        g_cnt_pool[dev] = static_cast<uint32_t*>(p);
+    }
+    uint32_t idx = CCB_CNT_NOTIFY_POOL;
+    for (uint32_t i = 0; i < CCB_CNT_NOTIFY_POOL; ++i) {
+        if (!g_cnt[i].alive) { idx = i; break; }
+    }
+    if (idx == CCB_CNT_NOTIFY_POOL) return CCB_ERR_RESOURCE_EXHAUSTED;
+    // count 0, no wait completed yet
+    uint32_t init[kLineWords];
+    memset(init, 0, sizeof(init));
+    init[1] = (uint32_t)CCB_ERR_NOT_READY;
+    if (hipMemcpy(g_cnt_pool[dev] + (size_t)idx * kLineWords, init, sizeof(init),
+                  hipMemcpyHostToDevice) != hipSuccess)
+        return CCB_ERR_HIP;
+    CntSlot& s = g_cnt[idx];
+    s.alive = true;
+    s.gen = (s.gen + 1) & 0xFFFFFu;
+    if (s.gen == 0) s.gen = 1;
+    s.device = dev;
+    *out = encode_handle(idx, s.gen);
+    return CCB_OK;
+}
+
+CCB_API ccbStatus ccb_cnt_notify_record(ccbCntNotify h, ccbStream stream,
+                                        const ccbCntRecordInfo* info)
+{
+    uint32_t* line = nullptr;
+    ccbStatus st = resolve(h, nullptr, &line);
+    if (st != CCB_OK) return st;
+    if (info == nullptr) return CCB_ERR_NULL_POINTER;
+    const int32_t m = info->mode;
+    if (!(m == CCB_CNT_RECORD_SET_VALUE || m == CCB_CNT_RECORD_ADD || m == CCB_CNT_RECORD_BIT_OR ||
+          m == CCB_CNT_RECORD_BIT_AND))
+        return CCB_ERR_INVALID_VALUE;
+    return from_hip(ccb::launch_cnt_record(line, m, info->value, (hipStream_t)stream));
+}
+
+CCB_API ccbStatus ccb_cnt_notify_wait(ccbCntNotify h, ccbStream stream, const ccbCntWaitInfo* info)
+{
+    uint32_t* line = nullptr;
+    ccbStatus st = resolve(h, nullptr, &line);
+    if (st != CCB_OK) return st;
+    if (info == nullptr) return CCB_ERR_NULL_POINTER;
+    if (info->mode < CCB_CNT_WAIT_LESS || info->mode > CCB_CNT_WAIT_EQUAL_WITH_BITMASK ||
+        info->isClear > 1 || info->rev[0] != 0 || info->rev[1] != 0 || info->rev[2] != 0)
+        return CCB_ERR_INVALID_VALUE;
+    DeviceInfo dinfo;
+    st = current_device(nullptr, &dinfo);
+    if (st != CCB_OK) return st;
+    const uint64_t ticks = (uint64_t)info->timeout * (uint64_t)dinfo.wallClockKHz * 1000ull;
+    return from_hip(ccb::launch_cnt_wait(line, info->mode, info->value, info->isClear, ticks,
+                                         (hipStream_t)stream));
+}
+
+CCB_API ccbStatus ccb_cnt_notify_reset(ccbCntNotify h, ccbStream stream)
+{
+    uint32_t* line = nullptr;
+    ccbStatus st = resolve(h, nullptr, &line);
+    if (st != CCB_OK) return st;
+    return from_hip(ccb::launch_cnt_reset(line, (hipStream_t)stream));
+}
+
+CCB_API ccbStatus ccb_cnt_notify_get_id(ccbCntNotify h, uint32_t* id)
+{
+    uint32_t idx = 0;
+    ccbStatus st = resolve(h, &idx, nullptr);
+    if (st != CCB_OK) return st;
+    if (id == nullptr) return CCB_ERR_NULL_POINTER;
+    *id = idx;
+    return CCB_OK;
+}
+
+CCB_API ccbStatus ccb_cnt_notify_destroy(ccbCntNotify h)
+{
+    uint32_t idx = 0;
+    ccbStatus st = resolve(h, &idx, nullptr);
+    if (st != CCB_OK) return st;
+    std::lock_guard<std::mutex> lk(g_cnt_mu);
+    g_cnt[idx].alive = false;
+    return CCB_OK;
+}
+
+CCB_API ccbStatus ccb_cnt_notify_query(ccbCntNotify h, uint32_t* value, ccbStatus* lastWait,
+                                       ccbStream stream)
+{
+    uint32_t* line = nullptr;
+    ccbStatus st = resolve(h, nullptr, &line);
+    if (st != CCB_OK) return st;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return CCB_ERR_HIP;
+    uint32_t words[2] = {0, 0};
+    if (hipMemcpy(words, line, sizeof(words), hipMemcpyDeviceToHost) != hipSuccess)
+        return CCB_ERR_HIP;
+    if (value) *value = words[0];
+    if (lastWait) *lastWait = (ccbStatus)words[1];
+    return CCB_OK;
+}
+
+CCB_API ccbStatus ccb_cnt_notify_batch(const uint32_t* val, const uint8_t* meta,
+                                       int64_t nCounters, int32_t nOps, uint32_t* final_,
+                                       uint8_t* rel, int32_t nRelRows, int32_t* err,
+                                       ccbStream stream)
+{
+    if (nCounters < 0 || nOps < 0 || nRelRows < 0) return CCB_ERR_INVALID_VALUE;
+    if (nCounters == 0) return CCB_OK;
+    if (final_ == nullptr) return CCB_ERR_NULL_POINTER;
+    if (nOps > 0 && (val == nullptr || meta == nullptr)) return CCB_ERR_NULL_POINTER;
+    if (nRelRows > 0 && rel == nullptr) return CCB_ERR_NULL_POINTER;
+    if (!aligned(final_, 4) || (val != nullptr && !aligned(val, 4))) return CCB_ERR_INVALID_VALUE;
+    ccbStatus st = current_device(nullptr, nullptr);
+    if (st != CCB_OK) return st;
+    const bool vec4 = (nCounters % 4) == 0 && (val == nullptr || aligned(val, 16)) &&
+                      (meta == nullptr || aligned(meta, 4)) && aligned(final_, 16) &&
+                      (rel == nullptr || aligned(rel, 4));
+    return from_hip(ccb::launch_cnt_batch(val, meta, nCounters, nOps, final_, rel, nRelRows, err,
+                                          vec4, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// ccb_internal.h -- private interface between the C entry points
+// (ccb_api.hip) and the kernels (ccb_kernels.hip).  Not installed.
+#ifndef CCB_INTERNAL_H
+#define CCB_INTERNAL_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ccb {
+
+// Tuning constants of the kernels.
+constexpr int kStencilUnroll = 8;   // 1-KiB loads in flight per wave
+constexpr bool kStencilNT = false;  // non-temporal stores for the stencil output
+constexpr int kCntUnroll = 8;       // ops loaded ahead per thread in the batch engine
+
+enum class KernelId { BarrierOnly, SlotRounds, GroupedRounds, Stencil };
+
+struct LaunchShape {
+    const void* fn;  // the kernel instance
+    int nGrid;
+    int threads;
+    size_t lds;  // dynamic LDS bytes per workgroup
+    hipStream_t stream;
+};
+
+const void* kernel_ptr(KernelId id, int32_t mode);
+
+hipError_t launch_barrier_only(const LaunchShape& ls, int32_t* ws, uint32_t* placement,
+                               int32_t* wgStatus, int32_t rounds, int32_t nMembers,
+                               uint32_t maxPoll);
+hipError_t launch_slot_rounds(const LaunchShape& ls, int32_t* ws, uint32_t* slots, uint32_t* out,
+                              int32_t* wgStatus, uint64_t seed, int32_t rounds, int32_t nMembers,
+                              uint32_t maxPoll);
+hipError_t launch_grouped_rounds(const LaunchShape& ls, int32_t* ws, uint32_t* slots,
+                                 uint32_t* out, int32_t* wgStatus, uint64_t seed, int32_t rounds,
+                                 uint32_t maxPoll);
+hipError_t launch_stencil(const LaunchShape& ls, int32_t* bufA, int32_t* bufB, int64_t n,
+                          int32_t iters, int32_t* ws, int32_t* halo, int64_t span,
+                          uint32_t maxPoll);
+hipError_t launch_cnt_batch(const uint32_t* val, const uint8_t* meta, int64_t nCounters,
+                            int32_t nOps, uint32_t* finalOut, uint8_t* rel, int32_t nRelRows,
+                            int32_t* err, bool vec4, hipStream_t s);
+hipError_t launch_cnt_record(uint32_t* line, int32_t mode, uint32_t value, hipStream_t s);
+hipError_t launch_cnt_wait(uint32_t* line, int32_t mode, uint32_t value, int32_t isClear,
+                           uint64_t timeoutTicks, hipStream_t s);
+hipError_t launch_cnt_reset(uint32_t* line, hipStream_t s);
+hipError_t launch_fill_zero(int32_t* p, int64_t nWords, hipStream_t s);
+hipError_t launch_atomic_chain(int32_t* line, uint64_t* ticks, int32_t iters, int32_t fenced,
+                               int32_t kind, hipStream_t s);
+hipError_t launch_atomic_contended(int32_t* line, uint64_t* ticks, int32_t iters, int32_t nGrid,
+                                   hipStream_t s);
+hipError_t launch_copy(int4* dst, const int4* src, int64_t n16, int nBlocks, hipStream_t s);
+
+}  // namespace ccb
+
+#endif  // CCB_INTERNAL_H

@@ -1,0 +1,766 @@
+// ccb_kernels.hip -- gfx950 kernels of the soft epoch barrier library.
+//
+// Persistent grids built on the device barrier of ccb_device.h:
+//   barrier-only rounds, witness (slot) rounds, grouped witness rounds and a
+//   barrier-separated 3-point stencil;
+// plus the batched CntNotify engine, the stream-ordered CntNotify record /
+// wait / reset kernels and the floor microbenchmarks.
+//
+// Sources: "PTO-ISA 跨核同步屏障 SYNCALL 实战指南" (PTO-ISA SYNCALL guide) §2,
+// §4-§7 for the barrier, and "CANN Runtime CntNotify（计数型通知）管理接口详解"
+// (CANN Runtime CntNotify interfaces) §3.1-§3.3, §4.2-§4.4 for the counter
+// operations.  Each kernel cites the passage it implements.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ccb.h"
+#include "ccb_device.h"
+#include "ccb_internal.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kRing = 4;  // witness slot rows reused round-robin
+
+__device__ __forceinline__ bool leader() { return threadIdx.x == 0; }
+
+// Witness value of member w in round r: SplitMix64 (Steele, Lea & Flood,
+// OOPSLA 2014) output number r*2^32 + w + 1 for the given seed -- the state
+// advanced that many times by the golden gamma, then the variant-13
+// finaliser -- keeping the high 32 bits.
+__device__ __forceinline__ uint32_t witness(uint64_t seed, uint32_t r, uint32_t w)
+{
+    const uint64_t key = ((uint64_t)r << 32) | (uint64_t)w;
+    uint64_t z = seed + 0x9E3779B97F4A7C15ull * (key + 1ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return (uint32_t)(z >> 32);
+}
+
+// Sum of v over the workgroup (mod 2^32); the result is valid in thread 0.
+// partial: LDS scratch of one word per wave.
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* partial)
+{
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x % kWave) == 0) partial[wave] = v;
+    __syncthreads();
+    uint32_t s = 0;
+    if (threadIdx.x == 0) {
+        const int nw = blockDim.x / kWave;
+        for (int i = 0; i < nw; ++i) s += partial[i];
+    }
+    return s;
+}
+
+__device__ __forceinline__ void record_placement(uint32_t* placement)
+{
+    if (placement != nullptr && leader()) {
+        placement[2 * blockIdx.x] = __builtin_amdgcn_s_getreg((31 << 11) | 4);       // HW_ID
+        placement[2 * blockIdx.x + 1] = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // XCC_ID
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Barrier variants.  K = stripes (1: the pages' single counter), V = the
+// visibility strength.  Shared witness data follows V: device-coherent
+// accesses across a CCB_VIS_ORDER barrier, plain accesses across a
+// CCB_VIS_FULL one (whose fences make them visible).
+// ---------------------------------------------------------------------------
+namespace {
+
+template <ccbVisibility V>
+__device__ __forceinline__ void shared_store(uint32_t* p, uint32_t v)
+{
+    if constexpr (V == CCB_VIS_ORDER) ccb_store_coherent(p, v);
+    else *p = v;
+}
+template <ccbVisibility V>
+__device__ __forceinline__ uint32_t shared_load(const uint32_t* p)
+{
+    if constexpr (V == CCB_VIS_ORDER) return ccb_load_coherent(p);
+    else return *p;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Barrier-only rounds: the latency benchmark of the soft barrier.
+// Members (w < nMembers) run `rounds` barriers; the rest take the partial-
+// participation exit of the SYNCALL guide §7.2 and mark themselves idle (§8).
+// ---------------------------------------------------------------------------
+template <int K, ccbVisibility V>
+__global__ __launch_bounds__(1024) void ccb_k_barrier_only(int32_t* ws, uint32_t* placement,
+                                                            int32_t* wgStatus, int32_t rounds,
+                                                            int32_t nMembers, uint32_t maxPoll)
+{
+    record_placement(placement);
+    const int32_t w = blockIdx.x;
+    if (w >= nMembers) {
+        if (wgStatus != nullptr && leader()) wgStatus[w] = 2;
+        return;
+    }
+    int32_t* err = ws + CCB_STRIPES * CCB_LINE_WORDS;
+    int32_t rc = CCB_OK;
+    for (int32_t r = 0; r < rounds && rc == CCB_OK; ++r)
+        rc = ccb_barrier<K, V>(ws, nMembers, w, maxPoll, err);
+    if (wgStatus != nullptr && leader()) wgStatus[w] = rc == CCB_OK ? 1 : 3;
+}
+
+// ---------------------------------------------------------------------------
+// Witness rounds on one barrier (the flag-slot test pattern of the SYNCALL
+// guide §6.1, run for many rounds): write own slot, barrier, sum all slots.
+// ---------------------------------------------------------------------------
+template <int K, ccbVisibility V>
+__global__ __launch_bounds__(1024) void ccb_k_slot_rounds(int32_t* ws, uint32_t* slots,
+                                                           uint32_t* out, int32_t* wgStatus,
+                                                           uint64_t seed, int32_t rounds,
+                                                           int32_t nMembers, uint32_t maxPoll)
+{
+    __shared__ uint32_t partial[1024 / kWave];
+    const int32_t w = blockIdx.x;
+    const int32_t nGrid = gridDim.x;
+    if (w >= nMembers) {
+        if (wgStatus != nullptr && leader()) wgStatus[w] = 2;
+        return;
+    }
+    int32_t* err = ws + CCB_STRIPES * CCB_LINE_WORDS;
+    int32_t rc = CCB_OK;
+    for (int32_t r = 0; r < rounds; ++r) {
+        uint32_t* row = slots + (size_t)(r % kRing) * nGrid;
+        if (leader()) shared_store<V>(row + w, witness(seed, (uint32_t)r, (uint32_t)w));
+        rc = ccb_barrier<K, V>(ws, nMembers, w, maxPoll, err);
+        if (rc != CCB_OK) break;
+        uint32_t s = 0;
+        for (int32_t i = threadIdx.x; i < nMembers; i += blockDim.x) s += shared_load<V>(row + i);
+        s = block_sum(s, partial);
+        if (leader()) out[(size_t)r * nGrid + w] = s;
+    }
+    if (wgStatus != nullptr && leader()) wgStatus[w] = rc == CCB_OK ? 1 : 3;
+}
+
+// ---------------------------------------------------------------------------
+// Grouped witness rounds: group A (even ids) on barrier 0, group B (odd ids)
+// on barrier 1, everyone on barrier 2; round kind r mod 3.  Each barrier's
+// members enter it in the same order the same number of times (SYNCALL
+// guide §6.2).  Slots are stored group-major (even ids first) so a group's
+// slots are contiguous; the sum does not depend on the layout.
+// ---------------------------------------------------------------------------
+template <int K, ccbVisibility V>
+__global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32_t* slots,
+                                                              uint32_t* out, int32_t* wgStatus,
+                                                              uint64_t seed, int32_t rounds,
+                                                              uint32_t maxPoll)
+{
+    __shared__ uint32_t partial[1024 / kWave];
+    const int32_t w = blockIdx.x;
+    const int32_t nGrid = gridDim.x;
+    const int32_t half = nGrid / 2;
+    const int32_t parity = w & 1;
+    const int32_t pos = parity * half + (w >> 1);
+    int32_t* err = ws + 3 * CCB_STRIPES * CCB_LINE_WORDS;
+    int32_t rc = CCB_OK;
+    for (int32_t r = 0; r < rounds; ++r) {
+        const int32_t kind = r % 3;
+        if (kind != 2 && kind != parity) continue;  // not a member of this round
+        uint32_t* row = slots + (size_t)(r % kRing) * nGrid;
+        if (leader()) shared_store<V>(row + pos, witness(seed, (uint32_t)r, (uint32_t)w));
+        const int32_t n = kind == 2 ? nGrid : half;
+        const int32_t member = kind == 2 ? w : (w >> 1);
+        rc = ccb_barrier<K, V>(ws + kind * CCB_STRIPES * CCB_LINE_WORDS, n, member, maxPoll, err);
+        if (rc != CCB_OK) break;
+        const int32_t first = kind == 2 ? 0 : kind * half;
+        uint32_t s = 0;
+        for (int32_t i = threadIdx.x; i < n; i += blockDim.x) s += shared_load<V>(row + first + i);
+        s = block_sum(s, partial);
+        if (leader()) out[(size_t)r * nGrid + w] = s;
+    }
+    if (wgStatus != nullptr && leader()) wgStatus[w] = rc == CCB_OK ? 1 : 3;
+}
+
+// ---------------------------------------------------------------------------
+// Barrier-separated 3-point stencil (persistent).
+//
+// Each wave owns a contiguous span of `span` elements (a multiple of 4) for
+// every iteration.  A wave step covers 256 elements: lane l holds elements
+// 4l..4l+3 of the step as one 16-byte load.  The left neighbour of a lane's
+// first element is lane l-1's last element (DPP wave shift right by one
+// lane); lane 0 takes it from the previous step's lane 63 (a scalar carried
+// across steps) or, at the start of the span, from the left halo.  The right
+// neighbour of a lane's last element is lane l+1's first (DPP wave shift
+// left); lane 63 takes it from the next step's lane 0, or past the span's end
+// from the right halo.  The array ends are clamped.  U steps are loaded
+// before any is used so that each wave keeps U 1-KiB loads in flight.
+//
+// A wave only ever touches its own span, so the only data that crosses
+// workgroups are the two halo elements per span.  Across a CCB_VIS_ORDER
+// barrier they travel through a small exchange buffer written and read with
+// device-coherent accesses (halo[t & 1][wave][0] = first output element of
+// the span in iteration t, [1] = last); the bulk data needs no cache
+// maintenance at all.  Across a CCB_VIS_FULL barrier they are read straight
+// from the source buffer.
+// ---------------------------------------------------------------------------
+namespace {
+
+__device__ __forceinline__ int32_t lane_from_left(int32_t v)  // lane l gets lane l-1
+{
+    return __builtin_amdgcn_update_dpp(0, v, 0x138 /* wave_shr:1 */, 0xf, 0xf, false);
+}
+__device__ __forceinline__ int32_t lane_from_right(int32_t v)  // lane l gets lane l+1
+{
+    return __builtin_amdgcn_update_dpp(0, v, 0x130 /* wave_shl:1 */, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ int32_t st3(int32_t a, int32_t b, int32_t c)
+{
+    return (a + 2 * b + c) >> 2;
+}
+
+template <bool kNT>
+__device__ __forceinline__ void store4(int32_t* p, int4 v)
+{
+    if constexpr (kNT) {
+        typedef int v4i __attribute__((ext_vector_type(4)));
+        const v4i nv = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(nv, reinterpret_cast<v4i*>(p));
+    } else {
+        *reinterpret_cast<int4*>(p) = v;
+    }
+}
+
+// One step: outputs for the 4 elements a lane holds.
+__device__ __forceinline__ int4 step4(int4 v, int32_t carry, int32_t nextFirst, int lane)
+{
+    int32_t left = lane_from_left(v.w);
+    int32_t right = lane_from_right(v.x);
+    if (lane == 0) left = carry;
+    if (lane == kWave - 1) right = nextFirst;
+    int4 o;
+    o.x = st3(left, v.x, v.y);
+    o.y = st3(v.x, v.y, v.z);
+    o.z = st3(v.y, v.z, v.w);
+    o.w = st3(v.z, v.w, right);
+    return o;
+}
+
+// Computes y[s0..s1) from x; leftHalo = x[s0-1] (clamped), rightHalo = x[s1]
+// (clamped).  If haloOut is non-null the span's first and last outputs are
+// also published there with device-coherent stores.
+template <int U, bool kNT>
+__device__ __forceinline__ void stencil_span(const int32_t* __restrict__ x, int32_t* __restrict__ y,
+                                             int64_t s0, int64_t s1, int32_t leftHalo,
+                                             int32_t rightHalo, int32_t* haloOut)
+{
+    const int lane = threadIdx.x % kWave;
+    const int64_t len = s1 - s0;
+    const int64_t nFull = len / 256;
+    int32_t carry = leftHalo;
+    int64_t j = 0;
+    for (; j + U <= nFull; j += U) {
+        int4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = *reinterpret_cast<const int4*>(x + s0 + (j + u) * 256 + 4 * lane);
+        // first element after this batch: next step's lane 0, or past the span
+        const int64_t after = s0 + (j + U) * 256;
+        const int32_t rightEdge = after < s1 ? x[after] : rightHalo;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t nextFirst = (u + 1 < U) ? __builtin_amdgcn_readlane(v[u + 1].x, 0) : rightEdge;
+            const int4 o = step4(v[u], carry, nextFirst, lane);
+            const int64_t e0 = s0 + (j + u) * 256 + 4 * lane;
+            store4<kNT>(y + e0, o);
+            if (haloOut != nullptr) {
+                if (e0 == s0) ccb_store_coherent(haloOut, o.x);
+                if (e0 + 3 == s1 - 1) ccb_store_coherent(haloOut + 1, o.w);
+            }
+            carry = __builtin_amdgcn_readlane(v[u].w, kWave - 1);
+        }
+    }
+    for (; j < nFull; ++j) {
+        const int4 v = *reinterpret_cast<const int4*>(x + s0 + j * 256 + 4 * lane);
+        const int64_t after = s0 + (j + 1) * 256;
+        const int32_t nextFirst = after < s1 ? x[after] : rightHalo;
+        const int4 o = step4(v, carry, nextFirst, lane);
+        const int64_t e0 = s0 + j * 256 + 4 * lane;
+        store4<kNT>(y + e0, o);
+        if (haloOut != nullptr) {
+            if (e0 == s0) ccb_store_coherent(haloOut, o.x);
+            if (e0 + 3 == s1 - 1) ccb_store_coherent(haloOut + 1, o.w);
+        }
+        carry = __builtin_amdgcn_readlane(v.w, kWave - 1);
+    }
+    // ragged tail of the span: one element per lane at a time
+    for (int64_t e = s0 + nFull * 256 + lane; e < s1; e += kWave) {
+        const int32_t a = e == s0 ? leftHalo : x[e - 1];
+        const int32_t c = e + 1 == s1 ? rightHalo : x[e + 1];
+        const int32_t o = st3(a, x[e], c);
+        y[e] = o;
+        if (haloOut != nullptr) {
+            if (e == s0) ccb_store_coherent(haloOut, o);
+            if (e == s1 - 1) ccb_store_coherent(haloOut + 1, o);
+        }
+    }
+}
+
+}  // namespace
+
+template <int K, ccbVisibility V>
+__global__ __launch_bounds__(1024) void ccb_k_stencil(int32_t* bufA, int32_t* bufB, int64_t n,
+                                                       int32_t iters, int32_t* ws, int32_t* halo,
+                                                       int64_t span, uint32_t maxPoll)
+{
+    const int64_t wavesPerWg = blockDim.x / kWave;
+    const int64_t nWaves = (int64_t)gridDim.x * wavesPerWg;
+    const int64_t waveId = (int64_t)blockIdx.x * wavesPerWg + threadIdx.x / kWave;
+    const int64_t s0 = waveId * span;
+    const int64_t s1 = s0 + span < n ? s0 + span : n;
+    int32_t* err = ws + CCB_STRIPES * CCB_LINE_WORDS;
+    const int32_t nGrid = gridDim.x;
+    for (int32_t t = 0; t < iters; ++t) {
+        const int32_t* x = (t & 1) ? bufB : bufA;
+        int32_t* y = (t & 1) ? bufA : bufB;
+        if (s0 < s1) {
+            int32_t leftHalo, rightHalo;
+            if (V == CCB_VIS_FULL || t == 0) {
+                leftHalo = x[s0 > 0 ? s0 - 1 : 0];
+                rightHalo = x[s1 < n ? s1 : n - 1];
+            } else {
+                const int32_t* prev = halo + (size_t)((t - 1) & 1) * nWaves * 2;
+                leftHalo = s0 > 0 ? ccb_load_coherent(prev + 2 * (waveId - 1) + 1) : x[0];
+                rightHalo = s1 < n ? ccb_load_coherent(prev + 2 * (waveId + 1)) : x[n - 1];
+            }
+            int32_t* haloOut = nullptr;
+            if (V == CCB_VIS_ORDER && t + 1 < iters)
+                haloOut = halo + (size_t)(t & 1) * nWaves * 2 + 2 * waveId;
+            stencil_span<ccb::kStencilUnroll, ccb::kStencilNT>(x, y, s0, s1, leftHalo, rightHalo, haloOut);
+        }
+        if (t + 1 < iters) {
+            if (ccb_barrier<K, V>(ws, nGrid, blockIdx.x, maxPoll, err) != CCB_OK) break;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// CntNotify operations (CntNotify interfaces §3.1 record modes, §3.2 wait
+// predicates; unsigned 32-bit arithmetic per §3.3).
+// ---------------------------------------------------------------------------
+namespace {
+
+// Record: returns the new count; *bad set for a code outside {0,1,2,4}.
+__device__ __forceinline__ uint32_t cnt_record(uint32_t c, uint32_t mode, uint32_t v, bool& bad)
+{
+    bad = !(mode == CCB_CNT_RECORD_SET_VALUE || mode == CCB_CNT_RECORD_ADD ||
+            mode == CCB_CNT_RECORD_BIT_OR || mode == CCB_CNT_RECORD_BIT_AND);
+    uint32_t r = c;
+    r = mode == CCB_CNT_RECORD_SET_VALUE ? v : r;
+    r = mode == CCB_CNT_RECORD_ADD ? c + v : r;
+    r = mode == CCB_CNT_RECORD_BIT_OR ? (c | v) : r;
+    r = mode == CCB_CNT_RECORD_BIT_AND ? (c & v) : r;
+    return r;
+}
+
+// Wait predicate; *bad set for a code above 4.
+__device__ __forceinline__ bool cnt_holds(uint32_t c, uint32_t mode, uint32_t v, bool& bad)
+{
+    bad = mode > CCB_CNT_WAIT_EQUAL_WITH_BITMASK;
+    bool h = false;
+    h = mode == CCB_CNT_WAIT_LESS ? (c < v) : h;
+    h = mode == CCB_CNT_WAIT_EQUAL ? (c == v) : h;
+    h = mode == CCB_CNT_WAIT_BIGGER ? (c > v) : h;
+    h = mode == CCB_CNT_WAIT_BIGGER_OR_EQUAL ? (c >= v) : h;
+    h = mode == CCB_CNT_WAIT_EQUAL_WITH_BITMASK ? ((c & v) == v) : h;
+    return h;
+}
+
+// One op of the batched engine on one counter.  Returns true when the op is
+// a wait (its release flag in flag).  rowOk: the wait has an output row; a
+// wait without one is malformed and leaves the count alone.
+__device__ __forceinline__ bool cnt_step(uint32_t& c, uint32_t m, uint32_t v, bool rowOk,
+                                         bool& bad, uint8_t& flag)
+{
+    const uint32_t mode = m & 7u;
+    const uint32_t clear = (m >> 3) & 1u;
+    const uint32_t reserved = (m >> 4) & 7u;
+    const bool isWait = (m & 0x80u) != 0;
+    if (isWait) {
+        bool b;
+        const bool h = cnt_holds(c, mode, v, b);
+        b = b || reserved != 0 || !rowOk;
+        const bool rel = h && !b;
+        // the clear follows the release (CntNotify interfaces §3.3, §7)
+        c = (rel && clear) ? 0u : c;
+        flag = rel ? 1 : 0;
+        bad = bad || b;
+    } else {
+        bool b;
+        const uint32_t r = cnt_record(c, mode, v, b);
+        b = b || reserved != 0 || clear != 0;
+        c = b ? c : r;
+        bad = bad || b;
+    }
+    return isWait;
+}
+
+}  // namespace
+
+// Four adjacent counters per thread: 4-byte meta loads and 16-byte operand
+// loads per op; nCounters must be a multiple of 4.
+template <int U>
+__global__ __launch_bounds__(256) void ccb_k_cnt_batch4(const uint32_t* __restrict__ val,
+                                                        const uint8_t* __restrict__ meta,
+                                                        int64_t nCounters, int32_t nOps,
+                                                        uint32_t* __restrict__ finalOut,
+                                                        uint8_t* __restrict__ rel,
+                                                        int32_t nRelRows, int32_t* err)
+{
+    const int64_t c0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (c0 >= nCounters) return;
+    uint32_t c[4] = {0u, 0u, 0u, 0u};
+    int32_t j[4] = {0, 0, 0, 0};
+    bool bad = false;
+    int32_t k = 0;
+    auto apply = [&](uint32_t m4, uint4 v4) {
+        const uint32_t vv[4] = {v4.x, v4.y, v4.z, v4.w};
+        uint8_t f[4] = {0, 0, 0, 0};
+        bool w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = cnt_step(c[i], (m4 >> (8 * i)) & 0xffu, vv[i], j[i] < nRelRows, bad, f[i]);
+        const bool allWait = w[0] && w[1] && w[2] && w[3];
+        if (allWait && j[0] == j[1] && j[0] == j[2] && j[0] == j[3] && j[0] < nRelRows) {
+            const uint32_t packed = (uint32_t)f[0] | ((uint32_t)f[1] << 8) |
+                                    ((uint32_t)f[2] << 16) | ((uint32_t)f[3] << 24);
+            *reinterpret_cast<uint32_t*>(rel + (int64_t)j[0] * nCounters + c0) = packed;
+            j[0]++; j[1]++; j[2]++; j[3]++;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (!w[i]) continue;
+                if (j[i] < nRelRows) rel[(int64_t)j[i] * nCounters + c0 + i] = f[i];
+                j[i]++;
+            }
+        }
+    };
+    for (; k + U <= nOps; k += U) {
+        uint32_t m4[U];
+        uint4 v4[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            m4[u] = *reinterpret_cast<const uint32_t*>(meta + (int64_t)(k + u) * nCounters + c0);
+            v4[u] = *reinterpret_cast<const uint4*>(val + (int64_t)(k + u) * nCounters + c0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) apply(m4[u], v4[u]);
+    }
+    for (; k < nOps; ++k) {
+        const uint32_t m4 = *reinterpret_cast<const uint32_t*>(meta + (int64_t)k * nCounters + c0);
+        const uint4 v4 = *reinterpret_cast<const uint4*>(val + (int64_t)k * nCounters + c0);
+        apply(m4, v4);
+    }
+    *reinterpret_cast<uint4*>(finalOut + c0) = make_uint4(c[0], c[1], c[2], c[3]);
+    if (bad && err != nullptr)
+        __hip_atomic_store(err, (int32_t)CCB_ERR_INVALID_VALUE, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One counter per thread: any nCounters.
+__global__ __launch_bounds__(256) void ccb_k_cnt_batch1(const uint32_t* __restrict__ val,
+                                                        const uint8_t* __restrict__ meta,
+                                                        int64_t nCounters, int32_t nOps,
+                                                        uint32_t* __restrict__ finalOut,
+                                                        uint8_t* __restrict__ rel,
+                                                        int32_t nRelRows, int32_t* err)
+{
+    const int64_t cidx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (cidx >= nCounters) return;
+    uint32_t c = 0;
+    int32_t j = 0;
+    bool bad = false;
+    for (int32_t k = 0; k < nOps; ++k) {
+        const uint32_t m = meta[(int64_t)k * nCounters + cidx];
+        const uint32_t v = val[(int64_t)k * nCounters + cidx];
+        uint8_t f = 0;
+        if (cnt_step(c, m, v, j < nRelRows, bad, f)) {
+            if (j < nRelRows) rel[(int64_t)j * nCounters + cidx] = f;
+            ++j;
+        }
+    }
+    finalOut[cidx] = c;
+    if (bad && err != nullptr)
+        __hip_atomic_store(err, (int32_t)CCB_ERR_INVALID_VALUE, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Stream-ordered record (CntNotify interfaces §4.2): one device-scope atomic
+// update of the count, after a release fence so that the producer stream's
+// earlier stores are visible to whoever is released by this record.
+__global__ void ccb_k_cnt_record(uint32_t* line, int32_t mode, uint32_t value)
+{
+    if (!leader()) return;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    switch (mode) {
+    case CCB_CNT_RECORD_SET_VALUE:
+        __hip_atomic_exchange(line, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+    case CCB_CNT_RECORD_ADD:
+        __hip_atomic_fetch_add(line, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+    case CCB_CNT_RECORD_BIT_OR:
+        __hip_atomic_fetch_or(line, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+    case CCB_CNT_RECORD_BIT_AND:
+        __hip_atomic_fetch_and(line, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+    default:
+        break;
+    }
+}
+
+// Stream-ordered wait (CntNotify interfaces §4.3): poll the count until the
+// predicate holds or the timeout passes.  A release with isClear swaps the
+// count it saw for 0 in one compare-and-swap, so a record landing between
+// the check and the clear makes the swap fail and the wait looks again.
+// The outcome goes to word 1 of the handle's line.
+__global__ void ccb_k_cnt_wait(uint32_t* line, int32_t mode, uint32_t value, int32_t isClear,
+                               uint64_t timeoutTicks)
+{
+    if (!leader()) return;
+    int32_t* outcome = reinterpret_cast<int32_t*>(line + 1);
+    const uint64_t t0 = wall_clock64();
+    int32_t result = CCB_ERR_TIMEOUT;
+    for (;;) {
+        uint32_t c = __hip_atomic_load(line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bool bad;
+        if (cnt_holds(c, (uint32_t)mode, value, bad)) {
+            if (!isClear) { result = CCB_OK; break; }
+            if (__hip_atomic_compare_exchange_strong(line, &c, 0u, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                result = CCB_OK;
+                break;
+            }
+            continue;  // the count moved under us: evaluate the new value
+        }
+        if (timeoutTicks != 0 && wall_clock64() - t0 >= timeoutTicks) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __hip_atomic_store(outcome, result, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Stream-ordered reset (CntNotify interfaces §4.4).
+__global__ void ccb_k_cnt_reset(uint32_t* line)
+{
+    if (!leader()) return;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_store(line, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Zero fill (used instead of a memset so that captured graphs hold no
+// memset nodes).
+__global__ void ccb_k_fill_zero(int32_t* p, int64_t nWords)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nWords;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// Floor microbenchmarks.
+// ---------------------------------------------------------------------------
+// kind 0: dependent fetch-adds; kind 1: dependent atomic loads.  The address
+// of each op depends on the previous result through `zero` (always 0), so
+// the ops cannot overlap.
+__global__ void ccb_k_atomic_chain(int32_t* line, uint64_t* ticks, int32_t iters, int32_t fenced,
+                                   int32_t kind, int32_t zero)
+{
+    if (!leader()) return;
+    int32_t v = 0;
+    const uint64_t t0 = wall_clock64();
+    if (kind == 0) {
+        for (int32_t i = 0; i < iters; ++i) {
+            if (fenced) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            v = __hip_atomic_fetch_add(line + (v & zero), 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            if (fenced) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+    } else {
+        for (int32_t i = 0; i < iters; ++i) {
+            if (fenced) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            v = __hip_atomic_load(line + (v & zero), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (fenced) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+    }
+    const uint64_t t1 = wall_clock64();
+    ticks[0] = t0;
+    ticks[1] = t1;
+    if (v == 0x7fffffff) ticks[0] = 0;  // keep v live
+}
+
+__global__ void ccb_k_atomic_contended(int32_t* line, uint64_t* ticks, int32_t iters, int32_t zero)
+{
+    if (!leader()) return;
+    int32_t v = 0;
+    const uint64_t t0 = wall_clock64();
+    for (int32_t i = 0; i < iters; ++i)
+        v = __hip_atomic_fetch_add(line + (v & zero), 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t t1 = wall_clock64();
+    ticks[2 * blockIdx.x] = t0;
+    ticks[2 * blockIdx.x + 1] = t1;
+    if (v == 0x7fffffff) ticks[2 * blockIdx.x] = 0;
+}
+
+__global__ __launch_bounds__(256) void ccb_k_copy(int4* __restrict__ dst,
+                                                  const int4* __restrict__ src, int64_t n16)
+{
+    constexpr int U = 4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        int4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u) dst[i + u * stride] = v[u];
+    }
+    for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+// Launch helpers (called by the validated C entry points in ccb_api.hip).
+// ---------------------------------------------------------------------------
+namespace ccb {
+
+static hipError_t coop(const void* fn, int nGrid, int threads, size_t lds, hipStream_t s,
+                       void** args)
+{
+    return hipLaunchCooperativeKernel(fn, dim3(nGrid), dim3(threads), args, (unsigned)lds, s);
+}
+
+#define CCB_PICK(kernel, mode)                                                                  \
+    ((mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_ORDER)                                     \
+         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_ORDER>)                   \
+     : (mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_FULL)                                    \
+         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_FULL>)                    \
+     : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_ORDER)                                      \
+         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_ORDER>)                             \
+         : reinterpret_cast<const void*>(&kernel<1, CCB_VIS_FULL>))
+
+const void* kernel_ptr(KernelId id, int32_t mode)
+{
+    switch (id) {
+    case KernelId::BarrierOnly: return CCB_PICK(ccb_k_barrier_only, mode);
+    case KernelId::SlotRounds: return CCB_PICK(ccb_k_slot_rounds, mode);
+    case KernelId::GroupedRounds: return CCB_PICK(ccb_k_grouped_rounds, mode);
+    case KernelId::Stencil: return CCB_PICK(ccb_k_stencil, mode);
+    }
+    return nullptr;
+}
+
+hipError_t launch_barrier_only(const LaunchShape& ls, int32_t* ws, uint32_t* placement,
+                               int32_t* wgStatus, int32_t rounds, int32_t nMembers,
+                               uint32_t maxPoll)
+{
+    void* args[] = {&ws, &placement, &wgStatus, &rounds, &nMembers, &maxPoll};
+    return coop(ls.fn, ls.nGrid, ls.threads, ls.lds, ls.stream, args);
+}
+
+hipError_t launch_slot_rounds(const LaunchShape& ls, int32_t* ws, uint32_t* slots, uint32_t* out,
+                              int32_t* wgStatus, uint64_t seed, int32_t rounds, int32_t nMembers,
+                              uint32_t maxPoll)
+{
+    void* args[] = {&ws, &slots, &out, &wgStatus, &seed, &rounds, &nMembers, &maxPoll};
+    return coop(ls.fn, ls.nGrid, ls.threads, ls.lds, ls.stream, args);
+}
+
+hipError_t launch_grouped_rounds(const LaunchShape& ls, int32_t* ws, uint32_t* slots,
+                                 uint32_t* out, int32_t* wgStatus, uint64_t seed, int32_t rounds,
+                                 uint32_t maxPoll)
+{
+    void* args[] = {&ws, &slots, &out, &wgStatus, &seed, &rounds, &maxPoll};
+    return coop(ls.fn, ls.nGrid, ls.threads, ls.lds, ls.stream, args);
+}
+
+hipError_t launch_stencil(const LaunchShape& ls, int32_t* bufA, int32_t* bufB, int64_t n,
+                          int32_t iters, int32_t* ws, int32_t* halo, int64_t span,
+                          uint32_t maxPoll)
+{
+    void* args[] = {&bufA, &bufB, &n, &iters, &ws, &halo, &span, &maxPoll};
+    return coop(ls.fn, ls.nGrid, ls.threads, ls.lds, ls.stream, args);
+}
+
+hipError_t launch_cnt_batch(const uint32_t* val, const uint8_t* meta, int64_t nCounters,
+                            int32_t nOps, uint32_t* finalOut, uint8_t* rel, int32_t nRelRows,
+                            int32_t* err, bool vec4, hipStream_t s)
+{
+    constexpr int kThreads = 256;
+    if (vec4) {
+        const int64_t nThreads = nCounters / 4;
+        const int64_t nBlocks = (nThreads + kThreads - 1) / kThreads;
+        hipLaunchKernelGGL((ccb_k_cnt_batch4<kCntUnroll>), dim3((unsigned)nBlocks), dim3(kThreads),
+                           0, s, val, meta, nCounters, nOps, finalOut, rel, nRelRows, err);
+    } else {
+        const int64_t nBlocks = (nCounters + kThreads - 1) / kThreads;
+        hipLaunchKernelGGL(ccb_k_cnt_batch1, dim3((unsigned)nBlocks), dim3(kThreads), 0, s, val,
+                           meta, nCounters, nOps, finalOut, rel, nRelRows, err);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_cnt_record(uint32_t* line, int32_t mode, uint32_t value, hipStream_t s)
+{
+    hipLaunchKernelGGL(ccb_k_cnt_record, dim3(1), dim3(kWave), 0, s, line, mode, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_cnt_wait(uint32_t* line, int32_t mode, uint32_t value, int32_t isClear,
+                           uint64_t timeoutTicks, hipStream_t s)
+{
+    hipLaunchKernelGGL(ccb_k_cnt_wait, dim3(1), dim3(kWave), 0, s, line, mode, value, isClear,
+                       timeoutTicks);
+    return hipGetLastError();
+}
+
+hipError_t launch_cnt_reset(uint32_t* line, hipStream_t s)
+{
+    hipLaunchKernelGGL(ccb_k_cnt_reset, dim3(1), dim3(kWave), 0, s, line);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(int32_t* p, int64_t nWords, hipStream_t s)
+{
+    const int64_t blocks = nWords / 256 + 1 < 1024 ? nWords / 256 + 1 : 1024;
+    hipLaunchKernelGGL(ccb_k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, s, p, nWords);
+    return hipGetLastError();
+}
+
+hipError_t launch_atomic_chain(int32_t* line, uint64_t* ticks, int32_t iters, int32_t fenced,
+                               int32_t kind, hipStream_t s)
+{
+    hipLaunchKernelGGL(ccb_k_atomic_chain, dim3(1), dim3(kWave), 0, s, line, ticks, iters, fenced,
+                       kind, 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_atomic_contended(int32_t* line, uint64_t* ticks, int32_t iters, int32_t nGrid,
+                                   hipStream_t s)
+{
+    int32_t zero = 0;
+    void* args[] = {&line, &ticks, &iters, &zero};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&ccb_k_atomic_contended),
+                                      dim3(nGrid), dim3(kWave), args, 0, s);
+}
+
+hipError_t launch_copy(int4* dst, const int4* src, int64_t n16, int nBlocks, hipStream_t s)
+{
+    hipLaunchKernelGGL(ccb_k_copy, dim3(nBlocks), dim3(256), 0, s, dst, src, n16);
+    return hipGetLastError();
+}
+
+}  // namespace ccb

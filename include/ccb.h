@@ -1,0 +1,384 @@
+/*
+ * ccb.h -- C ABI of the MI355X (gfx950) soft epoch barrier and CntNotify
+ * library (libccb.so).
+ *
+ * Two pages define what this library computes:
+ *   [SYNCALL]   "PTO-ISA 跨核同步屏障 SYNCALL 实战指南" (PTO-ISA cross-core
+ *               barrier SYNCALL guide) -- the Soft (global-memory atomic
+ *               counter) barrier: §2 semantics, §4.1 workspace, §4.2
+ *               usedCores, §5.2 the epoch algorithm, §6.1-§6.3 usage rules,
+ *               §7.2 partial participation, §8 tests and idle marks.
+ *   [CNTNOTIFY] "CANN Runtime CntNotify（计数型通知）管理接口详解" (CANN Runtime
+ *               CntNotify interfaces) -- §3.1 record modes, §3.2 wait modes,
+ *               §3.3 info structs, §4.1-§4.6 the six calls, §5 usage, §7 advice.
+ *
+ * Conventions for every call below.
+ *   - Every call returns a ccbStatus; 0 is success ([CNTNOTIFY] §4).
+ *   - Pointers documented as "device" point to GPU memory that the CALLER
+ *     allocated and owns (for example a torch tensor's data_ptr()); the
+ *     library never frees them.  Pointers documented as "host" point to host
+ *     memory.
+ *   - ccbStream is a hipStream_t passed as an opaque pointer; NULL is the
+ *     default (null) stream ([CNTNOTIFY] §5).  Calls that take a stream only
+ *     enqueue work on it and return without waiting, unless stated otherwise.
+ *   - Calls act on the HIP device that is current on the calling thread.
+ *     That device must be a gfx950 GPU, else CCB_ERR_UNSUPPORTED_DEVICE.
+ *   - Arguments are validated before anything is enqueued; on an error
+ *     return nothing has been enqueued and no output has been written.
+ */
+#ifndef CCB_H
+#define CCB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CCB_API __attribute__((visibility("default")))
+
+typedef int32_t ccbStatus;
+typedef void* ccbStream; /* hipStream_t; NULL = default stream */
+
+enum {
+    CCB_OK = 0,
+    CCB_ERR_INVALID_VALUE = 1,      /* bad size, count, mode code, flag, alignment */
+    CCB_ERR_NULL_POINTER = 2,       /* a required pointer is NULL */
+    CCB_ERR_INVALID_HANDLE = 3,     /* unknown or destroyed CntNotify handle */
+    CCB_ERR_RESOURCE_EXHAUSTED = 4, /* CntNotify pool full ([CNTNOTIFY] §4.1) */
+    CCB_ERR_TIMEOUT = 5,            /* a CntNotify wait expired ([CNTNOTIFY] §3.3) */
+    CCB_ERR_DEADLOCK = 6,           /* a barrier poll hit its bound ([SYNCALL] §5.2) */
+    CCB_ERR_NOT_CORESIDENT = 7,     /* the grid cannot be resident at once ([SYNCALL] §6.3) */
+    CCB_ERR_UNSUPPORTED_DEVICE = 8, /* current device is not gfx950 */
+    CCB_ERR_HIP = 9,                /* the HIP runtime reported an error */
+    CCB_ERR_NOT_READY = 10          /* no CntNotify wait has completed yet */
+};
+
+/* Default poll bound of the soft barrier: [SYNCALL] §5.2 bounds the poll at
+ * one million iterations before reporting a possible deadlock. */
+#define CCB_SOFT_MAX_POLL 1000000u
+
+/* Bytes of one workspace line.  [SYNCALL] §4.1 gives each counter a cache
+ * line of its own (64 B on the pages' hardware); gfx950's L2 line is 128 B. */
+#define CCB_LINE_BYTES 128
+
+/* Counter stripes reserved per barrier in a workspace (see ccb_device.h). */
+#define CCB_STRIPES 32
+
+/* Barrier variant used by a workload launcher: one counter layout ORed with
+ * one visibility strength.
+ *   CCB_BARRIER_STRIPED   the counter split over CCB_STRIPES lines; member m
+ *                         arrives on stripe m mod CCB_STRIPES and one wave
+ *                         polls every stripe with a single gather load
+ *   CCB_BARRIER_FLAT      the pages' single counter ([SYNCALL] §5.2)
+ *   CCB_VISIBILITY_ORDER  arrival plus ordering of each thread's memory
+ *                         operations, no cache maintenance ([SYNCALL] §6.1);
+ *                         the workloads then share data through
+ *                         device-coherent accesses
+ *   CCB_VISIBILITY_FULL   agent-scope release and acquire fences around the
+ *                         arrival and poll; the workloads share data through
+ *                         plain accesses */
+enum {
+    CCB_BARRIER_STRIPED = 0,
+    CCB_BARRIER_FLAT = 1,
+    CCB_VISIBILITY_ORDER = 0,
+    CCB_VISIBILITY_FULL = 2
+};
+
+/* CntNotify mode codes, as enumerated in [CNTNOTIFY] §3.1 and §3.2. */
+enum {
+    CCB_CNT_RECORD_SET_VALUE = 0, /* count = value */
+    CCB_CNT_RECORD_ADD = 1,       /* count = count + value (mod 2^32) */
+    CCB_CNT_RECORD_BIT_OR = 2,    /* count = count | value */
+    CCB_CNT_RECORD_BIT_AND = 4    /* count = count & value (there is no code 3) */
+};
+enum {
+    CCB_CNT_WAIT_LESS = 0,              /* release when count <  value */
+    CCB_CNT_WAIT_EQUAL = 1,             /* release when count == value */
+    CCB_CNT_WAIT_BIGGER = 2,            /* release when count >  value */
+    CCB_CNT_WAIT_BIGGER_OR_EQUAL = 3,   /* release when count >= value */
+    CCB_CNT_WAIT_EQUAL_WITH_BITMASK = 4 /* release when (count & value) == value */
+};
+
+/* ========================================================================
+ * Miscellaneous
+ * ======================================================================== */
+
+/* Human-readable name of a status code (static string, never NULL). */
+CCB_API const char* ccb_status_string(ccbStatus s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+CCB_API int32_t ccb_version(void);
+
+/* Checks that the current device is gfx950 and fills (each may be NULL):
+ * number of compute units, LDS bytes per CU, wall-clock rate in kHz.
+ * Errors: CCB_ERR_UNSUPPORTED_DEVICE, CCB_ERR_HIP. */
+CCB_API ccbStatus ccb_device_info(int32_t* numCUs, int32_t* ldsPerCU, int32_t* wallClockKHz);
+
+/* ========================================================================
+ * Soft epoch barrier ([SYNCALL] §4.1, §4.2, §5.2)
+ *
+ * Workspace layout.  A workspace for k barriers is (k * CCB_STRIPES + 1)
+ * lines of CCB_LINE_BYTES bytes, 128-byte aligned, device memory owned by
+ * the caller:
+ *   lines b*CCB_STRIPES .. (b+1)*CCB_STRIPES-1: the counter stripes of
+ *        barrier b, an int32 at byte 0 of each line; the other 124 bytes are
+ *        reserved and never shared with data ([SYNCALL] §4.1).  A FLAT
+ *        barrier uses only its first stripe;
+ *   line k*CCB_STRIPES: int32 error word at byte 0 (CCB_OK, or
+ *        CCB_ERR_DEADLOCK once any member's poll hit its bound).
+ * Every stripe must be zero (or a multiple of its participant count) when a
+ * launch starts ([SYNCALL] §4.1); ccb_syncall_workspace_reset zeroes the
+ * workspace.  A stripe stays valid while the number of arrivals on it since
+ * the last reset plus the participant count stays below 2^31.
+ *
+ * Every workload launcher below runs one persistent grid in which each
+ * workgroup is resident for the whole launch ([SYNCALL] §6.3: the
+ * participant set is fixed by the launch).  The launcher checks the
+ * occupancy first and returns CCB_ERR_NOT_CORESIDENT when nGrid workgroups of
+ * `threads` threads cannot all be resident at once.  `wgsPerCu` > 0 also
+ * sizes each workgroup's LDS so that at most that many share a compute unit
+ * (0 = no shaping).  `maxPoll` bounds each barrier's poll loop (0 = the
+ * default CCB_SOFT_MAX_POLL); a member that exhausts it sets the error word
+ * and leaves its round loop, and so does every member that then sees the
+ * error word -- no launch traps or hangs.  `mode` picks the barrier variant
+ * (CCB_BARRIER_* | CCB_VISIBILITY_*); any other value is INVALID_VALUE.  Read
+ * the outcome with ccb_syncall_status after the stream has run the launch.
+ * ======================================================================== */
+
+/* Size in bytes of a workspace for nBarriers barriers:
+ * (nBarriers * CCB_STRIPES + 1) * CCB_LINE_BYTES. */
+CCB_API size_t ccb_syncall_workspace_bytes(uint32_t nBarriers);
+
+/* Enqueue a zero fill of a workspace of nBarriers barriers (device, 128-B
+ * aligned, ccb_syncall_workspace_bytes(nBarriers) bytes).
+ * Errors: NULL_POINTER, INVALID_VALUE (nBarriers == 0 or misaligned). */
+CCB_API ccbStatus ccb_syncall_workspace_reset(int32_t* ws, uint32_t nBarriers, ccbStream stream);
+
+/* Wait for `stream`, then read the error word of a workspace of nBarriers
+ * barriers and (optionally, arrivals may be NULL) store in arrivals[b] the
+ * total number of arrivals on barrier b (the sum of its stripes).  Returns
+ * CCB_OK or CCB_ERR_DEADLOCK (or HIP errors).  Blocks the host thread. */
+CCB_API ccbStatus ccb_syncall_status(const int32_t* ws, uint32_t nBarriers, int32_t* arrivals,
+                                     ccbStream stream);
+
+/* Barrier-only persistent grid: `rounds` consecutive soft barriers on
+ * counter 0 of `ws` (1 counter), with participants chosen as in [SYNCALL]
+ * §4.2 and §7.2: usedCores == 0 means all nGrid workgroups; otherwise
+ * workgroups 0..usedCores-1 take part and the others return at once without
+ * calling the barrier.
+ *   ws         device, workspace of 1 barrier
+ *   placement  device, 2 * nGrid uint32, may be NULL: per workgroup w the
+ *              hardware location it ran on: [2w] = the HW_ID register
+ *              (CU id bits 8-11, SH id bit 12, SE id bits 13-15), [2w+1] = the
+ *              XCC (XCD) id
+ *   wgStatus   device, nGrid int32, may be NULL: 1 member finished, 2 idle
+ *              (ran, skipped the barrier: the idle mark of [SYNCALL] §8),
+ *              3 member stopped on the error word
+ * Errors: NULL_POINTER, INVALID_VALUE (rounds < 0, nGrid < 1, threads not a
+ * multiple of 64 in [64, 1024], usedCores < 0 or > nGrid), NOT_CORESIDENT. */
+CCB_API ccbStatus ccb_run_barrier_only(int32_t* ws, uint32_t* placement, int32_t* wgStatus,
+                                       int32_t rounds, int32_t nGrid, int32_t threads,
+                                       int32_t usedCores, int32_t wgsPerCu, uint32_t maxPoll,
+                                       int32_t mode, ccbStream stream);
+
+/* Witness rounds on one counter ([SYNCALL] §6.1's pattern of slots written
+ * before a barrier and read after it).  For r = 0..rounds-1 every member w
+ * stores hash(seed, r, w) into its slot of ring row r mod 4, passes the
+ * barrier, then stores the sum (mod 2^32) of every member's row-(r mod 4)
+ * slot into out[r * nGrid + w].  hash is SplitMix64 output number
+ * r * 2^32 + w + 1 for seed `seed`, high 32 bits.  Members are chosen by
+ * usedCores as in ccb_run_barrier_only; non-members write no slot and no
+ * output.
+ *   ws        device, workspace of 1 barrier (zeroed)
+ *   slots     device, 4 * nGrid uint32 scratch (contents on entry ignored)
+ *   out       device, rounds * nGrid uint32; entries of non-members untouched
+ *   wgStatus  device, nGrid int32 (see ccb_run_barrier_only), may be NULL
+ * Errors: as ccb_run_barrier_only, plus NULL_POINTER for slots/out (which
+ * may be NULL only when rounds == 0). */
+CCB_API ccbStatus ccb_run_slot_rounds(int32_t* ws, uint32_t* slots, uint32_t* out,
+                                      int32_t* wgStatus, uint64_t seed, int32_t rounds,
+                                      int32_t nGrid, int32_t threads, int32_t usedCores,
+                                      int32_t wgsPerCu, uint32_t maxPoll, int32_t mode,
+                                      ccbStream stream);
+
+/* Grouped witness rounds on three barriers: group A = even workgroup ids on
+ * barrier 0, group B = odd ids on barrier 1, "mix" = every workgroup on
+ * barrier 2.  Round r is an A round when r mod 3 == 0, B when 1, mix when 2;
+ * its members store hash(seed, r, w), pass that group's barrier (N = nGrid/2
+ * for A and B, nGrid for mix) and store the sum of the round's members'
+ * slots into out[r * nGrid + w].  Non-members of a round do nothing in it.
+ * Every member enters each counter's barriers in the same order the same
+ * number of times ([SYNCALL] §6.2).
+ *   ws     device, workspace of 3 barriers (zeroed)
+ *   slots  device, 4 * nGrid uint32 scratch
+ *   out    device, rounds * nGrid uint32
+ * Errors: as ccb_run_slot_rounds; nGrid must be even. */
+CCB_API ccbStatus ccb_run_grouped_rounds(int32_t* ws, uint32_t* slots, uint32_t* out,
+                                         int32_t* wgStatus, uint64_t seed, int32_t rounds,
+                                         int32_t nGrid, int32_t threads, int32_t wgsPerCu,
+                                         uint32_t maxPoll, int32_t mode, ccbStream stream);
+
+/* Persistent barrier-separated stencil.  Iteration t reads buffer t & 1 and
+ * writes buffer (t + 1) & 1 (buffer 0 = bufA, 1 = bufB):
+ *   y[i] = (x[i-1] + 2 x[i] + x[i+1]) >> 2,  x[-1] = x[0], x[n] = x[n-1],
+ * with one soft barrier over all nGrid workgroups between consecutive
+ * iterations (iters - 1 barriers).  The result is in bufA when iters is even,
+ * in bufB when odd.  The caller guarantees |x| < 2^29 so that the int32 sum
+ * cannot overflow.  Each wave owns one contiguous span of the array in every
+ * iteration, so only two halo elements per span cross workgroups; with
+ * CCB_VISIBILITY_ORDER they go through `halo`.
+ *   bufA, bufB  device, n int32 each, 16-B aligned, not overlapping
+ *   ws          device, workspace of 1 barrier (zeroed)
+ *   halo        device, ccb_stencil_halo_bytes(nGrid, threads) bytes of
+ *               scratch (contents ignored); may be NULL with
+ *               CCB_VISIBILITY_FULL
+ * Errors: NULL_POINTER, INVALID_VALUE (n < 1, iters < 0, misaligned or
+ * overlapping buffers, bad nGrid/threads), NOT_CORESIDENT. */
+CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32_t iters,
+                                  int32_t* ws, int32_t* halo, int32_t nGrid, int32_t threads,
+                                  int32_t wgsPerCu, uint32_t maxPoll, int32_t mode,
+                                  ccbStream stream);
+
+/* Bytes of the halo exchange scratch ccb_run_stencil needs with
+ * CCB_VISIBILITY_ORDER: 16 bytes per wave (nGrid * threads / 64 waves). */
+CCB_API size_t ccb_stencil_halo_bytes(int32_t nGrid, int32_t threads);
+
+/* ========================================================================
+ * Floor microbenchmarks (the barrier's latency and bandwidth roofline)
+ * ======================================================================== */
+
+/* One lane runs `iters` dependent agent-scope fetch-adds of 1 on the int32 at
+ * byte 0 of `line` (device, 128-B aligned, exclusive).  fenced != 0 wraps
+ * each one in an agent-scope release fence before and acquire fence after.
+ * kind 1 runs dependent agent-scope atomic loads instead of fetch-adds.
+ * ticksOut (device, 2 uint64): wall-clock ticks at start and end (rate from
+ * ccb_device_info).  Errors: NULL_POINTER, INVALID_VALUE (iters < 1, kind). */
+CCB_API ccbStatus ccb_bench_atomic_chain(int32_t* line, uint64_t* ticksOut, int32_t iters,
+                                         int32_t fenced, int32_t kind, ccbStream stream);
+
+/* nGrid workgroups, lane 0 of each runs `iters` dependent agent-scope
+ * fetch-adds of 1 on the same int32 (device, 128-B line).  Final value grows
+ * by nGrid * iters.  ticksOut (device, 2 * nGrid uint64): per workgroup
+ * start/end ticks.  Errors: NULL_POINTER, INVALID_VALUE, NOT_CORESIDENT. */
+CCB_API ccbStatus ccb_bench_atomic_contended(int32_t* line, uint64_t* ticksOut, int32_t iters,
+                                             int32_t nGrid, ccbStream stream);
+
+/* Streaming copy of nBytes (multiple of 16) from src to dst (device, 16-B
+ * aligned, not overlapping): the achievable HBM ceiling for the data phases.
+ * Errors: NULL_POINTER, INVALID_VALUE. */
+CCB_API ccbStatus ccb_bench_copy(void* dst, const void* src, int64_t nBytes, ccbStream stream);
+
+/* ========================================================================
+ * CntNotify ([CNTNOTIFY] §3, §4)
+ *
+ * A CntNotify is an opaque handle ([CNTNOTIFY] §1) owned by the library.
+ * Its uint32 count lives alone on a 128-byte line of a fixed pool of
+ * CCB_CNT_NOTIFY_POOL lines in the device memory of the device that was
+ * current at create time; every call on a handle must run with that device
+ * current.  Record, wait and reset only enqueue work on their stream
+ * ([CNTNOTIFY] §4.2-§4.4, §7): the host thread never waits for them.
+ * Handle calls are thread-safe (one mutex guards the handle table).
+ * ======================================================================== */
+
+#define CCB_CNT_NOTIFY_POOL 1024
+
+typedef struct ccbCntNotify_st* ccbCntNotify;
+
+/* [CNTNOTIFY] §3.3: record descriptor. mode: CCB_CNT_RECORD_*. 8 bytes. */
+typedef struct {
+    int32_t mode;
+    uint32_t value;
+} ccbCntRecordInfo;
+
+/* [CNTNOTIFY] §3.3: wait descriptor. mode: CCB_CNT_WAIT_*; timeout in
+ * seconds, 0 = wait forever; isClear = 1 zeroes the count after the wait has
+ * been released, 0 leaves it; rev must be zero.  16 bytes. */
+typedef struct {
+    int32_t mode;
+    uint32_t value;
+    uint32_t timeout;
+    uint8_t isClear;
+    uint8_t rev[3];
+} ccbCntWaitInfo;
+
+/* [CNTNOTIFY] §4.1.  *out receives a new handle whose count is 0.  flag is
+ * reserved and must be 0.  Blocks the host (it initialises the line).
+ * Errors: NULL_POINTER (out), INVALID_VALUE (flag != 0), RESOURCE_EXHAUSTED
+ * (all CCB_CNT_NOTIFY_POOL lines in use), UNSUPPORTED_DEVICE, HIP. */
+CCB_API ccbStatus ccb_cnt_notify_create(ccbCntNotify* out, uint64_t flag);
+
+/* [CNTNOTIFY] §4.2.  Enqueue on `stream` one update of the count by
+ * info->mode / info->value (stream is where the counted event happens).
+ * The update is atomic at device scope and is ordered after everything
+ * enqueued earlier on `stream`.
+ * Errors: INVALID_HANDLE, NULL_POINTER (info), INVALID_VALUE (mode). */
+CCB_API ccbStatus ccb_cnt_notify_record(ccbCntNotify h, ccbStream stream,
+                                        const ccbCntRecordInfo* info);
+
+/* [CNTNOTIFY] §4.3.  Enqueue on `stream` a wait that blocks the stream's
+ * later work until the predicate info->mode / info->value holds for the
+ * count, or until info->timeout seconds have passed (0 = no limit).  When it
+ * is released and isClear is 1 the count is set to 0 atomically with the
+ * check that released it (a concurrent record is never lost).  The outcome
+ * (CCB_OK or CCB_ERR_TIMEOUT) is stored with the handle; read it with
+ * ccb_cnt_notify_query.  A timed-out wait does not clear.
+ * Errors: INVALID_HANDLE, NULL_POINTER (info), INVALID_VALUE (mode,
+ * isClear > 1, rev not zero). */
+CCB_API ccbStatus ccb_cnt_notify_wait(ccbCntNotify h, ccbStream stream,
+                                      const ccbCntWaitInfo* info);
+
+/* [CNTNOTIFY] §4.4.  Enqueue on `stream` a reset of the count to 0.
+ * Errors: INVALID_HANDLE. */
+CCB_API ccbStatus ccb_cnt_notify_reset(ccbCntNotify h, ccbStream stream);
+
+/* [CNTNOTIFY] §4.5.  *id receives the handle's id (its pool line index,
+ * stable for the handle's life; reused after destroy).
+ * Errors: INVALID_HANDLE, NULL_POINTER (id). */
+CCB_API ccbStatus ccb_cnt_notify_get_id(ccbCntNotify h, uint32_t* id);
+
+/* [CNTNOTIFY] §4.6.  Return the handle's line to the pool; the handle is
+ * invalid afterwards (later calls on it return CCB_ERR_INVALID_HANDLE).  The
+ * caller must not destroy a handle that queued work still uses.
+ * Errors: INVALID_HANDLE. */
+CCB_API ccbStatus ccb_cnt_notify_destroy(ccbCntNotify h);
+
+/* Test and diagnostics hook (not on the pages): wait for `stream`, then copy
+ * the current count to *value and the outcome of the last completed wait to
+ * *lastWait (CCB_OK, CCB_ERR_TIMEOUT, or CCB_ERR_NOT_READY if none has
+ * completed since create).  Either pointer may be NULL.  Blocks the host.
+ * Errors: INVALID_HANDLE, HIP. */
+CCB_API ccbStatus ccb_cnt_notify_query(ccbCntNotify h, uint32_t* value, ccbStatus* lastWait,
+                                       ccbStream stream);
+
+/* Batched CntNotify engine: nCounters independent counts, each starting at
+ * 0, each applying nOps operations in order k = 0..nOps-1.  Inputs are
+ * op-major device arrays:
+ *   val[k * nCounters + c]   uint32 operand
+ *   meta[k * nCounters + c]  uint8: bits 0-2 mode code, bit 3 isClear (waits
+ *                            only), bits 4-6 zero, bit 7 = 1 for a wait,
+ *                            0 for a record
+ * Records follow [CNTNOTIFY] §3.1; a wait evaluates the §3.2 predicate on
+ * the current count, releases if it holds and then clears if isClear; with no
+ * concurrent writer a false predicate never becomes true, so it is not
+ * released and the count is unchanged.
+ * Outputs (device): final[c] uint32; rel[j * nCounters + c] uint8 = 1 if the
+ * j-th wait of counter c released, else 0 (j = 0.. per counter, at most
+ * nRelRows rows).
+ * A malformed op (bad mode, reserved bit, isClear on a record, a wait beyond
+ * nRelRows) leaves the count unchanged, writes rel 0 for a wait that has a
+ * row, and sets *err (device int32, may be NULL) to CCB_ERR_INVALID_VALUE;
+ * *err is not written otherwise, so the caller zeroes it first.
+ * val, final must be 4-B aligned; nCounters * nOps may be 0.
+ * Errors: NULL_POINTER, INVALID_VALUE (negative sizes). */
+CCB_API ccbStatus ccb_cnt_notify_batch(const uint32_t* val, const uint8_t* meta,
+                                       int64_t nCounters, int32_t nOps, uint32_t* final_,
+                                       uint8_t* rel, int32_t nRelRows, int32_t* err,
+                                       ccbStream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCB_H */

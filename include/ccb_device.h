@@ -1,0 +1,206 @@
+/*
+ * ccb_device.h -- device-side soft epoch barrier for HIP kernels on gfx950.
+ *
+ * The in-kernel counterpart of the Soft SYNCALL of "PTO-ISA 跨核同步屏障
+ * SYNCALL 实战指南" (PTO-ISA SYNCALL guide), §5.2: every participant adds one
+ * to a counter in global memory, takes back the old value, derives from it
+ * the count at which its round is complete, and polls until the counter gets
+ * there.  The round number is implicit in the count (§5.2), so no per-core
+ * state is kept between barriers.
+ *
+ * Participants are workgroups whose thread count is a multiple of 64.  Every
+ * thread of a participating workgroup calls the barrier (uniform control
+ * flow); wave 0 does the arrival and the poll, and the workgroup's own
+ * barrier spreads the result.
+ *
+ * Striped counters.  On gfx950 a device-scope atomic on one address costs
+ * about 11 ns of that address's time, so N arrivals on a single counter take
+ * N * 11 ns one after another (2.9 us at 256 workgroups).  The counter is
+ * therefore split into K stripes, each an int32 alone on its own 128-byte
+ * line: member m arrives on stripe m mod K, whose participant count is
+ * n_s = ceil((N - s) / K).  Each stripe is an epoch counter of its own:
+ * from the old value its member derives the round e = before / n_s + 1 (the
+ * pages' target rule, target = e * n_s, applied per stripe), and the round is
+ * complete once every stripe l has reached e * n_l.  Wave 0 checks that with
+ * one gather load -- lane l reads stripe l.  With K = 1 this is exactly the
+ * pages' single-counter algorithm.  Because no member can arrive for round
+ * e + 1 before every member has arrived for round e, a stripe at or above
+ * e * n_l means all its members arrived for round e, and ">=" (not "==") is
+ * the correct poll condition (fast members may already be in round e + 1).
+ *
+ * Rules inherited from the pages:
+ *   - Every stripe must be zero (or a multiple of its n_s) before first use
+ *     ([SYNCALL] §4.1); each sits alone on its line.
+ *   - usedCores == 0 means every launched workgroup; an explicit count means
+ *     workgroups that are not members must never call ([SYNCALL] §4.2, §7.2).
+ *   - Every member enters the same barriers in the same order the same
+ *     number of times ([SYNCALL] §6.2).
+ *   - Every member must be resident at once; launch persistent grids
+ *     cooperatively ([SYNCALL] §6.3).
+ *
+ * Visibility -- two strengths:
+ *   CCB_VIS_FULL   agent-scope release fence before the arrival and acquire
+ *                  fence after the poll: plain global stores made before the
+ *                  barrier are visible to plain loads after it on every XCD.
+ *                  On gfx950 each fence is an L2 write-back / invalidate that
+ *                  the device serialises (about 7 ns each), so this costs
+ *                  about N * 14 ns per barrier.
+ *   CCB_VIS_ORDER  the pages' own contract ([SYNCALL] §6.1: the barrier
+ *                  counts arrivals, cache maintenance is the caller's): every
+ *                  thread's earlier memory operations have completed before
+ *                  the arrival, and later ones start after the release, but
+ *                  no cache is written back or invalidated.  Data that one
+ *                  workgroup writes before the barrier and another reads
+ *                  after it must go through ccb_store_coherent /
+ *                  ccb_load_coherent (device-coherent accesses).
+ *
+ * Failure.  The poll is bounded ([SYNCALL] §5.2 bounds it at 10^6 polls and
+ * asserts).  A GPU trap would kill the context, so instead the member that
+ * runs out of polls stores CCB_ERR_DEADLOCK into an error word and the call
+ * returns CCB_ERR_DEADLOCK; members still polling see the error word and
+ * return the same.  The caller must then leave its barrier loop.
+ */
+#ifndef CCB_DEVICE_H
+#define CCB_DEVICE_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ccb.h"
+
+/* s_sleep argument between polls (units of 64 clocks); 0 = no sleep. */
+#ifndef CCB_POLL_SLEEP
+#define CCB_POLL_SLEEP 1
+#endif
+
+/* How often (in polls) a waiting wave also looks at the error word. */
+#ifndef CCB_ERR_CHECK_EVERY
+#define CCB_ERR_CHECK_EVERY 64u
+#endif
+
+#define CCB_LINE_WORDS (CCB_LINE_BYTES / 4)
+
+enum ccbVisibility { CCB_VIS_FULL = 0, CCB_VIS_ORDER = 1 };
+
+/* Device-coherent accesses for data shared across a CCB_VIS_ORDER barrier. */
+__device__ __forceinline__ void ccb_store_coherent(int32_t* p, int32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ccb_store_coherent(uint32_t* p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ccb_load_coherent(const int32_t* p)
+{
+    return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ccb_load_coherent(const uint32_t* p)
+{
+    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+/* Wait until every memory operation this thread issued has completed. */
+__device__ __forceinline__ void ccb_wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+/* The barrier proper.
+ *   ctr      K stripe lines (stripe s: int32 at ctr[s * CCB_LINE_WORDS])
+ *   n        participant count (> 0)
+ *   member   this workgroup's index among the participants, 0..n-1
+ *   maxPoll  poll bound (> 0)
+ *   err      error word (on a line of its own)
+ * Every thread of the workgroup calls it.  Returns CCB_OK or
+ * CCB_ERR_DEADLOCK (the same value in every thread). */
+template <int K, ccbVisibility kVis>
+__device__ __forceinline__ int32_t ccb_barrier(int32_t* ctr, int32_t n, int32_t member,
+                                               uint32_t maxPoll, int32_t* err)
+{
+    static_assert(K >= 1 && K <= 64, "stripes are polled by one wave");
+    __shared__ int32_t ccb_result;
+    if (kVis == CCB_VIS_ORDER) ccb_wait_memory();  // this thread's accesses are done
+    __syncthreads();
+    const uint32_t tid = threadIdx.x + blockDim.x * (threadIdx.y + blockDim.y * threadIdx.z);
+    if (tid < 64) {  // wave 0
+        const int lane = (int)tid;
+        const int32_t ks = n < K ? n : K;  // stripes in use
+        int32_t epoch = 0;
+        if (lane == 0) {
+            // release: the workgroup's earlier global stores become visible at
+            // agent scope before the arrival can be observed
+            if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            const int32_t s = member % K;
+            const int32_t ns = (n - s + K - 1) / K;
+            const int32_t before = __hip_atomic_fetch_add(ctr + s * CCB_LINE_WORDS, 1,
+                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            epoch = before / ns + 1;
+        }
+        epoch = __shfl(epoch, 0, 64);
+        // stripe `lane` is complete for this round at epoch * n_lane arrivals
+        const int32_t need = lane < ks ? epoch * ((n - lane + K - 1) / K) : 0;
+        int32_t* mine = ctr + (lane < ks ? lane : 0) * CCB_LINE_WORDS;
+        int32_t rc = CCB_OK;
+        uint32_t polls = 0;
+        for (;;) {
+            const int32_t v = lane < ks ? __hip_atomic_load(mine, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT)
+                                        : 0;
+            if (__all(v >= need)) break;
+            if (++polls >= maxPoll) {
+                if (lane == 0)
+                    __hip_atomic_store(err, (int32_t)CCB_ERR_DEADLOCK, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                rc = CCB_ERR_DEADLOCK;
+                break;
+            }
+            if ((polls % CCB_ERR_CHECK_EVERY) == 0) {
+                const int32_t e = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (e != CCB_OK) {
+                    rc = CCB_ERR_DEADLOCK;
+                    break;
+                }
+            }
+            if (CCB_POLL_SLEEP > 0) __builtin_amdgcn_s_sleep(CCB_POLL_SLEEP);
+        }
+        // acquire: loads after the barrier see every member's released stores
+        if (kVis == CCB_VIS_FULL && lane == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (lane == 0) ccb_result = rc;
+    }
+    __syncthreads();
+    return ccb_result;
+}
+
+/* Linear index of this workgroup in the grid. */
+__device__ __forceinline__ int32_t ccb_block_linear()
+{
+    return (int32_t)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+}
+
+/* [SYNCALL] §3's Soft overload: ws is a workspace of one barrier
+ * (CCB_STRIPES stripe lines, then the error line), usedCores as in §4.2
+ * (members are the workgroups with linear index < usedCores).  Full
+ * visibility. */
+__device__ __forceinline__ int32_t ccb_syncall_soft(int32_t* ws, int32_t usedCores)
+{
+    const int32_t n = usedCores != 0 ? usedCores : (int32_t)(gridDim.x * gridDim.y * gridDim.z);
+    return ccb_barrier<CCB_STRIPES, CCB_VIS_FULL>(ws, n, ccb_block_linear(), CCB_SOFT_MAX_POLL,
+                                                  ws + CCB_STRIPES * CCB_LINE_WORDS);
+}
+
+/* The same barrier with the pages' arrival-only contract (CCB_VIS_ORDER). */
+__device__ __forceinline__ int32_t ccb_syncall_soft_ordered(int32_t* ws, int32_t usedCores)
+{
+    const int32_t n = usedCores != 0 ? usedCores : (int32_t)(gridDim.x * gridDim.y * gridDim.z);
+    return ccb_barrier<CCB_STRIPES, CCB_VIS_ORDER>(ws, n, ccb_block_linear(), CCB_SOFT_MAX_POLL,
+                                                   ws + CCB_STRIPES * CCB_LINE_WORDS);
+}
+
+/* The pages' single-counter barrier exactly (one counter line, full
+ * visibility); same workspace layout, only stripe 0 is used. */
+__device__ __forceinline__ int32_t ccb_syncall_soft_flat(int32_t* ws, int32_t usedCores)
+{
+    const int32_t n = usedCores != 0 ? usedCores : (int32_t)(gridDim.x * gridDim.y * gridDim.z);
+    return ccb_barrier<1, CCB_VIS_FULL>(ws, n, ccb_block_linear(), CCB_SOFT_MAX_POLL,
+                                        ws + CCB_STRIPES * CCB_LINE_WORDS);
+}
+
+#endif /* CCB_DEVICE_H */

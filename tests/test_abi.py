@@ -1,0 +1,128 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the
+headers declare, its structs have the documented layout, its constants match
+the pages' tables, and argument validation that precedes any device work
+returns the documented codes.  No compute call is made here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _declared():
+    names = set()
+    for fn in sorted(os.listdir(INCLUDE)):
+        if fn.endswith(".h"):
+            text = open(os.path.join(INCLUDE, fn)).read()
+            names |= set(re.findall(r"CCB_API\s+[\w\s\*]+?\b(ccb_\w+)\s*\(", text))
+    return names
+
+
+def _header_enum(name_prefix):
+    text = open(os.path.join(INCLUDE, "ccb.h")).read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(rf"\b({name_prefix}\w*)\s*=\s*(\d+)", text)}
+
+
+@pytest.fixture(scope="module")
+def ccb():
+    from cross_core_barrier_amd import ccb as lib
+    return lib
+
+
+def test_library_exports_every_declared_symbol(ccb):
+    lib = ctypes.CDLL(ccb.LIB_PATH)
+    declared = _declared()
+    assert len(declared) >= 20
+    missing = [n for n in sorted(declared) if not hasattr(lib, n)]
+    assert missing == []
+    assert set(ccb.EXPORTED) == declared
+
+
+def test_struct_layouts(ccb):
+    assert ctypes.sizeof(ccb.ccbCntRecordInfo) == 8
+    assert ctypes.sizeof(ccb.ccbCntWaitInfo) == 16
+    assert ccb.ccbCntWaitInfo.isClear.offset == 12
+    assert ccb.ccbCntWaitInfo.rev.offset == 13
+
+
+def _golden(name):
+    rows = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                code, label, _ = line.split()
+                rows[label] = int(code)
+    return rows
+
+
+def test_mode_codes_match_pages():
+    rec = _header_enum("CCB_CNT_RECORD_")
+    wait = _header_enum("CCB_CNT_WAIT_")
+    assert {k[len("CCB_CNT_RECORD_"):]: v for k, v in rec.items()} == _golden("cntnotify_record_modes.txt")
+    assert {k[len("CCB_CNT_WAIT_"):]: v for k, v in wait.items()} == _golden("cntnotify_wait_modes.txt")
+
+
+def test_status_codes_consistent(ccb):
+    hdr = _header_enum("CCB_ERR_")
+    for name, val in hdr.items():
+        assert getattr(ccb, name) == val
+        assert ccb.ccb_status_string(val) == name
+    assert ccb.ccb_status_string(0) == "CCB_OK"
+    assert ccb.ccb_version() >= 100
+
+
+def test_constants_match_pages(ccb):
+    consts = {}
+    with open(os.path.join(GOLDEN, "syncall_constants.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = line.split()
+                consts[k] = int(v)
+    text = open(os.path.join(INCLUDE, "ccb.h")).read()
+    m = re.search(r"#define CCB_SOFT_MAX_POLL (\d+)u", text)
+    assert int(m.group(1)) == consts["soft_max_poll_iterations"] == ccb.CCB_SOFT_MAX_POLL
+    assert ccb.ccb_syncall_workspace_bytes(1) == (ccb.CCB_STRIPES + 1) * 128
+    assert ccb.ccb_syncall_workspace_bytes(3) == (3 * ccb.CCB_STRIPES + 1) * 128
+    assert ccb.ccb_stencil_halo_bytes(1024, 256) == 1024 * 4 * 16
+    assert ccb.ccb_stencil_halo_bytes(0, 256) == 0
+
+
+def test_validation_before_device_work(ccb):
+    # CntNotify §4.1: flag must be 0; a null out-pointer is rejected
+    assert ccb.ccb_cnt_notify_create(1)[0] == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_cnt_notify_create(0, null_out=True)[0] == ccb.CCB_ERR_NULL_POINTER
+    # §6.1: an unknown handle is an error, not a crash
+    for bogus in (None, 1, 0x12345, (5 << 20) | 3):
+        assert ccb.ccb_cnt_notify_record(bogus, None, ccb.record_info(1, 1)) == ccb.CCB_ERR_INVALID_HANDLE
+        assert ccb.ccb_cnt_notify_wait(bogus, None, ccb.wait_info(3, 1, 1)) == ccb.CCB_ERR_INVALID_HANDLE
+        assert ccb.ccb_cnt_notify_reset(bogus) == ccb.CCB_ERR_INVALID_HANDLE
+        assert ccb.ccb_cnt_notify_get_id(bogus)[0] == ccb.CCB_ERR_INVALID_HANDLE
+        assert ccb.ccb_cnt_notify_destroy(bogus) == ccb.CCB_ERR_INVALID_HANDLE
+    # barrier launchers: null and malformed arguments
+    assert ccb.ccb_syncall_workspace_reset(None, 1) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_syncall_workspace_reset(128, 0) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_syncall_workspace_reset(64, 1) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_barrier_only(None, None, None, 1, 8, 64) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_run_barrier_only(128, None, None, -1, 8, 64) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_barrier_only(128, None, None, 1, 8, 100) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_barrier_only(128, None, None, 1, 8, 64, 9) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_slot_rounds(128, None, 256, None, 0, 1, 8, 64) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_run_grouped_rounds(128, 256, 256, None, 0, 1, 7, 64) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_stencil(None, 256, 10, 1, 128, 512, 1, 64) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_run_stencil(4096, 4096, 10, 1, 128, 512, 1, 64) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_stencil(4100, 8192, 10, 1, 128, 512, 1, 64) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_stencil(4096, 8192, 10, 1, 128, None, 1, 64) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_run_barrier_only(128, None, None, 1, 8, 64, mode=9) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_bench_atomic_chain(None, 256, 1) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_bench_atomic_chain(128, 256, 0) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_bench_copy(256, 512, 17) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_cnt_notify_batch(None, None, -1, 1, None, None, 1) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_cnt_notify_batch(None, None, 0, 1, None, None, 1) == ccb.CCB_OK
+    assert ccb.ccb_cnt_notify_batch(None, None, 4, 1, 256, 256, 1) == ccb.CCB_ERR_NULL_POINTER

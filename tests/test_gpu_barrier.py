@@ -1,0 +1,191 @@
+"""GPU parity of the soft epoch barrier workloads against the CPU oracle.
+
+Every comparison is bit-exact (all arithmetic on the path is integer).  Each
+test prints the case it is about to launch before the launch.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    print(f"[gpu case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def ccb():
+    from cross_core_barrier_amd import ccb as lib
+    st, cus, lds, clk = lib.ccb_device_info()
+    assert st == 0, lib.ccb_status_string(st)
+    return lib
+
+
+@pytest.fixture(scope="module")
+def wl(ccb):
+    from cross_core_barrier_amd import workloads
+    return workloads
+
+
+def _u32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+MODES = [0, 1, 2, 3]  # striped/flat x ordering-only/full fences
+MODE_IDS = ["striped-order", "flat-order", "striped-full", "flat-full"]
+_oracle_cache = {}
+
+
+def _oracle_slot(seed, rounds, n_grid, used):
+    key = ("slot", seed, rounds, n_grid, used)
+    if key not in _oracle_cache:
+        _oracle_cache[key] = oracle.slot_rounds(seed, rounds, n_grid, used)
+    return _oracle_cache[key]
+
+
+def _oracle_grouped(seed, rounds, n_grid):
+    key = ("grouped", seed, rounds, n_grid)
+    if key not in _oracle_cache:
+        _oracle_cache[key] = oracle.grouped_rounds(seed, rounds, n_grid)
+    return _oracle_cache[key]
+
+
+# --- witness rounds (whole grid / leading subset) ----------------------------
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+@pytest.mark.parametrize("seed,rounds,n_grid,threads,used,wpc", [
+    (0, 100, 8, 64, 0, 0),          # 8 WGs x 64 threads, 100 rounds (small workload)
+    (0, 333, 37, 192, 0, 0),        # ragged grid and block, more WGs than stripes
+    (7, 257, 37, 128, 19, 0),       # partial participation, odd member count
+    (3, 50, 1, 64, 0, 0),           # single participant
+    (5, 0, 16, 64, 0, 0),           # zero rounds
+    (6, 200, 100, 64, 67, 0),       # stripes with 2 and 3 members
+])
+def test_slot_rounds_small(wl, seed, rounds, n_grid, threads, used, wpc, mode):
+    _say(f"slot_rounds mode={mode} seed={seed} rounds={rounds} grid={n_grid}x{threads} used={used}")
+    res = wl.slot_rounds(seed, rounds, n_grid, threads, used, wpc, mode=mode)
+    want_out, want_status, want_ctr, rc = _oracle_slot(seed, rounds, n_grid, used)
+    assert rc == 0
+    assert res.status == 0
+    np.testing.assert_array_equal(_u32(res.out), want_out)
+    np.testing.assert_array_equal(res.wg_status.cpu().numpy(), want_status)
+    assert res.counters == [want_ctr]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+@pytest.mark.parametrize("used", [0, 128])
+def test_slot_rounds_grid_full(wl, used, mode):
+    """256 WGs x 256 threads, one per CU, 10,000 rounds; then usedCores=128
+    with WGs 128..255 idle (the bench's launch configuration)."""
+    _say(f"slot_rounds full 256x256 rounds=10000 used={used} wgsPerCu=1 mode={mode}")
+    res = wl.slot_rounds(1, 10_000, 256, 256, used, wgs_per_cu=1, mode=mode)
+    want_out, want_status, want_ctr, rc = _oracle_slot(1, 10_000, 256, used)
+    assert rc == 0 and res.status == 0
+    assert res.counters == [want_ctr] == [2_560_000 if used == 0 else 1_280_000]
+    np.testing.assert_array_equal(res.wg_status.cpu().numpy(), want_status)
+    np.testing.assert_array_equal(_u32(res.out), want_out)
+
+
+# --- grouped rounds -----------------------------------------------------------
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+@pytest.mark.parametrize("seed,rounds,n_grid,threads", [(4, 60, 6, 64), (9, 301, 34, 192),
+                                                        (2, 150, 130, 64)])
+def test_grouped_small(wl, seed, rounds, n_grid, threads, mode):
+    _say(f"grouped mode={mode} seed={seed} rounds={rounds} grid={n_grid}x{threads}")
+    res = wl.grouped_rounds(seed, rounds, n_grid, threads, mode=mode)
+    want_out, want_status, want_ctrs, rc = _oracle_grouped(seed, rounds, n_grid)
+    assert rc == 0 and res.status == 0
+    assert tuple(res.counters) == want_ctrs
+    np.testing.assert_array_equal(_u32(res.out), want_out)
+    np.testing.assert_array_equal(res.wg_status.cpu().numpy(), want_status)
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_grouped_full(wl, mode):
+    """512 WGs (2 per CU), groups A/B/mix, 100,000 rounds."""
+    _say(f"grouped full 512x256 rounds=100000 wgsPerCu=2 mode={mode}")
+    res = wl.grouped_rounds(4, 100_000, 512, 256, wgs_per_cu=2, mode=mode)
+    want_out, _, want_ctrs, rc = _oracle_grouped(4, 100_000, 512)
+    assert rc == 0 and res.status == 0
+    assert tuple(res.counters) == want_ctrs == (8_533_504, 8_533_248, 17_066_496)
+    np.testing.assert_array_equal(_u32(res.out), want_out)
+
+
+# --- barrier only ----------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_barrier_only_counts_and_placement(wl, mode):
+    _say(f"barrier_only 256x256 rounds=1000 wgsPerCu=1 placement mode={mode}")
+    st, ctrs, wg, pl = wl.barrier_only(1000, 256, 256, wgs_per_cu=1, placement=True, mode=mode)
+    assert st == 0 and ctrs == [256_000]
+    assert (wg.cpu().numpy() == 1).all()
+    p = pl.cpu().numpy().view(np.uint32).reshape(-1, 2)
+    cu = (p[:, 0] >> 8) & 0xF
+    sh = (p[:, 0] >> 12) & 0x1
+    se = (p[:, 0] >> 13) & 0x7
+    key = set(zip(p[:, 1].tolist(), se.tolist(), sh.tolist(), cu.tolist()))
+    print(f"distinct CUs used by 256 WGs: {len(key)}; XCDs: {sorted(set(p[:, 1].tolist()))}")
+    assert len(set(p[:, 1].tolist())) == 8
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_barrier_only_partial(wl, mode):
+    _say(f"barrier_only 64x64 rounds=500 used=40 mode={mode}")
+    st, ctrs, wg, _ = wl.barrier_only(500, 64, 64, used_cores=40, mode=mode)
+    assert st == 0 and ctrs == [500 * 40]
+    w = wg.cpu().numpy()
+    assert (w[:40] == 1).all() and (w[40:] == 2).all()
+
+
+# --- failure handling (forced from the host, bounded polls) -------------------------
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_forced_deadlock_is_reported(ccb, wl, mode):
+    """A counter (stripe 0) that starts at 1 (not a multiple of its member
+    count) makes the final arrival's target unreachable; the bounded poll
+    reports DEADLOCK instead of hanging, and every workgroup exits."""
+    _say(f"barrier_only forced deadlock: stripe 0 preset 1, N=4, maxPoll=2000, mode={mode}")
+    ws = wl.workspace(1)
+    ws[0] = 1
+    wg = torch.zeros(4, dtype=torch.int32, device="cuda")
+    st = ccb.ccb_run_barrier_only(ws, None, wg, 5, 4, 64, 0, 0, 2000, mode, None)
+    assert st == 0
+    st, ctrs = ccb.ccb_syncall_status(ws, 1, None)
+    assert st == ccb.CCB_ERR_DEADLOCK
+    w = wg.cpu().numpy()
+    assert (w == 3).any() and set(w.tolist()) <= {1, 3}
+
+
+def test_reset_clears_error_word(ccb, wl):
+    ws = wl.workspace(1)
+    ws[0] = 5
+    ws[32] = 3
+    ws[ccb.CCB_STRIPES * 32] = ccb.CCB_ERR_DEADLOCK
+    assert ccb.ccb_syncall_workspace_reset(ws, 1, None) == 0
+    torch.cuda.synchronize()
+    assert int(ws.abs().sum()) == 0
+    assert ccb.ccb_syncall_status(ws, 1, None) == (0, [0])
+
+
+def test_not_coresident_rejected(ccb, wl):
+    _say("barrier_only oversize grid: expect NOT_CORESIDENT, nothing launched")
+    ws = wl.workspace(1)
+    st = ccb.ccb_run_barrier_only(ws, None, None, 1, 256 * 64, 1024, 0, 0, 100, 0, None)
+    assert st == ccb.CCB_ERR_NOT_CORESIDENT
+    assert ccb.ccb_syncall_status(ws, 1, None) == (0, [0])
+
+
+def test_invalid_arguments(ccb, wl):
+    ws = wl.workspace(1)
+    assert ccb.ccb_run_barrier_only(ws, None, None, 1, 8, 65) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_barrier_only(ws, None, None, 1, 8, 64, 9) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_barrier_only(ws, None, None, 1, 8, 64, -1) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_barrier_only(ws, None, None, 1, 8, 64, mode=4) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_barrier_only(ws.data_ptr() + 4, None, None, 1, 8, 64) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_grouped_rounds(ws, ws, ws, None, 0, 1, 7, 64) == ccb.CCB_ERR_INVALID_VALUE
