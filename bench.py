@@ -1,0 +1,374 @@
+#!/usr/bin/env python3
+"""Benchmark of the soft epoch barrier on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode striped-order]
+
+A step is one pass of the headline workload: 256 workgroups x 256 threads
+(one per CU), 10,000 witness rounds on one barrier with usedCores = 0 (every
+round: each workgroup stores its witness, all pass the barrier, each sums all
+256 witnesses).  `value` is barriers per second over the K timed steps.
+
+The same run also measures, each on its own stream with HIP events:
+  - the floor: dependent agent-scope atomic round trips by one lane
+    (fetch-add and load, with and without fences) and 256-way contention;
+  - barrier-only latency for every barrier variant (slope over rounds);
+  - the 128-member pass and the grouped A/B/mix rounds (512 workgroups);
+  - the persistent stencil (2^26 int32, 64 iterations, 1024 workgroups):
+    the HBM roofline of the data phases;
+  - the batched CntNotify engine (2^20 counters x 64 ops);
+  - a 512 MiB streaming copy (achievable HBM ceiling);
+  - the CPU oracle on the host cores (cpu_baseline).
+It prints ONE JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+STENCIL_N = 1 << 26
+STENCIL_ITERS = 64
+STENCIL_BYTES_PER_ITER = 2 * 4 * STENCIL_N  # read x, write x' (int32)
+CNT_COUNTERS, CNT_OPS = 1 << 20, 64
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--mode", default="striped-order",
+                    choices=["striped-order", "flat-order", "striped-full", "flat-full"])
+    ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
+    ap.add_argument("--only", choices=["stencil"], default=None,
+                    help="run only the copy ceiling and the stencil (counter collection)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ("cross_core_barrier_amd/csrc/ccb_kernels.hip", "include/ccb_device.h",
+                "cross_core_barrier_amd/csrc/ccb_internal.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic():
+    """HBM bytes per stencil launch from the committed rocprofv3 PMC summary,
+    or None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "ccb_k_stencil_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+class Timer:
+    """HIP events on the given torch stream."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def __call__(self, fn, reps=1):
+        torch = self.torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(reps):
+            fn()
+        e1.record(self.stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps  # ms per call
+
+
+class Bench:
+    def __init__(self, args):
+        import numpy as np
+        import torch
+
+        from cross_core_barrier_amd import ccb, inputs, workloads
+        self.np, self.torch, self.ccb, self.inputs, self.wl = np, torch, ccb, inputs, workloads
+        self.args = args
+        self.mode = ccb.MODES[args.mode]
+        torch.cuda.set_device(0)
+        st, self.n_cu, _, clk_khz = ccb.ccb_device_info()
+        ccb.check(st, "ccb_device_info")
+        self.tick_ns = 1e6 / clk_khz
+        self.stream = torch.cuda.Stream()
+        self.timer = Timer(torch, self.stream)
+        self.dev = torch.device("cuda")
+        self.ws = workloads.workspace(3)
+        self.extra = {}
+
+    # ------------------------------------------------------------ headline
+    def headline(self):
+        torch, ccb, args = self.torch, self.ccb, self.args
+        cfg = self.inputs.WITNESS_GRID
+        n_grid, threads, rounds = cfg["n_wg"], cfg["threads"], cfg["rounds"]
+        ws, stream, mode = self.ws, self.stream, self.mode
+        slots = torch.zeros(4 * n_grid, dtype=torch.int32, device=self.dev)
+        out = torch.zeros((rounds, n_grid), dtype=torch.int32, device=self.dev)
+
+        def step():
+            ccb.check(ccb.ccb_syncall_workspace_reset(ws, 1, stream), "reset")
+            ccb.check(ccb.ccb_run_slot_rounds(ws, slots, out, None, cfg["seed"], rounds, n_grid,
+                                              threads, 0, 1, 0, mode, stream), "slot_rounds")
+
+        log(f"headline: witness rounds {n_grid}x{threads}, {rounds} rounds, mode {args.mode}")
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ms_events = self.timer(step, reps=args.steps)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        st, arrivals = ccb.ccb_syncall_status(ws, 1, stream)
+        ccb.check(st, "headline status")
+        assert arrivals == [rounds * n_grid], arrivals
+        ms_per_step = max(ms_events, wall * 1e3 / args.steps)
+        self.extra["ns_per_round_with_witness"] = round(ms_per_step * 1e6 / rounds, 1)
+
+        def pass2():
+            ccb.check(ccb.ccb_syncall_workspace_reset(ws, 1, stream), "reset")
+            ccb.check(ccb.ccb_run_slot_rounds(ws, slots, out, None, cfg["seed"], rounds, n_grid,
+                                              threads, cfg["used_cores_pass2"], 1, 0, mode, stream),
+                      "slot_rounds pass 2")
+        pass2()
+        ms = min(self.timer(pass2) for _ in range(3))
+        st, arr = ccb.ccb_syncall_status(ws, 1, stream)
+        ccb.check(st, "pass 2 status")
+        assert arr == [rounds * cfg["used_cores_pass2"]], arr
+        self.extra["ns_per_round_128_members"] = round(ms * 1e6 / rounds, 1)
+        return ms_per_step, rounds
+
+    # ------------------------------------------------------------ floor
+    def floor(self):
+        torch, ccb, stream = self.torch, self.ccb, self.stream
+        lines = torch.zeros(64 * 32, dtype=torch.int32, device=self.dev)
+        ticks = torch.zeros(2, dtype=torch.int64, device=self.dev)
+
+        def chain(kind, fenced, line_idx, iters=20000):
+            line = lines[line_idx * 32:]
+            ccb.check(ccb.ccb_bench_atomic_chain(line, ticks, iters, fenced, kind, stream), "chain")
+            stream.synchronize()
+            t = ticks.cpu().numpy()
+            return (t[1] - t[0]) * self.tick_ns / iters
+
+        floor = {}
+        for name, kind, fenced in (("fetch_add_ns", 0, 0), ("load_ns", 1, 0),
+                                   ("fetch_add_fenced_ns", 0, 1), ("load_fenced_ns", 1, 1)):
+            chain(kind, fenced, 0, 1000)
+            vals = [chain(kind, fenced, i) for i in range(0, 64, 8)]
+            floor[name] = round(statistics.median(vals), 1)
+        tk = torch.zeros(2 * 256, dtype=torch.int64, device=self.dev)
+        ccb.check(ccb.ccb_bench_atomic_contended(lines, tk, 2000, 256, stream), "contended")
+        stream.synchronize()
+        t = tk.cpu().numpy().reshape(-1, 2)
+        floor["same_address_fetch_add_ns_at_256"] = round(
+            float(t[:, 1].max() - t[:, 0].min()) * self.tick_ns / (2000 * 256), 2)
+        self.extra["floor"] = floor
+        log(f"floor: {floor}")
+        return floor
+
+    # ------------------------------------------------------------ barrier-only latency
+    def latency(self, floor):
+        ccb, ws, stream = self.ccb, self.ws, self.stream
+        lat = {}
+        for name, m in ccb.MODES.items():
+            res = {}
+            for r in (1000, 5000):
+                def f(r=r, m=m):
+                    ccb.check(ccb.ccb_syncall_workspace_reset(ws, 1, stream), "reset")
+                    ccb.check(ccb.ccb_run_barrier_only(ws, None, None, r, 256, 256, 0, 1, 0, m,
+                                                       stream), "barrier_only")
+                f()
+                res[r] = min(self.timer(f) for _ in range(3))
+            st, _ = ccb.ccb_syncall_status(ws, 1, stream)
+            ccb.check(st, "barrier_only status")
+            lat[name] = round((res[5000] - res[1000]) / 4000 * 1e6, 1)
+        self.extra["barrier_only_ns_at_256"] = lat
+        best = lat[self.args.mode]
+        self.extra["latency_roofline"] = {
+            "bound": "atomic_round_trip", "achieved_ns_per_barrier": best,
+            "floor_ns": floor["fetch_add_ns"], "ratio": round(best / floor["fetch_add_ns"], 2),
+            "target_ratio": 2.0}
+        log(f"barrier-only ns/barrier at 256 WGs: {lat}")
+
+    # ------------------------------------------------------------ grouped rounds
+    def grouped(self):
+        torch, ccb, ws, stream = self.torch, self.ccb, self.ws, self.stream
+        g = self.inputs.GROUPED
+        gout = torch.zeros((g["rounds"], g["n_wg"]), dtype=torch.int32, device=self.dev)
+        gslots = torch.zeros(4 * g["n_wg"], dtype=torch.int32, device=self.dev)
+
+        def run():
+            ccb.check(ccb.ccb_syncall_workspace_reset(ws, 3, stream), "reset")
+            ccb.check(ccb.ccb_run_grouped_rounds(ws, gslots, gout, None, g["seed"], g["rounds"],
+                                                 g["n_wg"], g["threads"], 2, 0, self.mode, stream),
+                      "grouped")
+        run()
+        ms = min(self.timer(run) for _ in range(2))
+        st, _ = ccb.ccb_syncall_status(ws, 3, stream)
+        ccb.check(st, "grouped status")
+        self.extra["grouped_ns_per_round"] = round(ms * 1e6 / g["rounds"], 1)
+
+    # ------------------------------------------------------------ streaming copy ceiling
+    def copy_ceiling(self):
+        torch, ccb, stream = self.torch, self.ccb, self.stream
+        src = torch.empty(1 << 27, dtype=torch.int32, device=self.dev).fill_(1)
+        dst = torch.empty_like(src)
+        copy_bytes = 2 * src.numel() * 4
+
+        def copy():
+            ccb.check(ccb.ccb_bench_copy(dst, src, src.numel() * 4, stream), "copy")
+        copy()
+        ms = min(self.timer(copy, reps=10) for _ in range(3))
+        gbs = copy_bytes / (ms / 1e3) / 1e9
+        self.extra["copy_512MiB_GBs"] = round(gbs, 1)
+        return gbs
+
+    # ------------------------------------------------------------ stencil roofline
+    def stencil(self, copy_gbs):
+        torch, ccb, ws, stream = self.torch, self.ccb, self.ws, self.stream
+        s = self.inputs.STENCIL
+        x0 = torch.from_numpy(self.inputs.stencil_input(s["seed"], STENCIL_N)).to(self.dev)
+        a = torch.empty_like(x0)
+        b = torch.empty_like(x0)
+        halo = self.wl.halo_scratch(STENCIL_N, s["threads"], s["n_wg"])
+
+        def run():
+            ccb.check(ccb.ccb_syncall_workspace_reset(ws, 1, stream), "reset")
+            ccb.check(ccb.ccb_run_stencil(a, b, STENCIL_N, STENCIL_ITERS, ws, halo, None, s["n_wg"],
+                                          s["threads"], 4, 0, self.mode, stream), "stencil")
+        a.copy_(x0)
+        run()
+        times = []
+        for _ in range(5):
+            a.copy_(x0)
+            torch.cuda.synchronize()
+            times.append(self.timer(run))
+        st, arr = ccb.ccb_syncall_status(ws, 1, stream)
+        ccb.check(st, "stencil status")
+        assert arr == [(STENCIL_ITERS - 1) * s["n_wg"]], arr
+        st_ms = statistics.median(times)
+        alg_bytes = STENCIL_BYTES_PER_ITER * STENCIL_ITERS
+        achieved = alg_bytes / (st_ms / 1e3) / 1e9
+        self.extra["stencil_barriers_per_launch"] = STENCIL_ITERS - 1
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": profiled_traffic(), "kernel": "ccb_k_stencil",
+                "launch_ms": round(st_ms, 4), "algorithmic_bytes": alg_bytes,
+                "frac_of_copy_ceiling": round(achieved / copy_gbs, 4) if copy_gbs else None}
+
+    # ------------------------------------------------------------ batched CntNotify
+    def cnt_batch(self):
+        np, torch, ccb, stream = self.np, self.torch, self.ccb, self.stream
+        c = self.inputs.CNT_BATCH
+        val, meta, rows = self.inputs.cnt_batch_input(c["seed"], CNT_COUNTERS, CNT_OPS)
+        v = torch.from_numpy(val.view(np.int32)).to(self.dev)
+        m = torch.from_numpy(meta).to(self.dev)
+        fin = torch.empty(CNT_COUNTERS, dtype=torch.int32, device=self.dev)
+        rel = torch.empty((rows, CNT_COUNTERS), dtype=torch.uint8, device=self.dev)
+        err = torch.zeros(1, dtype=torch.int32, device=self.dev)
+
+        def batch():
+            ccb.check(ccb.ccb_cnt_notify_batch(v, m, CNT_COUNTERS, CNT_OPS, fin, rel, rows, err,
+                                               stream), "batch")
+        batch()
+        bms = min(self.timer(batch, reps=20) for _ in range(3))
+        assert int(err.item()) == 0
+        cnt_bytes = val.nbytes + meta.nbytes + CNT_COUNTERS * 4 + rows * CNT_COUNTERS
+        gbs = cnt_bytes / (bms / 1e3) / 1e9
+        self.extra["cntnotify_batch"] = {"us_per_launch": round(bms * 1e3, 2), "GBs": round(gbs, 1),
+                                         "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                                         "ops_per_s": round(CNT_COUNTERS * CNT_OPS / (bms / 1e3), 0)}
+
+    # ------------------------------------------------------------ CPU baseline
+    def cpu_baseline(self):
+        import oracle
+        cfg = self.inputs.WITNESS_GRID
+        reps, t_cpu = 0, 0.0
+        while t_cpu < 10.0 and reps < 30:
+            t1 = time.perf_counter()
+            _, _, ctr, rc = oracle.slot_rounds(cfg["seed"], cfg["rounds"], cfg["n_wg"], 0)
+            t_cpu += time.perf_counter() - t1
+            reps += 1
+            assert rc == 0 and ctr == cfg["rounds"] * cfg["n_wg"]
+        return {"value": round(cfg["rounds"] * reps / t_cpu, 1), "unit": "barriers/s", "cores": 1,
+                "kind": "oracle",
+                "sample": f"{reps} full runs of the 256-workgroup, 10000-round witness simulation "
+                          f"({t_cpu:.1f} s on one thread; the host has {os.cpu_count()} cores)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    b = Bench(args)
+    if args.only == "stencil":
+        gbs = b.copy_ceiling()
+        roof = b.stencil(gbs)
+        print(json.dumps({"copy_512MiB_GBs": round(gbs, 1), "roofline": roof}), flush=True)
+        return
+
+    ms_per_step, rounds = b.headline()
+    value = rounds / (ms_per_step / 1e3)
+    roofline = None
+    cpu = None
+    if not args.quick:
+        floor = b.floor()
+        b.latency(floor)
+        b.grouped()
+        gbs = b.copy_ceiling()
+        roofline = b.stencil(gbs)
+        b.cnt_batch()
+        if not args.no_cpu:
+            cpu = b.cpu_baseline()
+
+    line = {
+        "metric": "grid barriers/s (ns/barrier) at 256 WGs; data-phase HBM GB/s vs peak",
+        "value": round(value, 1),
+        "unit": "barriers/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": "witness rounds: 256 workgroups x 256 threads (one per CU), "
+                               "10000 rounds, usedCores=0, seed 1",
+                   "barrier": args.mode, "ns_per_barrier": round(1e9 / value, 1)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        **b.extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

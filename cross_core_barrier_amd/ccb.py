@@ -41,7 +41,7 @@ CCB_ERR_NOT_READY = 10
 
 CCB_SOFT_MAX_POLL = 1_000_000
 CCB_LINE_BYTES = 128
-CCB_STRIPES = 32
+CCB_STRIPES = 64
 CCB_CNT_NOTIFY_POOL = 1024
 
 CCB_BARRIER_STRIPED, CCB_BARRIER_FLAT = 0, 1
@@ -102,9 +102,9 @@ _f = {
                                 _I32, _I32, _U32, _I32, _V),
     "ccb_run_grouped_rounds": _sig("ccb_run_grouped_rounds", _I32, _V, _V, _V, _V, _U64, _I32, _I32,
                                    _I32, _I32, _U32, _I32, _V),
-    "ccb_run_stencil": _sig("ccb_run_stencil", _I32, _V, _V, _I64, _I32, _V, _V, _I32, _I32, _I32,
-                            _U32, _I32, _V),
-    "ccb_stencil_halo_bytes": _sig("ccb_stencil_halo_bytes", ctypes.c_size_t, _I32, _I32),
+    "ccb_run_stencil": _sig("ccb_run_stencil", _I32, _V, _V, _I64, _I32, _V, _V, ctypes.c_size_t,
+                            _I32, _I32, _I32, _U32, _I32, _V),
+    "ccb_stencil_halo_bytes": _sig("ccb_stencil_halo_bytes", ctypes.c_size_t, _I64, _I32, _I32),
     "ccb_bench_atomic_chain": _sig("ccb_bench_atomic_chain", _I32, _V, _V, _I32, _I32, _I32, _V),
     "ccb_bench_atomic_contended": _sig("ccb_bench_atomic_contended", _I32, _V, _V, _I32, _I32, _V),
     "ccb_bench_copy": _sig("ccb_bench_copy", _I32, _V, _V, _I64, _V),
@@ -191,14 +191,18 @@ def ccb_run_grouped_rounds(ws, slots, out, wg_status, seed, rounds, n_grid, thre
                                         n_grid, threads, wgs_per_cu, max_poll, mode, _s(stream))
 
 
-def ccb_stencil_halo_bytes(n_grid: int, threads: int) -> int:
-    return int(_f["ccb_stencil_halo_bytes"](n_grid, threads))
+def ccb_stencil_halo_bytes(n: int, threads: int, n_grid: int) -> int:
+    return int(_f["ccb_stencil_halo_bytes"](n, threads, n_grid))
 
 
-def ccb_run_stencil(buf_a, buf_b, n, iters, ws, halo, n_grid, threads, wgs_per_cu=0, max_poll=0,
-                    mode=0, stream=None) -> int:
-    return _f["ccb_run_stencil"](_p(buf_a), _p(buf_b), n, iters, _p(ws), _p(halo), n_grid, threads,
-                                 wgs_per_cu, max_poll, mode, _s(stream))
+def ccb_run_stencil(buf_a, buf_b, n, iters, ws, halo, halo_bytes, n_grid, threads, wgs_per_cu=0,
+                    max_poll=0, mode=0, stream=None) -> int:
+    """halo_bytes: size of the halo scratch; for a torch tensor pass None to
+    use its size."""
+    if halo_bytes is None:
+        halo_bytes = 0 if halo is None else halo.numel() * halo.element_size()
+    return _f["ccb_run_stencil"](_p(buf_a), _p(buf_b), n, iters, _p(ws), _p(halo), halo_bytes,
+                                 n_grid, threads, wgs_per_cu, max_poll, mode, _s(stream))
 
 
 # --- floor microbenchmarks --------------------------------------------------------

@@ -304,24 +304,28 @@ CCB_API ccbStatus ccb_run_grouped_rounds(int32_t* ws, uint32_t* slots, uint32_t*
                                                poll_bound(maxPoll)));
 }
 
-CCB_API size_t ccb_stencil_halo_bytes(int32_t nGrid, int32_t threads)
+CCB_API size_t ccb_stencil_halo_bytes(int64_t n, int32_t threads, int32_t nGrid)
 {
-    if (nGrid < 1 || !valid_threads(threads)) return 0;
-    return (size_t)nGrid * (size_t)(threads / 64) * 4 * sizeof(int32_t);
+    if (n < 1 || !valid_threads(threads) || nGrid < 1) return 0;
+    const int64_t chunk = 4 * (int64_t)threads;
+    const int64_t nChunks = (n + chunk - 1) / chunk;
+    const int64_t kMax = (nChunks + nGrid - 1) / nGrid;
+    return (size_t)2 * (size_t)nGrid * (size_t)kMax * 2 * sizeof(int32_t);
 }
 
 CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32_t iters,
-                                  int32_t* ws, int32_t* halo, int32_t nGrid, int32_t threads,
-                                  int32_t wgsPerCu, uint32_t maxPoll, int32_t mode,
-                                  ccbStream stream)
+                                  int32_t* ws, int32_t* halo, size_t haloBytes, int32_t nGrid,
+                                  int32_t threads, int32_t wgsPerCu, uint32_t maxPoll,
+                                  int32_t mode, ccbStream stream)
 {
     if (bufA == nullptr || bufB == nullptr || ws == nullptr) return CCB_ERR_NULL_POINTER;
-    if (valid_mode(mode) && (mode & CCB_VISIBILITY_FULL) == 0 && halo == nullptr)
-        return CCB_ERR_NULL_POINTER;
+    const bool needHalo = valid_mode(mode) && (mode & CCB_VISIBILITY_FULL) == 0;
+    if (needHalo && halo == nullptr) return CCB_ERR_NULL_POINTER;
     if (n < 1 || iters < 0 || !aligned(ws, CCB_LINE_BYTES) || !aligned(bufA, 16) ||
         !aligned(bufB, 16) || nGrid < 1 || !valid_threads(threads) || wgsPerCu < 0 ||
         !valid_mode(mode) || (halo != nullptr && !aligned(halo, 4)))
         return CCB_ERR_INVALID_VALUE;
+    if (needHalo && haloBytes < ccb_stencil_halo_bytes(n, threads, nGrid)) return CCB_ERR_INVALID_VALUE;
     const uintptr_t a0 = (uintptr_t)bufA, a1 = a0 + (uintptr_t)n * 4;
     const uintptr_t b0 = (uintptr_t)bufB, b1 = b0 + (uintptr_t)n * 4;
     if (a0 < b1 && b0 < a1) return CCB_ERR_INVALID_VALUE;  // overlapping buffers
@@ -329,12 +333,7 @@ CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32
     ccbStatus st = plan_persistent(ccb::KernelId::Stencil, mode, nGrid, threads, wgsPerCu,
                                    (hipStream_t)stream, &ls);
     if (st != CCB_OK) return st;
-    // equal contiguous spans per wave, a multiple of 4 elements (16 B)
-    const int64_t waves = (int64_t)nGrid * (threads / 64);
-    int64_t span = (n + waves - 1) / waves;
-    span = (span + 3) / 4 * 4;
-    return from_hip(ccb::launch_stencil(ls, bufA, bufB, n, iters, ws, halo, span,
-                                        poll_bound(maxPoll)));
+    return from_hip(ccb::launch_stencil(ls, bufA, bufB, n, iters, ws, halo, poll_bound(maxPoll)));
 }
 
 // ===========================================================================

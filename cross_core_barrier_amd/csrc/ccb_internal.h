@@ -9,9 +9,15 @@
 namespace ccb {
 
 // Tuning constants of the kernels.
-constexpr int kStencilUnroll = 8;   // 1-KiB loads in flight per wave
-constexpr bool kStencilNT = false;  // non-temporal stores for the stencil output
-constexpr int kCntUnroll = 8;       // ops loaded ahead per thread in the batch engine
+#ifndef CCB_STENCIL_NT_STORE
+#define CCB_STENCIL_NT_STORE 0
+#endif
+#ifndef CCB_STENCIL_NT_LOAD
+#define CCB_STENCIL_NT_LOAD 1
+#endif
+constexpr bool kStencilNT = CCB_STENCIL_NT_STORE != 0;      // non-temporal stores of the output
+constexpr bool kStencilNTLoad = CCB_STENCIL_NT_LOAD != 0;   // non-temporal loads of the input
+constexpr int kCntUnroll = 2;       // ops loaded ahead per thread in the batch engine
 
 enum class KernelId { BarrierOnly, SlotRounds, GroupedRounds, Stencil };
 
@@ -35,8 +41,7 @@ hipError_t launch_grouped_rounds(const LaunchShape& ls, int32_t* ws, uint32_t* s
                                  uint32_t* out, int32_t* wgStatus, uint64_t seed, int32_t rounds,
                                  uint32_t maxPoll);
 hipError_t launch_stencil(const LaunchShape& ls, int32_t* bufA, int32_t* bufB, int64_t n,
-                          int32_t iters, int32_t* ws, int32_t* halo, int64_t span,
-                          uint32_t maxPoll);
+                          int32_t iters, int32_t* ws, int32_t* halo, uint32_t maxPoll);
 hipError_t launch_cnt_batch(const uint32_t* val, const uint8_t* meta, int64_t nCounters,
                             int32_t nOps, uint32_t* finalOut, uint8_t* rel, int32_t nRelRows,
                             int32_t* err, bool vec4, hipStream_t s);

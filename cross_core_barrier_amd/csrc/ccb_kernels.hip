@@ -115,7 +115,44 @@ __global__ __launch_bounds__(1024) void ccb_k_barrier_only(int32_t* ws, uint32_t
 // ---------------------------------------------------------------------------
 // Witness rounds on one barrier (the flag-slot test pattern of the SYNCALL
 // guide §6.1, run for many rounds): write own slot, barrier, sum all slots.
+//
+// With CCB_VIS_FULL each round is written in that order with plain accesses.
+// With CCB_VIS_ORDER the round is pipelined without changing what is
+// computed: right after passing barrier r a member already stores its
+// witness for round r + 1 (ring row (r + 1) mod 4, which nobody reads before
+// barrier r + 1), then reads round r's slots; its partial sums go to LDS and
+// lane 0 finishes the sum and stores out[r] while its arrival for barrier
+// r + 1 is in flight.  The slot store has completed before the member's
+// last slot load returned (the wait below), so the barrier needs no further
+// wait.  The brute-force enumerator checks this schedule (early writes)
+// against the ring depth.
 // ---------------------------------------------------------------------------
+namespace {
+
+// Wave-level sum (mod 2^32) of v; the result is valid in lane 0.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v)
+{
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// Finishes round r's sum from the per-wave partials and stores it.
+struct FinishRound {
+    const uint32_t* partial;
+    int nWave;
+    uint32_t* dst;  // nullptr: nothing to store
+    __device__ __forceinline__ void operator()() const
+    {
+        if (dst == nullptr) return;
+        uint32_t s = 0;
+        for (int i = 0; i < nWave; ++i) s += partial[i];
+        *dst = s;
+    }
+};
+
+}  // namespace
+
 template <int K, ccbVisibility V>
 __global__ __launch_bounds__(1024) void ccb_k_slot_rounds(int32_t* ws, uint32_t* slots,
                                                            uint32_t* out, int32_t* wgStatus,
@@ -125,21 +162,45 @@ __global__ __launch_bounds__(1024) void ccb_k_slot_rounds(int32_t* ws, uint32_t*
     __shared__ uint32_t partial[1024 / kWave];
     const int32_t w = blockIdx.x;
     const int32_t nGrid = gridDim.x;
+    const int nWave = blockDim.x / kWave;
     if (w >= nMembers) {
         if (wgStatus != nullptr && leader()) wgStatus[w] = 2;
         return;
     }
     int32_t* err = ws + CCB_STRIPES * CCB_LINE_WORDS;
     int32_t rc = CCB_OK;
-    for (int32_t r = 0; r < rounds; ++r) {
-        uint32_t* row = slots + (size_t)(r % kRing) * nGrid;
-        if (leader()) shared_store<V>(row + w, witness(seed, (uint32_t)r, (uint32_t)w));
-        rc = ccb_barrier<K, V>(ws, nMembers, w, maxPoll, err);
-        if (rc != CCB_OK) break;
-        uint32_t s = 0;
-        for (int32_t i = threadIdx.x; i < nMembers; i += blockDim.x) s += shared_load<V>(row + i);
-        s = block_sum(s, partial);
-        if (leader()) out[(size_t)r * nGrid + w] = s;
+    if constexpr (V == CCB_VIS_FULL) {
+        for (int32_t r = 0; r < rounds; ++r) {
+            uint32_t* row = slots + (size_t)(r % kRing) * nGrid;
+            if (leader()) shared_store<V>(row + w, witness(seed, (uint32_t)r, (uint32_t)w));
+            rc = ccb_barrier<K, V>(ws, nMembers, w, maxPoll, err);
+            if (rc != CCB_OK) break;
+            uint32_t s = 0;
+            for (int32_t i = threadIdx.x; i < nMembers; i += blockDim.x) s += shared_load<V>(row + i);
+            s = block_sum(s, partial);
+            if (leader()) out[(size_t)r * nGrid + w] = s;
+        }
+    } else {
+        if (leader() && rounds > 0) ccb_store_coherent(slots + w, witness(seed, 0u, (uint32_t)w));
+        ccb_wait_memory();
+        uint32_t* pending = nullptr;  // out entry of the round whose partials are in LDS
+        for (int32_t r = 0; r < rounds; ++r) {
+            rc = ccb_barrier<K, V, false>(ws, nMembers, w, maxPoll, err,
+                                          FinishRound{partial, nWave, pending});
+            if (rc != CCB_OK) break;
+            const uint32_t* row = slots + (size_t)(r % kRing) * nGrid;
+            if (leader() && r + 1 < rounds)
+                ccb_store_coherent(slots + (size_t)((r + 1) % kRing) * nGrid + w,
+                                   witness(seed, (uint32_t)(r + 1), (uint32_t)w));
+            uint32_t s = 0;
+            for (int32_t i = threadIdx.x; i < nMembers; i += blockDim.x) s += ccb_load_coherent(row + i);
+            s = wave_sum(s);
+            ccb_wait_memory();  // the witness store above is complete
+            if ((threadIdx.x % kWave) == 0) partial[threadIdx.x / kWave] = s;
+            pending = out + (size_t)r * nGrid + w;
+        }
+        __syncthreads();
+        if (leader() && rc == CCB_OK) FinishRound{partial, nWave, pending}();
     }
     if (wgStatus != nullptr && leader()) wgStatus[w] = rc == CCB_OK ? 1 : 3;
 }
@@ -149,7 +210,10 @@ __global__ __launch_bounds__(1024) void ccb_k_slot_rounds(int32_t* ws, uint32_t*
 // on barrier 1, everyone on barrier 2; round kind r mod 3.  Each barrier's
 // members enter it in the same order the same number of times (SYNCALL
 // guide §6.2).  Slots are stored group-major (even ids first) so a group's
-// slots are contiguous; the sum does not depend on the layout.
+// slots are contiguous; the sum does not depend on the layout.  With
+// CCB_VIS_ORDER the rounds are pipelined as in the witness rounds above: a
+// member stores the witness of the next round it belongs to right after
+// passing a barrier.
 // ---------------------------------------------------------------------------
 template <int K, ccbVisibility V>
 __global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32_t* slots,
@@ -163,22 +227,58 @@ __global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32
     const int32_t half = nGrid / 2;
     const int32_t parity = w & 1;
     const int32_t pos = parity * half + (w >> 1);
+    const int nWave = blockDim.x / kWave;
     int32_t* err = ws + 3 * CCB_STRIPES * CCB_LINE_WORDS;
     int32_t rc = CCB_OK;
-    for (int32_t r = 0; r < rounds; ++r) {
-        const int32_t kind = r % 3;
-        if (kind != 2 && kind != parity) continue;  // not a member of this round
-        uint32_t* row = slots + (size_t)(r % kRing) * nGrid;
-        if (leader()) shared_store<V>(row + pos, witness(seed, (uint32_t)r, (uint32_t)w));
-        const int32_t n = kind == 2 ? nGrid : half;
-        const int32_t member = kind == 2 ? w : (w >> 1);
-        rc = ccb_barrier<K, V>(ws + kind * CCB_STRIPES * CCB_LINE_WORDS, n, member, maxPoll, err);
-        if (rc != CCB_OK) break;
-        const int32_t first = kind == 2 ? 0 : kind * half;
-        uint32_t s = 0;
-        for (int32_t i = threadIdx.x; i < n; i += blockDim.x) s += shared_load<V>(row + first + i);
-        s = block_sum(s, partial);
-        if (leader()) out[(size_t)r * nGrid + w] = s;
+    auto member_of = [&](int32_t r) { return (r % 3) == 2 || (r % 3) == parity; };
+    if constexpr (V == CCB_VIS_FULL) {
+        for (int32_t r = 0; r < rounds; ++r) {
+            const int32_t kind = r % 3;
+            if (!member_of(r)) continue;
+            uint32_t* row = slots + (size_t)(r % kRing) * nGrid;
+            if (leader()) shared_store<V>(row + pos, witness(seed, (uint32_t)r, (uint32_t)w));
+            const int32_t n = kind == 2 ? nGrid : half;
+            const int32_t member = kind == 2 ? w : (w >> 1);
+            rc = ccb_barrier<K, V>(ws + kind * CCB_STRIPES * CCB_LINE_WORDS, n, member, maxPoll, err);
+            if (rc != CCB_OK) break;
+            const int32_t first = kind == 2 ? 0 : kind * half;
+            uint32_t s = 0;
+            for (int32_t i = threadIdx.x; i < n; i += blockDim.x) s += shared_load<V>(row + first + i);
+            s = block_sum(s, partial);
+            if (leader()) out[(size_t)r * nGrid + w] = s;
+        }
+    } else {
+        int32_t r = 0;
+        while (r < rounds && !member_of(r)) ++r;
+        if (leader() && r < rounds)
+            ccb_store_coherent(slots + (size_t)(r % kRing) * nGrid + pos,
+                               witness(seed, (uint32_t)r, (uint32_t)w));
+        ccb_wait_memory();
+        uint32_t* pending = nullptr;
+        for (; r < rounds;) {
+            const int32_t kind = r % 3;
+            const int32_t n = kind == 2 ? nGrid : half;
+            const int32_t member = kind == 2 ? w : (w >> 1);
+            rc = ccb_barrier<K, V, false>(ws + kind * CCB_STRIPES * CCB_LINE_WORDS, n, member,
+                                          maxPoll, err, FinishRound{partial, nWave, pending});
+            if (rc != CCB_OK) break;
+            int32_t next = r + 1;
+            while (next < rounds && !member_of(next)) ++next;
+            if (leader() && next < rounds)
+                ccb_store_coherent(slots + (size_t)(next % kRing) * nGrid + pos,
+                                   witness(seed, (uint32_t)next, (uint32_t)w));
+            const uint32_t* row = slots + (size_t)(r % kRing) * nGrid;
+            const int32_t first = kind == 2 ? 0 : kind * half;
+            uint32_t s = 0;
+            for (int32_t i = threadIdx.x; i < n; i += blockDim.x) s += ccb_load_coherent(row + first + i);
+            s = wave_sum(s);
+            ccb_wait_memory();
+            if ((threadIdx.x % kWave) == 0) partial[threadIdx.x / kWave] = s;
+            pending = out + (size_t)r * nGrid + w;
+            r = next;
+        }
+        __syncthreads();
+        if (leader() && rc == CCB_OK) FinishRound{partial, nWave, pending}();
     }
     if (wgStatus != nullptr && leader()) wgStatus[w] = rc == CCB_OK ? 1 : 3;
 }
@@ -186,24 +286,27 @@ __global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32
 // ---------------------------------------------------------------------------
 // Barrier-separated 3-point stencil (persistent).
 //
-// Each wave owns a contiguous span of `span` elements (a multiple of 4) for
-// every iteration.  A wave step covers 256 elements: lane l holds elements
-// 4l..4l+3 of the step as one 16-byte load.  The left neighbour of a lane's
-// first element is lane l-1's last element (DPP wave shift right by one
-// lane); lane 0 takes it from the previous step's lane 63 (a scalar carried
-// across steps) or, at the start of the span, from the left halo.  The right
-// neighbour of a lane's last element is lane l+1's first (DPP wave shift
-// left); lane 63 takes it from the next step's lane 0, or past the span's end
-// from the right halo.  The array ends are clamped.  U steps are loaded
-// before any is used so that each wave keeps U 1-KiB loads in flight.
+// Layout: the array is cut into chunks of 4 * blockDim.x elements (4 KiB for
+// 256 threads).  Workgroup w owns chunks w, w + G, w + 2G, ... (G = grid
+// size) in every iteration, so at any moment the whole grid streams one
+// compact window of memory -- on MI355X that sweep order reaches about 5.7
+// TB/s where per-wave contiguous spans stay near 4.2 TB/s.  Inside a chunk,
+// lane l of wave v holds elements 4l..4l+3 of the wave's 256-element piece
+// as one 16-byte load.  The left neighbour of a lane's first element is lane
+// l-1's last element (DPP wave shift right by one lane), the right
+// neighbour of its last element is lane l+1's first (DPP wave shift left);
+// lanes 0 and 63 take the element just outside the piece, which belongs to
+// the neighbouring wave of the same workgroup or, at a chunk boundary, to
+// the neighbouring chunk of another workgroup.  The array ends are clamped.
 //
-// A wave only ever touches its own span, so the only data that crosses
-// workgroups are the two halo elements per span.  Across a CCB_VIS_ORDER
-// barrier they travel through a small exchange buffer written and read with
-// device-coherent accesses (halo[t & 1][wave][0] = first output element of
-// the span in iteration t, [1] = last); the bulk data needs no cache
-// maintenance at all.  Across a CCB_VIS_FULL barrier they are read straight
-// from the source buffer.
+// Chunks never move between workgroups, so the only data that crosses
+// workgroups are the two boundary elements of each chunk.  Across a
+// CCB_VIS_ORDER barrier they travel through a small exchange buffer written
+// and read with device-coherent accesses (halo[t & 1][chunk][0] = first
+// output element of the chunk in iteration t, [1] = last); the bulk data
+// needs no cache maintenance at all.  Across a CCB_VIS_FULL barrier they
+// are read straight from the source buffer.  A partial last chunk is
+// processed one element per thread.
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -233,115 +336,195 @@ __device__ __forceinline__ void store4(int32_t* p, int4 v)
     }
 }
 
-// One step: outputs for the 4 elements a lane holds.
-__device__ __forceinline__ int4 step4(int4 v, int32_t carry, int32_t nextFirst, int lane)
+template <bool kNT>
+__device__ __forceinline__ int4 load4(const int32_t* p)
 {
-    int32_t left = lane_from_left(v.w);
-    int32_t right = lane_from_right(v.x);
-    if (lane == 0) left = carry;
-    if (lane == kWave - 1) right = nextFirst;
-    int4 o;
-    o.x = st3(left, v.x, v.y);
-    o.y = st3(v.x, v.y, v.z);
-    o.z = st3(v.y, v.z, v.w);
-    o.w = st3(v.z, v.w, right);
-    return o;
+    if constexpr (kNT) {
+        typedef int v4i __attribute__((ext_vector_type(4)));
+        const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+        return make_int4(v.x, v.y, v.z, v.w);
+    } else {
+        return *reinterpret_cast<const int4*>(p);
+    }
 }
 
-// Computes y[s0..s1) from x; leftHalo = x[s0-1] (clamped), rightHalo = x[s1]
-// (clamped).  If haloOut is non-null the span's first and last outputs are
-// also published there with device-coherent stores.
-template <int U, bool kNT>
-__device__ __forceinline__ void stencil_span(const int32_t* __restrict__ x, int32_t* __restrict__ y,
-                                             int64_t s0, int64_t s1, int32_t leftHalo,
-                                             int32_t rightHalo, int32_t* haloOut)
+// Largest number of chunks per workgroup whose halos are staged in LDS; a
+// launch with more chunks per workgroup reads them one by one instead.
+constexpr int kHaloLds = 1024;
+
+// Where a chunk's two outside neighbours come from in one iteration.
+enum class HaloSrc { Direct, Staged, Coherent };
+
+struct StencilGeom {
+    int64_t n, chunk, nFullChunks, nChunks, G, w, kMax, myChunks;
+};
+
+// Exchange-buffer entry (workgroup v, chunk index k, end e) of parity p.
+__device__ __forceinline__ int32_t* halo_entry(int32_t* base, const StencilGeom& g, int p,
+                                               int64_t v, int64_t k, int e)
+{
+    return base + (((size_t)p * g.G + v) * g.kMax + k) * 2 + e;
+}
+
+// Outside neighbours of chunk k of this workgroup (c = w + k * G):
+// x[c0 - 1] and x[c1], clamped at the array ends.
+template <HaloSrc S>
+__device__ __forceinline__ int32_t chunk_left(const StencilGeom& g, const int32_t* x, int64_t k,
+                                              const int32_t* inLeft, int32_t* halo, int p)
+{
+    const int64_t c = g.w + k * g.G;
+    if constexpr (S == HaloSrc::Direct) {
+        const int64_t c0 = c * g.chunk;
+        return x[c0 > 0 ? c0 - 1 : 0];
+    } else if constexpr (S == HaloSrc::Staged) {
+        return inLeft[k];
+    } else {
+        if (c == 0) return x[0];
+        return ccb_load_coherent(g.w > 0 ? halo_entry(halo, g, p, g.w - 1, k, 1)
+                                         : halo_entry(halo, g, p, g.G - 1, k - 1, 1));
+    }
+}
+template <HaloSrc S>
+__device__ __forceinline__ int32_t chunk_right(const StencilGeom& g, const int32_t* x, int64_t k,
+                                               const int32_t* inRight, int32_t* halo, int p)
+{
+    const int64_t c = g.w + k * g.G;
+    if constexpr (S == HaloSrc::Direct) {
+        const int64_t c1 = c * g.chunk + g.chunk;
+        return x[c1 < g.n ? c1 : g.n - 1];
+    } else if constexpr (S == HaloSrc::Staged) {
+        return inRight[k];
+    } else {
+        if (c + 1 >= g.nChunks) return x[g.n - 1];
+        return ccb_load_coherent(g.w + 1 < g.G ? halo_entry(halo, g, p, g.w + 1, k, 0)
+                                               : halo_entry(halo, g, p, 0, k + 1, 0));
+    }
+}
+
+// One iteration over this workgroup's chunks.  pubFirst/pubLast (LDS, may be
+// null) receive each chunk's first and last output; pubHalo (may be null)
+// receives them directly with device-coherent stores.
+template <HaloSrc S>
+__device__ __forceinline__ void stencil_sweep(const StencilGeom& g, const int32_t* __restrict__ x,
+                                              int32_t* __restrict__ y, const int32_t* inLeft,
+                                              const int32_t* inRight, int32_t* halo, int pIn,
+                                              int32_t* pubFirst, int32_t* pubLast,
+                                              int32_t* pubHalo, int pOut)
 {
     const int lane = threadIdx.x % kWave;
-    const int64_t len = s1 - s0;
-    const int64_t nFull = len / 256;
-    int32_t carry = leftHalo;
-    int64_t j = 0;
-    for (; j + U <= nFull; j += U) {
-        int4 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            v[u] = *reinterpret_cast<const int4*>(x + s0 + (j + u) * 256 + 4 * lane);
-        // first element after this batch: next step's lane 0, or past the span
-        const int64_t after = s0 + (j + U) * 256;
-        const int32_t rightEdge = after < s1 ? x[after] : rightHalo;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int32_t nextFirst = (u + 1 < U) ? __builtin_amdgcn_readlane(v[u + 1].x, 0) : rightEdge;
-            const int4 o = step4(v[u], carry, nextFirst, lane);
-            const int64_t e0 = s0 + (j + u) * 256 + 4 * lane;
-            store4<kNT>(y + e0, o);
-            if (haloOut != nullptr) {
-                if (e0 == s0) ccb_store_coherent(haloOut, o.x);
-                if (e0 + 3 == s1 - 1) ccb_store_coherent(haloOut + 1, o.w);
+    // wave index as a scalar: branches on it are uniform
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int nWave = blockDim.x / kWave;
+    const int64_t fullMine = g.w < g.nFullChunks ? (g.nFullChunks - 1 - g.w) / g.G + 1 : 0;
+    for (int64_t k = 0; k < fullMine; ++k) {
+        const int64_t c = g.w + k * g.G;
+        const int64_t w0 = c * g.chunk + (int64_t)wave * 256;  // this wave's piece
+        const int4 v = load4<ccb::kStencilNTLoad>(x + w0 + 4 * lane);
+        int32_t lh, rh;
+        if (wave == 0) lh = chunk_left<S>(g, x, k, inLeft, halo, pIn);
+        else lh = x[w0 - 1];
+        if (wave == nWave - 1) rh = chunk_right<S>(g, x, k, inRight, halo, pIn);
+        else rh = x[w0 + 256];
+        int32_t left = lane_from_left(v.w);
+        int32_t right = lane_from_right(v.x);
+        if (lane == 0) left = lh;
+        if (lane == kWave - 1) right = rh;
+        int4 o;
+        o.x = st3(left, v.x, v.y);
+        o.y = st3(v.x, v.y, v.z);
+        o.z = st3(v.y, v.z, v.w);
+        o.w = st3(v.z, v.w, right);
+        store4<ccb::kStencilNT>(y + w0 + 4 * lane, o);
+        if (wave == 0 && lane == 0) {
+            if (pubFirst != nullptr) pubFirst[k] = o.x;
+            if (pubHalo != nullptr) ccb_store_coherent(halo_entry(pubHalo, g, pOut, g.w, k, 0), o.x);
+        }
+        if (wave == nWave - 1 && lane == kWave - 1) {
+            if (pubLast != nullptr) pubLast[k] = o.w;
+            if (pubHalo != nullptr) ccb_store_coherent(halo_entry(pubHalo, g, pOut, g.w, k, 1), o.w);
+        }
+    }
+    if (fullMine < g.myChunks) {
+        // the partial last chunk, one element per thread
+        const int64_t k = fullMine;
+        const int64_t c0 = (g.w + k * g.G) * g.chunk;
+        const int32_t cl = chunk_left<S>(g, x, k, inLeft, halo, pIn);
+        for (int64_t e = c0 + threadIdx.x; e < g.n; e += blockDim.x) {
+            const int32_t a = e == c0 ? cl : x[e - 1];
+            const int32_t b = e + 1 < g.n ? x[e + 1] : x[g.n - 1];
+            const int32_t o = st3(a, x[e], b);
+            y[e] = o;
+            if (e == c0) {
+                if (pubFirst != nullptr) pubFirst[k] = o;
+                if (pubHalo != nullptr) ccb_store_coherent(halo_entry(pubHalo, g, pOut, g.w, k, 0), o);
             }
-            carry = __builtin_amdgcn_readlane(v[u].w, kWave - 1);
-        }
-    }
-    for (; j < nFull; ++j) {
-        const int4 v = *reinterpret_cast<const int4*>(x + s0 + j * 256 + 4 * lane);
-        const int64_t after = s0 + (j + 1) * 256;
-        const int32_t nextFirst = after < s1 ? x[after] : rightHalo;
-        const int4 o = step4(v, carry, nextFirst, lane);
-        const int64_t e0 = s0 + j * 256 + 4 * lane;
-        store4<kNT>(y + e0, o);
-        if (haloOut != nullptr) {
-            if (e0 == s0) ccb_store_coherent(haloOut, o.x);
-            if (e0 + 3 == s1 - 1) ccb_store_coherent(haloOut + 1, o.w);
-        }
-        carry = __builtin_amdgcn_readlane(v.w, kWave - 1);
-    }
-    // ragged tail of the span: one element per lane at a time
-    for (int64_t e = s0 + nFull * 256 + lane; e < s1; e += kWave) {
-        const int32_t a = e == s0 ? leftHalo : x[e - 1];
-        const int32_t c = e + 1 == s1 ? rightHalo : x[e + 1];
-        const int32_t o = st3(a, x[e], c);
-        y[e] = o;
-        if (haloOut != nullptr) {
-            if (e == s0) ccb_store_coherent(haloOut, o);
-            if (e == s1 - 1) ccb_store_coherent(haloOut + 1, o);
+            if (e == g.n - 1) {
+                if (pubLast != nullptr) pubLast[k] = o;
+                if (pubHalo != nullptr) ccb_store_coherent(halo_entry(pubHalo, g, pOut, g.w, k, 1), o);
+            }
         }
     }
 }
 
 }  // namespace
 
+// The exchange buffer is workgroup-major: halo[parity][w][k][2] holds the
+// first and last output element of workgroup w's k-th chunk (chunk
+// w + k * G).  At the start of an iteration each workgroup copies the
+// entries it needs -- the last elements of its left neighbour's chunks and
+// the first elements of its right neighbour's chunks -- into LDS with one
+// device-coherent load per entry, and at the end it publishes its own
+// entries the same way, so no coherent access sits inside the sweep.
 template <int K, ccbVisibility V>
 __global__ __launch_bounds__(1024) void ccb_k_stencil(int32_t* bufA, int32_t* bufB, int64_t n,
                                                        int32_t iters, int32_t* ws, int32_t* halo,
-                                                       int64_t span, uint32_t maxPoll)
+                                                       uint32_t maxPoll)
 {
-    const int64_t wavesPerWg = blockDim.x / kWave;
-    const int64_t nWaves = (int64_t)gridDim.x * wavesPerWg;
-    const int64_t waveId = (int64_t)blockIdx.x * wavesPerWg + threadIdx.x / kWave;
-    const int64_t s0 = waveId * span;
-    const int64_t s1 = s0 + span < n ? s0 + span : n;
+    __shared__ int32_t inLeft[kHaloLds], inRight[kHaloLds];   // neighbours of my chunks
+    __shared__ int32_t outFirst[kHaloLds], outLast[kHaloLds]; // my chunks' end outputs
+    StencilGeom g;
+    g.n = n;
+    g.chunk = 4 * (int64_t)blockDim.x;
+    g.nFullChunks = n / g.chunk;
+    g.nChunks = (n + g.chunk - 1) / g.chunk;
+    g.G = gridDim.x;
+    g.w = blockIdx.x;
+    g.kMax = (g.nChunks + g.G - 1) / g.G;  // chunks of the busiest workgroup
+    g.myChunks = g.w < g.nChunks ? (g.nChunks - 1 - g.w) / g.G + 1 : 0;
+    const bool staged = g.kMax <= kHaloLds;
     int32_t* err = ws + CCB_STRIPES * CCB_LINE_WORDS;
-    const int32_t nGrid = gridDim.x;
     for (int32_t t = 0; t < iters; ++t) {
         const int32_t* x = (t & 1) ? bufB : bufA;
         int32_t* y = (t & 1) ? bufA : bufB;
-        if (s0 < s1) {
-            int32_t leftHalo, rightHalo;
-            if (V == CCB_VIS_FULL || t == 0) {
-                leftHalo = x[s0 > 0 ? s0 - 1 : 0];
-                rightHalo = x[s1 < n ? s1 : n - 1];
-            } else {
-                const int32_t* prev = halo + (size_t)((t - 1) & 1) * nWaves * 2;
-                leftHalo = s0 > 0 ? ccb_load_coherent(prev + 2 * (waveId - 1) + 1) : x[0];
-                rightHalo = s1 < n ? ccb_load_coherent(prev + 2 * (waveId + 1)) : x[n - 1];
+        const bool publish = V == CCB_VIS_ORDER && t + 1 < iters;
+        const int pIn = (t - 1) & 1, pOut = t & 1;
+        if (V == CCB_VIS_FULL || t == 0) {
+            stencil_sweep<HaloSrc::Direct>(g, x, y, nullptr, nullptr, halo, pIn,
+                                           publish && staged ? outFirst : nullptr,
+                                           publish && staged ? outLast : nullptr,
+                                           publish && !staged ? halo : nullptr, pOut);
+        } else if (staged) {
+            for (int64_t k = threadIdx.x; k < g.myChunks; k += blockDim.x) {
+                inLeft[k] = chunk_left<HaloSrc::Coherent>(g, x, k, nullptr, halo, pIn);
+                inRight[k] = chunk_right<HaloSrc::Coherent>(g, x, k, nullptr, halo, pIn);
             }
-            int32_t* haloOut = nullptr;
-            if (V == CCB_VIS_ORDER && t + 1 < iters)
-                haloOut = halo + (size_t)(t & 1) * nWaves * 2 + 2 * waveId;
-            stencil_span<ccb::kStencilUnroll, ccb::kStencilNT>(x, y, s0, s1, leftHalo, rightHalo, haloOut);
+            __syncthreads();
+            stencil_sweep<HaloSrc::Staged>(g, x, y, inLeft, inRight, halo, pIn,
+                                           publish ? outFirst : nullptr,
+                                           publish ? outLast : nullptr, nullptr, pOut);
+        } else {
+            stencil_sweep<HaloSrc::Coherent>(g, x, y, nullptr, nullptr, halo, pIn, nullptr,
+                                             nullptr, publish ? halo : nullptr, pOut);
+        }
+        if (publish && staged) {
+            __syncthreads();
+            for (int64_t k = threadIdx.x; k < g.myChunks; k += blockDim.x) {
+                ccb_store_coherent(halo_entry(halo, g, pOut, g.w, k, 0), outFirst[k]);
+                ccb_store_coherent(halo_entry(halo, g, pOut, g.w, k, 1), outLast[k]);
+            }
         }
         if (t + 1 < iters) {
-            if (ccb_barrier<K, V>(ws, nGrid, blockIdx.x, maxPoll, err) != CCB_OK) break;
+            if (ccb_barrier<K, V>(ws, (int32_t)g.G, (int32_t)g.w, maxPoll, err) != CCB_OK) break;
         }
     }
 }
@@ -688,10 +871,9 @@ hipError_t launch_grouped_rounds(const LaunchShape& ls, int32_t* ws, uint32_t* s
 }
 
 hipError_t launch_stencil(const LaunchShape& ls, int32_t* bufA, int32_t* bufB, int64_t n,
-                          int32_t iters, int32_t* ws, int32_t* halo, int64_t span,
-                          uint32_t maxPoll)
+                          int32_t iters, int32_t* ws, int32_t* halo, uint32_t maxPoll)
 {
-    void* args[] = {&bufA, &bufB, &n, &iters, &ws, &halo, &span, &maxPoll};
+    void* args[] = {&bufA, &bufB, &n, &iters, &ws, &halo, &maxPoll};
     return coop(ls.fn, ls.nGrid, ls.threads, ls.lds, ls.stream, args);
 }
 

@@ -85,8 +85,8 @@ def barrier_only(rounds: int, n_grid: int, threads: int, used_cores: int = 0, wg
     return st, ctrs, wg, pl
 
 
-def halo_scratch(n_grid: int, threads: int, device=None) -> torch.Tensor:
-    nbytes = ccb.ccb_stencil_halo_bytes(n_grid, threads)
+def halo_scratch(n: int, threads: int, n_grid: int, device=None) -> torch.Tensor:
+    nbytes = ccb.ccb_stencil_halo_bytes(n, threads, n_grid)
     return torch.zeros(max(nbytes // 4, 1), dtype=torch.int32, device=_dev(device))
 
 
@@ -96,8 +96,8 @@ def stencil(x: torch.Tensor, iters: int, n_grid: int, threads: int, wgs_per_cu: 
     a = x.clone()
     b = torch.empty_like(a)
     ws = workspace(1, x.device)
-    halo = halo_scratch(n_grid, threads, x.device)
-    st = ccb.ccb_run_stencil(a, b, a.numel(), iters, ws, halo, n_grid, threads, wgs_per_cu,
+    halo = halo_scratch(x.numel(), threads, n_grid, x.device)
+    st = ccb.ccb_run_stencil(a, b, a.numel(), iters, ws, halo, None, n_grid, threads, wgs_per_cu,
                              max_poll, mode, stream)
     ccb.check(st, "ccb_run_stencil")
     st, _ = ccb.ccb_syncall_status(ws, 1, stream)

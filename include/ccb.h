@@ -64,7 +64,7 @@ enum {
 #define CCB_LINE_BYTES 128
 
 /* Counter stripes reserved per barrier in a workspace (see ccb_device.h). */
-#define CCB_STRIPES 32
+#define CCB_STRIPES 64
 
 /* Barrier variant used by a workload launcher: one counter layout ORed with
  * one visibility strength.
@@ -226,24 +226,27 @@ CCB_API ccbStatus ccb_run_grouped_rounds(int32_t* ws, uint32_t* slots, uint32_t*
  * with one soft barrier over all nGrid workgroups between consecutive
  * iterations (iters - 1 barriers).  The result is in bufA when iters is even,
  * in bufB when odd.  The caller guarantees |x| < 2^29 so that the int32 sum
- * cannot overflow.  Each wave owns one contiguous span of the array in every
- * iteration, so only two halo elements per span cross workgroups; with
+ * cannot overflow.  The array is cut into chunks of 4 * threads elements;
+ * workgroup w owns chunks w, w + nGrid, ... in every iteration, so only the
+ * two boundary elements of each chunk cross workgroups; with
  * CCB_VISIBILITY_ORDER they go through `halo`.
  *   bufA, bufB  device, n int32 each, 16-B aligned, not overlapping
  *   ws          device, workspace of 1 barrier (zeroed)
- *   halo        device, ccb_stencil_halo_bytes(nGrid, threads) bytes of
- *               scratch (contents ignored); may be NULL with
- *               CCB_VISIBILITY_FULL
+ *   halo        device, haloBytes bytes of scratch (contents ignored), at
+ *               least ccb_stencil_halo_bytes(n, threads, nGrid); may be NULL (and
+ *               haloBytes 0) with CCB_VISIBILITY_FULL
  * Errors: NULL_POINTER, INVALID_VALUE (n < 1, iters < 0, misaligned or
- * overlapping buffers, bad nGrid/threads), NOT_CORESIDENT. */
+ * overlapping buffers, halo scratch too small, bad nGrid/threads/mode),
+ * NOT_CORESIDENT. */
 CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32_t iters,
-                                  int32_t* ws, int32_t* halo, int32_t nGrid, int32_t threads,
-                                  int32_t wgsPerCu, uint32_t maxPoll, int32_t mode,
-                                  ccbStream stream);
+                                  int32_t* ws, int32_t* halo, size_t haloBytes, int32_t nGrid,
+                                  int32_t threads, int32_t wgsPerCu, uint32_t maxPoll,
+                                  int32_t mode, ccbStream stream);
 
 /* Bytes of the halo exchange scratch ccb_run_stencil needs with
- * CCB_VISIBILITY_ORDER: 16 bytes per wave (nGrid * threads / 64 waves). */
-CCB_API size_t ccb_stencil_halo_bytes(int32_t nGrid, int32_t threads);
+ * CCB_VISIBILITY_ORDER: two parities x nGrid workgroups x the chunks of the
+ * busiest workgroup x 2 int32 (0 for invalid arguments). */
+CCB_API size_t ccb_stencil_halo_bytes(int64_t n, int32_t threads, int32_t nGrid);
 
 /* ========================================================================
  * Floor microbenchmarks (the barrier's latency and bandwidth roofline)

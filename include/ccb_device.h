@@ -103,21 +103,33 @@ __device__ __forceinline__ uint32_t ccb_load_coherent(const uint32_t* p)
 /* Wait until every memory operation this thread issued has completed. */
 __device__ __forceinline__ void ccb_wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
+/* No work between the arrival and the poll. */
+struct ccb_no_overlap {
+    __device__ __forceinline__ void operator()() const {}
+};
+
 /* The barrier proper.
  *   ctr      K stripe lines (stripe s: int32 at ctr[s * CCB_LINE_WORDS])
  *   n        participant count (> 0)
  *   member   this workgroup's index among the participants, 0..n-1
  *   maxPoll  poll bound (> 0)
  *   err      error word (on a line of its own)
+ *   overlap  run by the arriving lane right after it has issued its arrival,
+ *            while the arrival is in flight (work that is not shared across
+ *            this barrier, e.g. a private output store)
+ * kPreWait (CCB_VIS_ORDER only): every thread first waits for all of its own
+ * memory operations.  A caller that has already waited for the stores it
+ * shares across the barrier may turn it off.
  * Every thread of the workgroup calls it.  Returns CCB_OK or
  * CCB_ERR_DEADLOCK (the same value in every thread). */
-template <int K, ccbVisibility kVis>
+template <int K, ccbVisibility kVis, bool kPreWait = true, class Overlap = ccb_no_overlap>
 __device__ __forceinline__ int32_t ccb_barrier(int32_t* ctr, int32_t n, int32_t member,
-                                               uint32_t maxPoll, int32_t* err)
+                                               uint32_t maxPoll, int32_t* err,
+                                               Overlap overlap = Overlap())
 {
     static_assert(K >= 1 && K <= 64, "stripes are polled by one wave");
     __shared__ int32_t ccb_result;
-    if (kVis == CCB_VIS_ORDER) ccb_wait_memory();  // this thread's accesses are done
+    if (kVis == CCB_VIS_ORDER && kPreWait) ccb_wait_memory();  // this thread's accesses are done
     __syncthreads();
     const uint32_t tid = threadIdx.x + blockDim.x * (threadIdx.y + blockDim.y * threadIdx.z);
     if (tid < 64) {  // wave 0
@@ -132,6 +144,7 @@ __device__ __forceinline__ int32_t ccb_barrier(int32_t* ctr, int32_t n, int32_t 
             const int32_t ns = (n - s + K - 1) / K;
             const int32_t before = __hip_atomic_fetch_add(ctr + s * CCB_LINE_WORDS, 1,
                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            overlap();
             epoch = before / ns + 1;
         }
         epoch = __shfl(epoch, 0, 64);

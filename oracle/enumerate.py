@@ -75,13 +75,37 @@ class Result:
 
 
 def _programs(rounds: Sequence[RoundSpec], n_participants: int,
-              skip: Sequence[Tuple[int, int]] = ()) -> List[List[Tuple[int, bool]]]:
-    """Per participant: the list of (round, takes_barrier) it executes."""
+              skip: Sequence[Tuple[int, int]] = (),
+              early_write: bool = False) -> List[List[Tuple[int, int]]]:
+    """Per participant: the flat list of (step kind, round) it executes.
+
+    In the plain schedule every member round is WRITE, ARRIVE, POLL, READ.
+    With early_write the member writes the witness of its NEXT member round
+    right after passing a barrier, before reading the current round (the
+    pipelined order the GPU kernels use); its first round's witness is
+    written before its first barrier.  A skipped barrier drops that round's
+    ARRIVE and POLL."""
     skipped = set(skip)
-    progs: List[List[Tuple[int, bool]]] = [[] for _ in range(n_participants)]
+    member_rounds: List[List[int]] = [[] for _ in range(n_participants)]
     for r, spec in enumerate(rounds):
         for p in spec.members:
-            progs[p].append((r, (p, r) not in skipped))
+            member_rounds[p].append(r)
+    progs: List[List[Tuple[int, int]]] = []
+    for p in range(n_participants):
+        mine = member_rounds[p]
+        steps: List[Tuple[int, int]] = []
+        if early_write and mine:
+            steps.append((WRITE, mine[0]))
+        for i, r in enumerate(mine):
+            if not early_write:
+                steps.append((WRITE, r))
+            if (p, r) not in skipped:
+                steps.append((ARRIVE, r))
+                steps.append((POLL, r))
+            if early_write and i + 1 < len(mine):
+                steps.append((WRITE, mine[i + 1]))
+            steps.append((READ, r))
+        progs.append(steps)
     return progs
 
 
@@ -89,6 +113,7 @@ def enumerate_schedules(rounds: Sequence[RoundSpec], n_participants: int, *,
                         ring_depth: int = 4, poll_cmp: str = "ge",
                         counter_init: Optional[Sequence[int]] = None,
                         skip: Sequence[Tuple[int, int]] = (),
+                        early_write: bool = False, stripes: int = 1,
                         max_states: int = 5_000_000) -> Result:
     """Explore every interleaving of the participants' steps.
 
@@ -98,18 +123,32 @@ def enumerate_schedules(rounds: Sequence[RoundSpec], n_participants: int, *,
     counter_init  starting value of each counter (default all zero)
     skip          (participant, round) pairs whose barrier is left out
                   (the participant still writes and reads)
+    early_write   use the pipelined step order (see _programs)
+    stripes       K: each counter is split into K stripes; the member with
+                  index m in its round's member list arrives on stripe m mod K,
+                  whose member count is n_s = ceil((N - s) / K), derives its
+                  round e = before // n_s + 1 from that stripe, and is released
+                  once every stripe l < min(N, K) holds at least e * n_l.  K = 1
+                  is the single counter of the SYNCALL guide.
     """
     n_counters = 1 + max(spec.counter for spec in rounds)
-    ctr0 = tuple(counter_init) if counter_init is not None else (0,) * n_counters
-    progs = _programs(rounds, n_participants, skip)
+    K = stripes
+    ctr0 = (tuple(c for c in counter_init for _ in range(1)) if counter_init is not None
+            else (0,) * n_counters)
+    if counter_init is not None:
+        # an initial value applies to stripe 0 of each counter
+        ctr0 = tuple(v if s == 0 else 0 for v in counter_init for s in range(K))
+    else:
+        ctr0 = (0,) * (n_counters * K)
+    progs = _programs(rounds, n_participants, skip, early_write)
     res = Result()
 
     # state = (pcs, counters, targets, slots)
-    #   pcs[p]     = (index into progs[p], phase)
-    #   targets[p] = the target derived at the last ARRIVE (or -1)
+    #   pcs[p]     = index of participant p's next step
+    #   targets[p] = the round (epoch) derived at its last ARRIVE (or -1)
     #   slots      = tuple over (ring row, participant) of the last round written
-    start = (tuple((0, WRITE) for _ in range(n_participants)), ctr0,
-             (-1,) * n_participants, (-1,) * (ring_depth * n_participants))
+    start = ((0,) * n_participants, ctr0, (-1,) * n_participants,
+             (-1,) * (ring_depth * n_participants))
     seen = set()
     stack = [start]
     while stack:
@@ -123,37 +162,45 @@ def enumerate_schedules(rounds: Sequence[RoundSpec], n_participants: int, *,
         successors = []
         all_done = True
         for p in range(n_participants):
-            idx, phase = pcs[p]
-            if idx >= len(progs[p]):
+            pc = pcs[p]
+            if pc >= len(progs[p]):
                 continue
             all_done = False
-            r, takes_barrier = progs[p][idx]
+            kind, r = progs[p][pc]
             spec = rounds[r]
             g = spec.counter
             row = r % ring_depth
-            if phase == WRITE:
+            nxt = _set(pcs, p, pc + 1)
+            if kind == WRITE:
                 new_slots = list(slots)
                 new_slots[row * n_participants + p] = r
-                nxt = ARRIVE if takes_barrier else READ
-                successors.append((_set(pcs, p, (idx, nxt)), ctrs, tgts, tuple(new_slots)))
-            elif phase == ARRIVE:
-                before = ctrs[g]
-                target = (before // spec.n + 1) * spec.n
-                successors.append((_set(pcs, p, (idx, POLL)), _set(ctrs, g, before + 1),
-                                   _set(tgts, p, target), slots))
-            elif phase == POLL:
-                c = ctrs[g]
-                ok = c >= tgts[p] if poll_cmp == "ge" else c == tgts[p]
+                successors.append((nxt, ctrs, tgts, tuple(new_slots)))
+            elif kind == ARRIVE:
+                n = spec.n
+                st = spec.members.index(p) % K
+                ns = (n - st + K - 1) // K
+                before = ctrs[g * K + st]
+                epoch = before // ns + 1       # target = epoch * ns, the pages' rule per stripe
+                successors.append((nxt, _set(ctrs, g * K + st, before + 1), _set(tgts, p, epoch),
+                                   slots))
+            elif kind == POLL:
+                n = spec.n
+                epoch = tgts[p]
+                ok = True
+                for lane in range(min(n, K)):
+                    nl = (n - lane + K - 1) // K
+                    c = ctrs[g * K + lane]
+                    ok = ok and (c >= epoch * nl if poll_cmp == "ge" else c == epoch * nl)
                 if ok:
-                    successors.append((_set(pcs, p, (idx, READ)), ctrs, tgts, slots))
+                    successors.append((nxt, ctrs, tgts, slots))
             else:  # READ
                 for q in spec.members:
                     got = slots[row * n_participants + q]
                     if got != r:
                         res.violations.append((r, p, q, got))
-                successors.append((_set(pcs, p, (idx + 1, WRITE)), ctrs, tgts, slots))
+                successors.append((nxt, ctrs, tgts, slots))
         if all_done:
-            res.final_counters.add(ctrs)
+            res.final_counters.add(tuple(sum(ctrs[g * K:(g + 1) * K]) for g in range(n_counters)))
             res.complete_schedules_seen = True
             continue
         if not successors:

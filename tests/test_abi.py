@@ -90,8 +90,10 @@ def test_constants_match_pages(ccb):
     assert int(m.group(1)) == consts["soft_max_poll_iterations"] == ccb.CCB_SOFT_MAX_POLL
     assert ccb.ccb_syncall_workspace_bytes(1) == (ccb.CCB_STRIPES + 1) * 128
     assert ccb.ccb_syncall_workspace_bytes(3) == (3 * ccb.CCB_STRIPES + 1) * 128
-    assert ccb.ccb_stencil_halo_bytes(1024, 256) == 1024 * 4 * 16
-    assert ccb.ccb_stencil_halo_bytes(0, 256) == 0
+    # 2^26 elements in chunks of 1024, 1024 workgroups: 64 chunks each
+    assert ccb.ccb_stencil_halo_bytes(1 << 26, 256, 1024) == 2 * 1024 * 64 * 2 * 4
+    assert ccb.ccb_stencil_halo_bytes((1 << 20) + 1, 256, 1024) == 2 * 1024 * 2 * 2 * 4
+    assert ccb.ccb_stencil_halo_bytes(0, 256, 4) == 0
 
 
 def test_validation_before_device_work(ccb):
@@ -115,10 +117,11 @@ def test_validation_before_device_work(ccb):
     assert ccb.ccb_run_barrier_only(128, None, None, 1, 8, 64, 9) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_run_slot_rounds(128, None, 256, None, 0, 1, 8, 64) == ccb.CCB_ERR_NULL_POINTER
     assert ccb.ccb_run_grouped_rounds(128, 256, 256, None, 0, 1, 7, 64) == ccb.CCB_ERR_INVALID_VALUE
-    assert ccb.ccb_run_stencil(None, 256, 10, 1, 128, 512, 1, 64) == ccb.CCB_ERR_NULL_POINTER
-    assert ccb.ccb_run_stencil(4096, 4096, 10, 1, 128, 512, 1, 64) == ccb.CCB_ERR_INVALID_VALUE
-    assert ccb.ccb_run_stencil(4100, 8192, 10, 1, 128, 512, 1, 64) == ccb.CCB_ERR_INVALID_VALUE
-    assert ccb.ccb_run_stencil(4096, 8192, 10, 1, 128, None, 1, 64) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_run_stencil(None, 256, 10, 1, 128, 512, 64, 1, 64) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_run_stencil(4096, 4096, 10, 1, 128, 512, 64, 1, 64) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_stencil(4100, 8192, 10, 1, 128, 512, 64, 1, 64) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_stencil(4096, 8192, 10, 1, 128, None, 0, 1, 64) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_run_stencil(4096, 8192, 10, 1, 128, 512, 8, 1, 64) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_run_barrier_only(128, None, None, 1, 8, 64, mode=9) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_bench_atomic_chain(None, 256, 1) == ccb.CCB_ERR_NULL_POINTER
     assert ccb.ccb_bench_atomic_chain(128, 256, 0) == ccb.CCB_ERR_INVALID_VALUE

@@ -32,7 +32,10 @@ MODE_IDS = ["striped-order", "flat-order", "striped-full", "flat-full"]
     (5, 4, 2, 64),                 # fewer elements than lanes
     (1000, 1, 3, 64),              # ragged spans, one iteration, no barrier
     (65536 * 3 + 17, 5, 16, 256),  # several full steps + ragged tail per wave
-    (1 << 20, 8, 64, 256),         # several tiles, exact spans
+    (1 << 20, 8, 64, 256),         # several chunks per workgroup, no partial chunk
+    (1024 * 5, 6, 7, 256),         # fewer chunks than workgroups
+    (256 * 9 + 3, 9, 2, 64),       # partial last chunk after full ones, n % 4 != 0
+    (1024 * 2000 + 5, 3, 1, 256),  # one workgroup, more chunks than the LDS staging holds
     (123457, 7, 37, 192),          # ragged everything, odd iteration count
     (4096, 0, 4, 64),              # zero iterations: result is the input
 ])
@@ -66,9 +69,12 @@ def test_stencil_invalid(wl):
     a = torch.zeros(1024, dtype=torch.int32, device="cuda")
     ws = wl.workspace(1)
     b = torch.zeros(1024, dtype=torch.int32, device="cuda")
-    halo = wl.halo_scratch(4, 64)
-    assert ccb.ccb_run_stencil(a, a, 1024, 1, ws, halo, 4, 64) == ccb.CCB_ERR_INVALID_VALUE  # overlap
-    assert ccb.ccb_run_stencil(a.data_ptr() + 4, b, 100, 1, ws, halo, 4, 64) == ccb.CCB_ERR_INVALID_VALUE
-    assert ccb.ccb_run_stencil(a, None, 1024, 1, ws, halo, 4, 64) == ccb.CCB_ERR_NULL_POINTER
-    assert ccb.ccb_run_stencil(a, b, 1024, 1, ws, None, 4, 64, mode=0) == ccb.CCB_ERR_NULL_POINTER
-    assert ccb.ccb_run_stencil(a, b, 1024, 1, ws, halo, 4, 64, mode=7) == ccb.CCB_ERR_INVALID_VALUE
+    halo = wl.halo_scratch(1024, 64, 4)
+    assert ccb.ccb_run_stencil(a, a, 1024, 1, ws, halo, None, 4, 64) == ccb.CCB_ERR_INVALID_VALUE  # overlap
+    assert ccb.ccb_run_stencil(a.data_ptr() + 4, b, 100, 1, ws, halo, None, 4, 64) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_stencil(a, None, 1024, 1, ws, halo, None, 4, 64) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_run_stencil(a, b, 1024, 1, ws, None, 0, 4, 64, mode=0) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_run_stencil(a, b, 1024, 1, ws, halo, None, 4, 64, mode=7) == ccb.CCB_ERR_INVALID_VALUE
+    # scratch too small for the chunk count: rejected before launch
+    assert ccb.ccb_run_stencil(a, b, 1024, 2, ws, halo, 16, 4, 64, mode=0) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_stencil(a, b, 1024, 2, ws, None, 0, 4, 64, mode=2) == ccb.CCB_OK
