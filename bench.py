@@ -271,6 +271,7 @@ class Bench:
         ccb.check(st, "stencil status")
         assert arr == [(STENCIL_ITERS - 1) * s["n_wg"]], arr
         st_ms = statistics.median(times)
+        self.stencil_phases(run_args=(a, b, x0, halo, s))
         alg_bytes = STENCIL_BYTES_PER_ITER * STENCIL_ITERS
         achieved = alg_bytes / (st_ms / 1e3) / 1e9
         self.extra["stencil_barriers_per_launch"] = STENCIL_ITERS - 1
@@ -279,6 +280,37 @@ class Bench:
                 "traffic": profiled_traffic(), "kernel": "ccb_k_stencil",
                 "launch_ms": round(st_ms, 4), "algorithmic_bytes": alg_bytes,
                 "frac_of_copy_ceiling": round(achieved / copy_gbs, 4) if copy_gbs else None}
+
+    def stencil_phases(self, run_args):
+        """One more launch with per-workgroup wall-clock stamps: the data
+        phases alone (first release to last data end of each iteration), the
+        barriers (last data end to last release) and the finish skew."""
+        np, torch, ccb, ws, stream = self.np, self.torch, self.ccb, self.ws, self.stream
+        a, b, x0, halo, s = run_args
+        G, iters = s["n_wg"], STENCIL_ITERS
+        tl = torch.zeros(G * (2 * iters + 1), dtype=torch.int64, device=self.dev)
+        a.copy_(x0)
+        torch.cuda.synchronize()
+        ccb.check(ccb.ccb_syncall_workspace_reset(ws, 1, stream), "reset")
+        ccb.check(ccb.ccb_run_stencil(a, b, STENCIL_N, iters, ws, halo, None, G, s["threads"], 4, 0,
+                                      self.mode, stream, timeline=tl), "stencil timeline")
+        stream.synchronize()
+        st, _ = ccb.ccb_syncall_status(ws, 1, stream)
+        ccb.check(st, "stencil timeline status")
+        t = tl.cpu().numpy().reshape(G, 2 * iters + 1).astype(np.float64) * self.tick_ns
+        start, dend, rel = t[:, 0], t[:, 1::2], t[:, 2::2]
+        first = np.concatenate([[start.min()], rel[:, :-1].min(axis=0)])
+        data = dend.max(axis=0) - first
+        barrier = (rel.max(axis=0) - dend.max(axis=0))[:-1]
+        skew = dend.max(axis=0) - dend.min(axis=0)
+        self.extra["stencil_phases"] = {
+            "data_phase_us_mean": round(float(data.mean()) / 1e3, 2),
+            "data_phase_GBs": round(STENCIL_BYTES_PER_ITER / float(data.mean()), 1),
+            "data_phase_frac_of_peak": round(STENCIL_BYTES_PER_ITER / float(data.mean()) / HBM_PEAK_GBS, 4),
+            "barrier_us_mean": round(float(barrier.mean()) / 1e3, 3),
+            "finish_skew_us_mean": round(float(skew.mean()) / 1e3, 2),
+            "in_kernel_total_ms": round(float(t[:, -1].max() - start.min()) / 1e6, 4)}
+        log(f"stencil phases: {self.extra['stencil_phases']}")
 
     # ------------------------------------------------------------ batched CntNotify
     def cnt_batch(self):

@@ -103,7 +103,7 @@ _f = {
     "ccb_run_grouped_rounds": _sig("ccb_run_grouped_rounds", _I32, _V, _V, _V, _V, _U64, _I32, _I32,
                                    _I32, _I32, _U32, _I32, _V),
     "ccb_run_stencil": _sig("ccb_run_stencil", _I32, _V, _V, _I64, _I32, _V, _V, ctypes.c_size_t,
-                            _I32, _I32, _I32, _U32, _I32, _V),
+                            _V, _I32, _I32, _I32, _U32, _I32, _V),
     "ccb_stencil_halo_bytes": _sig("ccb_stencil_halo_bytes", ctypes.c_size_t, _I64, _I32, _I32),
     "ccb_bench_atomic_chain": _sig("ccb_bench_atomic_chain", _I32, _V, _V, _I32, _I32, _I32, _V),
     "ccb_bench_atomic_contended": _sig("ccb_bench_atomic_contended", _I32, _V, _V, _I32, _I32, _V),
@@ -196,13 +196,14 @@ def ccb_stencil_halo_bytes(n: int, threads: int, n_grid: int) -> int:
 
 
 def ccb_run_stencil(buf_a, buf_b, n, iters, ws, halo, halo_bytes, n_grid, threads, wgs_per_cu=0,
-                    max_poll=0, mode=0, stream=None) -> int:
+                    max_poll=0, mode=0, stream=None, timeline=None) -> int:
     """halo_bytes: size of the halo scratch; for a torch tensor pass None to
     use its size."""
     if halo_bytes is None:
         halo_bytes = 0 if halo is None else halo.numel() * halo.element_size()
     return _f["ccb_run_stencil"](_p(buf_a), _p(buf_b), n, iters, _p(ws), _p(halo), halo_bytes,
-                                 n_grid, threads, wgs_per_cu, max_poll, mode, _s(stream))
+                                 _p(timeline), n_grid, threads, wgs_per_cu, max_poll, mode,
+                                 _s(stream))
 
 
 # --- floor microbenchmarks --------------------------------------------------------

@@ -314,9 +314,10 @@ CCB_API size_t ccb_stencil_halo_bytes(int64_t n, int32_t threads, int32_t nGrid)
 }
 
 CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32_t iters,
-                                  int32_t* ws, int32_t* halo, size_t haloBytes, int32_t nGrid,
-                                  int32_t threads, int32_t wgsPerCu, uint32_t maxPoll,
-                                  int32_t mode, ccbStream stream)
+                                  int32_t* ws, int32_t* halo, size_t haloBytes,
+                                  uint64_t* timeline, int32_t nGrid, int32_t threads,
+                                  int32_t wgsPerCu, uint32_t maxPoll, int32_t mode,
+                                  ccbStream stream)
 {
     if (bufA == nullptr || bufB == nullptr || ws == nullptr) return CCB_ERR_NULL_POINTER;
     const bool needHalo = valid_mode(mode) && (mode & CCB_VISIBILITY_FULL) == 0;
@@ -333,7 +334,9 @@ CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32
     ccbStatus st = plan_persistent(ccb::KernelId::Stencil, mode, nGrid, threads, wgsPerCu,
                                    (hipStream_t)stream, &ls);
     if (st != CCB_OK) return st;
-    return from_hip(ccb::launch_stencil(ls, bufA, bufB, n, iters, ws, halo, poll_bound(maxPoll)));
+    if (timeline != nullptr && !aligned(timeline, 8)) return CCB_ERR_INVALID_VALUE;
+    return from_hip(ccb::launch_stencil(ls, bufA, bufB, n, iters, ws, halo, timeline,
+                                        poll_bound(maxPoll)));
 }
 
 // ===========================================================================
@@ -373,7 +376,7 @@ CCB_API ccbStatus ccb_bench_copy(void* dst, const void* src, int64_t nBytes, ccb
     if (st != CCB_OK) return st;
     if (nBytes == 0) return CCB_OK;
     return from_hip(ccb::launch_copy(static_cast<int4*>(dst), static_cast<const int4*>(src),
-                                     nBytes / 16, info.numCUs * 8, (hipStream_t)stream));
+                                     nBytes / 16, info.numCUs * 4, (hipStream_t)stream));
 }
 
 // ===========================================================================

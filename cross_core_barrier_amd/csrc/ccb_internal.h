@@ -41,7 +41,8 @@ hipError_t launch_grouped_rounds(const LaunchShape& ls, int32_t* ws, uint32_t* s
                                  uint32_t* out, int32_t* wgStatus, uint64_t seed, int32_t rounds,
                                  uint32_t maxPoll);
 hipError_t launch_stencil(const LaunchShape& ls, int32_t* bufA, int32_t* bufB, int64_t n,
-                          int32_t iters, int32_t* ws, int32_t* halo, uint32_t maxPoll);
+                          int32_t iters, int32_t* ws, int32_t* halo, uint64_t* timeline,
+                          uint32_t maxPoll);
 hipError_t launch_cnt_batch(const uint32_t* val, const uint8_t* meta, int64_t nCounters,
                             int32_t nOps, uint32_t* finalOut, uint8_t* rel, int32_t nRelRows,
                             int32_t* err, bool vec4, hipStream_t s);

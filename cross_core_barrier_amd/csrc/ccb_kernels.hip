@@ -348,6 +348,16 @@ __device__ __forceinline__ int4 load4(const int32_t* p)
     }
 }
 
+__device__ __forceinline__ void set_prio(int p)
+{
+    switch (p & 3) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+    }
+}
+
 // Largest number of chunks per workgroup whose halos are staged in LDS; a
 // launch with more chunks per workgroup reads them one by one instead.
 constexpr int kHaloLds = 1024;
@@ -418,6 +428,12 @@ __device__ __forceinline__ void stencil_sweep(const StencilGeom& g, const int32_
     const int64_t fullMine = g.w < g.nFullChunks ? (g.nFullChunks - 1 - g.w) / g.G + 1 : 0;
     for (int64_t k = 0; k < fullMine; ++k) {
         const int64_t c = g.w + k * g.G;
+        // Rotate the wave priority chunk by chunk.  With equal priorities
+        // the oldest wave wins every issue arbitration, so of the workgroups
+        // sharing a CU the last-dispatched one finishes each iteration ~9 us
+        // behind the first, and the barrier waits for it.  Rotating makes
+        // the workgroups take turns (w * 4 / G is the dispatch round).
+        set_prio((int)((g.w * 4 / g.G + k) & 3));
         const int64_t w0 = c * g.chunk + (int64_t)wave * 256;  // this wave's piece
         const int4 v = load4<ccb::kStencilNTLoad>(x + w0 + 4 * lane);
         int32_t lh, rh;
@@ -444,6 +460,7 @@ __device__ __forceinline__ void stencil_sweep(const StencilGeom& g, const int32_
             if (pubHalo != nullptr) ccb_store_coherent(halo_entry(pubHalo, g, pOut, g.w, k, 1), o.w);
         }
     }
+    set_prio(0);
     if (fullMine < g.myChunks) {
         // the partial last chunk, one element per thread
         const int64_t k = fullMine;
@@ -470,15 +487,16 @@ __device__ __forceinline__ void stencil_sweep(const StencilGeom& g, const int32_
 
 // The exchange buffer is workgroup-major: halo[parity][w][k][2] holds the
 // first and last output element of workgroup w's k-th chunk (chunk
-// w + k * G).  At the start of an iteration each workgroup copies the
-// entries it needs -- the last elements of its left neighbour's chunks and
-// the first elements of its right neighbour's chunks -- into LDS with one
-// device-coherent load per entry, and at the end it publishes its own
-// entries the same way, so no coherent access sits inside the sweep.
+// w + k * G).  Only wave 0 (which needs the left neighbours of the chunks)
+// and the last wave (right neighbours) touch it: at the start of an
+// iteration each copies the entries it needs into its own LDS array with
+// device-coherent loads issued next to its first data load, and at the end
+// each publishes its own entries from LDS.  No workgroup barrier is needed
+// for that, and the other waves never wait on a coherent access.
 template <int K, ccbVisibility V>
 __global__ __launch_bounds__(1024) void ccb_k_stencil(int32_t* bufA, int32_t* bufB, int64_t n,
                                                        int32_t iters, int32_t* ws, int32_t* halo,
-                                                       uint32_t maxPoll)
+                                                       uint64_t* timeline, uint32_t maxPoll)
 {
     __shared__ int32_t inLeft[kHaloLds], inRight[kHaloLds];   // neighbours of my chunks
     __shared__ int32_t outFirst[kHaloLds], outLast[kHaloLds]; // my chunks' end outputs
@@ -492,7 +510,14 @@ __global__ __launch_bounds__(1024) void ccb_k_stencil(int32_t* bufA, int32_t* bu
     g.kMax = (g.nChunks + g.G - 1) / g.G;  // chunks of the busiest workgroup
     g.myChunks = g.w < g.nChunks ? (g.nChunks - 1 - g.w) / g.G + 1 : 0;
     const bool staged = g.kMax <= kHaloLds;
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int nWave = blockDim.x / kWave;
     int32_t* err = ws + CCB_STRIPES * CCB_LINE_WORDS;
+    // timeline (optional): per workgroup, the start, then for every iteration
+    // the end of its data phase and the moment it left the following barrier
+    uint64_t* stamps = timeline != nullptr ? timeline + (size_t)g.w * (2 * (size_t)iters + 1) : nullptr;
+    if (stamps != nullptr && threadIdx.x == 0) stamps[0] = wall_clock64();
     for (int32_t t = 0; t < iters; ++t) {
         const int32_t* x = (t & 1) ? bufB : bufA;
         int32_t* y = (t & 1) ? bufA : bufB;
@@ -504,11 +529,16 @@ __global__ __launch_bounds__(1024) void ccb_k_stencil(int32_t* bufA, int32_t* bu
                                            publish && staged ? outLast : nullptr,
                                            publish && !staged ? halo : nullptr, pOut);
         } else if (staged) {
-            for (int64_t k = threadIdx.x; k < g.myChunks; k += blockDim.x) {
-                inLeft[k] = chunk_left<HaloSrc::Coherent>(g, x, k, nullptr, halo, pIn);
-                inRight[k] = chunk_right<HaloSrc::Coherent>(g, x, k, nullptr, halo, pIn);
+            if (wave == 0)
+                for (int64_t k = lane; k < g.myChunks; k += kWave)
+                    inLeft[k] = chunk_left<HaloSrc::Coherent>(g, x, k, nullptr, halo, pIn);
+            if (wave == nWave - 1)
+                for (int64_t k = lane; k < g.myChunks; k += kWave)
+                    inRight[k] = chunk_right<HaloSrc::Coherent>(g, x, k, nullptr, halo, pIn);
+            if (g.myChunks > 0 && (g.w + (g.myChunks - 1) * g.G) >= g.nFullChunks) {
+                // a partial chunk reads its left neighbour from every thread
+                __syncthreads();
             }
-            __syncthreads();
             stencil_sweep<HaloSrc::Staged>(g, x, y, inLeft, inRight, halo, pIn,
                                            publish ? outFirst : nullptr,
                                            publish ? outLast : nullptr, nullptr, pOut);
@@ -517,15 +547,35 @@ __global__ __launch_bounds__(1024) void ccb_k_stencil(int32_t* bufA, int32_t* bu
                                              nullptr, publish ? halo : nullptr, pOut);
         }
         if (publish && staged) {
+            const bool partial = g.myChunks > 0 && (g.w + (g.myChunks - 1) * g.G) >= g.nFullChunks;
+            if (partial) __syncthreads();  // partial-chunk ends come from any thread
+            if (wave == 0 || partial)
+                for (int64_t k = (partial ? threadIdx.x : lane); k < g.myChunks;
+                     k += (partial ? blockDim.x : kWave))
+                    ccb_store_coherent(halo_entry(halo, g, pOut, g.w, k, 0), outFirst[k]);
+            if (wave == nWave - 1 || partial)
+                for (int64_t k = (partial ? threadIdx.x : lane); k < g.myChunks;
+                     k += (partial ? blockDim.x : kWave))
+                    ccb_store_coherent(halo_entry(halo, g, pOut, g.w, k, 1), outLast[k]);
+        }
+        if (stamps != nullptr) {
             __syncthreads();
-            for (int64_t k = threadIdx.x; k < g.myChunks; k += blockDim.x) {
-                ccb_store_coherent(halo_entry(halo, g, pOut, g.w, k, 0), outFirst[k]);
-                ccb_store_coherent(halo_entry(halo, g, pOut, g.w, k, 1), outLast[k]);
-            }
+            if (threadIdx.x == 0) stamps[1 + 2 * t] = wall_clock64();
         }
         if (t + 1 < iters) {
-            if (ccb_barrier<K, V>(ws, (int32_t)g.G, (int32_t)g.w, maxPoll, err) != CCB_OK) break;
+            // Only the coherent halo stores are shared with other workgroups
+            // across the barrier, so only the waves that issued them wait for
+            // their memory operations; the data stores are read back by this
+            // workgroup alone (ordered by the workgroup barrier).
+            if (V == CCB_VIS_ORDER) {
+                const bool partial =
+                    g.myChunks > 0 && (g.w + (g.myChunks - 1) * g.G) >= g.nFullChunks;
+                if (wave == 0 || wave == nWave - 1 || partial || !staged) ccb_wait_memory();
+            }
+            if (ccb_barrier<K, V, false>(ws, (int32_t)g.G, (int32_t)g.w, maxPoll, err) != CCB_OK)
+                break;
         }
+        if (stamps != nullptr && threadIdx.x == 0) stamps[2 + 2 * t] = wall_clock64();
     }
 }
 
@@ -799,20 +849,18 @@ __global__ void ccb_k_atomic_contended(int32_t* line, uint64_t* ticks, int32_t i
     if (v == 0x7fffffff) ticks[2 * blockIdx.x] = 0;
 }
 
+// Streaming copy: every thread moves one 16-byte vector per step and the
+// whole grid advances through memory together (the access order that gets
+// the most out of HBM on this GPU), loads non-temporal.
 __global__ __launch_bounds__(256) void ccb_k_copy(int4* __restrict__ dst,
                                                   const int4* __restrict__ src, int64_t n16)
 {
-    constexpr int U = 4;
+    typedef int v4i __attribute__((ext_vector_type(4)));
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + (U - 1) * stride < n16; i += U * stride) {
-        int4 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = src[i + u * stride];
-#pragma unroll
-        for (int u = 0; u < U; ++u) dst[i + u * stride] = v[u];
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+        const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + i));
+        dst[i] = make_int4(v.x, v.y, v.z, v.w);
     }
-    for (; i < n16; i += stride) dst[i] = src[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -871,9 +919,10 @@ hipError_t launch_grouped_rounds(const LaunchShape& ls, int32_t* ws, uint32_t* s
 }
 
 hipError_t launch_stencil(const LaunchShape& ls, int32_t* bufA, int32_t* bufB, int64_t n,
-                          int32_t iters, int32_t* ws, int32_t* halo, uint32_t maxPoll)
+                          int32_t iters, int32_t* ws, int32_t* halo, uint64_t* timeline,
+                          uint32_t maxPoll)
 {
-    void* args[] = {&bufA, &bufB, &n, &iters, &ws, &halo, &maxPoll};
+    void* args[] = {&bufA, &bufB, &n, &iters, &ws, &halo, &timeline, &maxPoll};
     return coop(ls.fn, ls.nGrid, ls.threads, ls.lds, ls.stream, args);
 }
 

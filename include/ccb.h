@@ -235,13 +235,19 @@ CCB_API ccbStatus ccb_run_grouped_rounds(int32_t* ws, uint32_t* slots, uint32_t*
  *   halo        device, haloBytes bytes of scratch (contents ignored), at
  *               least ccb_stencil_halo_bytes(n, threads, nGrid); may be NULL (and
  *               haloBytes 0) with CCB_VISIBILITY_FULL
+ *   timeline    device, nGrid * (2 * iters + 1) uint64 wall-clock stamps, or
+ *               NULL: for workgroup w, [w*(2*iters+1)] = its start, then for
+ *               each iteration t, [.. + 1 + 2t] = the end of its data phase and
+ *               [.. + 2 + 2t] = when it left the following barrier (the end of
+ *               the launch for the last iteration); 8-B aligned
  * Errors: NULL_POINTER, INVALID_VALUE (n < 1, iters < 0, misaligned or
  * overlapping buffers, halo scratch too small, bad nGrid/threads/mode),
  * NOT_CORESIDENT. */
 CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32_t iters,
-                                  int32_t* ws, int32_t* halo, size_t haloBytes, int32_t nGrid,
-                                  int32_t threads, int32_t wgsPerCu, uint32_t maxPoll,
-                                  int32_t mode, ccbStream stream);
+                                  int32_t* ws, int32_t* halo, size_t haloBytes,
+                                  uint64_t* timeline, int32_t nGrid, int32_t threads,
+                                  int32_t wgsPerCu, uint32_t maxPoll, int32_t mode,
+                                  ccbStream stream);
 
 /* Bytes of the halo exchange scratch ccb_run_stencil needs with
  * CCB_VISIBILITY_ORDER: two parities x nGrid workgroups x the chunks of the
