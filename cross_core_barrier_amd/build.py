@@ -26,6 +26,9 @@ def hipcc_command(out: str, extra=()) -> list:
         "hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed-FP32 instructions stay off for all device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # every atomic here is issued by one lane; the wave-level atomic
+        # rewrite would only add a wait on the reply before the barrier's poll
+        "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
         "-fvisibility=hidden", "-Wall",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         *extra,

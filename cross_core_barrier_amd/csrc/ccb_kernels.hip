@@ -21,7 +21,7 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kRing = 4;  // witness slot rows reused round-robin
+constexpr int kRing = CCB_SLOT_ROWS;  // witness slot rows reused round-robin
 
 __device__ __forceinline__ bool leader() { return threadIdx.x == 0; }
 
@@ -99,6 +99,7 @@ __global__ __launch_bounds__(1024) void ccb_k_barrier_only(int32_t* ws, uint32_t
                                                             int32_t* wgStatus, int32_t rounds,
                                                             int32_t nMembers, uint32_t maxPoll)
 {
+    __shared__ int32_t result[2];
     record_placement(placement);
     const int32_t w = blockIdx.x;
     if (w >= nMembers) {
@@ -107,8 +108,21 @@ __global__ __launch_bounds__(1024) void ccb_k_barrier_only(int32_t* ws, uint32_t
     }
     int32_t* err = ws + CCB_STRIPES * CCB_LINE_WORDS;
     int32_t rc = CCB_OK;
-    for (int32_t r = 0; r < rounds && rc == CCB_OK; ++r)
-        rc = ccb_barrier<K, V>(ws, nMembers, w, maxPoll, err);
+    // Rounds follow each other with nothing in between, so the workgroup
+    // barrier that releases round r also orders round r + 1's arrival: one
+    // per round.  The result word alternates so that wave 0 can publish
+    // round r + 1's result while a slow wave still reads round r's.
+    for (int32_t r = 0; r < rounds; ++r) {
+        if (threadIdx.x < kWave) {
+            int32_t before = 0;
+            if (leader()) before = ccb_arrive<K, V>(ws, w);
+            const int32_t e = ccb_await<K, V>(ws, nMembers, w, before, maxPoll, err);
+            if (leader()) result[r & 1] = e;
+        }
+        __syncthreads();
+        rc = result[r & 1];
+        if (rc != CCB_OK) break;
+    }
     if (wgStatus != nullptr && leader()) wgStatus[w] = rc == CCB_OK ? 1 : 3;
 }
 
@@ -117,15 +131,25 @@ __global__ __launch_bounds__(1024) void ccb_k_barrier_only(int32_t* ws, uint32_t
 // guide §6.1, run for many rounds): write own slot, barrier, sum all slots.
 //
 // With CCB_VIS_FULL each round is written in that order with plain accesses.
-// With CCB_VIS_ORDER the round is pipelined without changing what is
-// computed: right after passing barrier r a member already stores its
-// witness for round r + 1 (ring row (r + 1) mod 4, which nobody reads before
-// barrier r + 1), then reads round r's slots; its partial sums go to LDS and
-// lane 0 finishes the sum and stores out[r] while its arrival for barrier
-// r + 1 is in flight.  The slot store has completed before the member's
-// last slot load returned (the wait below), so the barrier needs no further
-// wait.  The brute-force enumerator checks this schedule (early writes)
-// against the ring depth.
+// With CCB_VIS_ORDER the rounds are pipelined two deep without changing what
+// is computed, and each round costs one workgroup barrier.  In its round i a
+// member
+//   * arrives at barrier i (its witness for round i was stored and waited
+//     for during round i - 1, and so were its loads of row i - 2),
+//   * while the arrival is in flight, loads row i - 1 (barrier i - 1 has been
+//     passed) without waiting, stores its witness for round i + 1, sums row
+//     i - 2 (loaded during round i - 1) into LDS partials and stores out for
+//     round i - 3 from the partials of the round before,
+//   * waits for barrier i, then for its own loads and stores, and releases
+//     the workgroup.
+// So the loads and stores of a round overlap a barrier's wait instead of
+// adding memory round trips to every round.  Counted in the member's own
+// rounds, a witness is written after passing the barrier two rounds before
+// its own and a row may be read until the member arrives two rounds after
+// it; the brute-force enumerator shows that this needs D >= 4 slot rows
+// for the whole grid and D >= 6 for the grouped pattern below, and
+// D = CCB_SLOT_ROWS = 6 is used for both.  The member's last wave does the
+// witness and output stores, so wave 0's poll does not wait for them.
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -135,6 +159,49 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v)
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
     return v;
+}
+
+// One witness row read by the workgroup, kept in flight across a barrier:
+// up to kRowRegs slots per thread are loaded without waiting and summed
+// later; members beyond kRowRegs * blockDim.x are read synchronously.
+constexpr int kRowRegs = 4;
+
+struct RowRead {
+    uint32_t v[kRowRegs];
+    uint32_t tail;
+    int32_t n;
+
+    __device__ __forceinline__ void issue(const uint32_t* row, int32_t count)
+    {
+        n = count;
+#pragma unroll
+        for (int j = 0; j < kRowRegs; ++j) {
+            const int32_t i = (int32_t)threadIdx.x + j * (int32_t)blockDim.x;
+            // wave-uniform test; lanes past the end reload slot 0 and are
+            // left out of the sum
+            if (j * (int32_t)blockDim.x < count) v[j] = ccb_load_coherent(row + (i < count ? i : 0));
+        }
+        tail = 0;
+        for (int32_t i = threadIdx.x + kRowRegs * blockDim.x; i < count; i += blockDim.x)
+            tail += ccb_load_coherent(row + i);
+    }
+
+    // This thread's share of the row sum (mod 2^32).
+    __device__ __forceinline__ uint32_t sum() const
+    {
+        uint32_t s = tail;
+#pragma unroll
+        for (int j = 0; j < kRowRegs; ++j)
+            if ((int32_t)threadIdx.x + j * (int32_t)blockDim.x < n) s += v[j];
+        return s;
+    }
+};
+
+// Stores this wave's share of a row sum into the LDS partials.
+__device__ __forceinline__ void wave_partial(uint32_t* partial, uint32_t s)
+{
+    s = wave_sum(s);
+    if ((threadIdx.x % kWave) == 0) partial[threadIdx.x / kWave] = s;
 }
 
 // Finishes round r's sum from the per-wave partials and stores it.
@@ -150,6 +217,78 @@ struct FinishRound {
         *dst = s;
     }
 };
+
+// The pipelined witness rounds of one member (CCB_VIS_ORDER).  Sched names
+// the member's rounds and where each one's counter, row and slot are:
+//   first(), next(q)        the member's first round and the one after q
+//                           (`rounds` once there are no more)
+//   counter(q), n(q), member(q)   barrier of round q
+//   row(q), len(q)          the slots summed in round q
+//   slot(q)                 this member's slot in round q
+template <int K, ccbVisibility V, class Sched>
+__device__ __forceinline__ int32_t witness_pipeline(const Sched& sc, int32_t rounds,
+                                                    uint32_t* out, int32_t nGrid, int32_t w,
+                                                    uint64_t seed, uint32_t maxPoll, int32_t* err)
+{
+    __shared__ uint32_t partials[2][1024 / kWave];
+    __shared__ int32_t result[2];
+    const int nWave = blockDim.x / kWave;
+    const bool scribe = threadIdx.x == (uint32_t)((nWave - 1) * kWave);
+    // the member's rounds: cur (this one), nxt, and the three before it
+    int32_t cur = sc.first();
+    int32_t nxt = cur < rounds ? sc.next(cur) : rounds;
+    int32_t p1 = -1, p2 = -1, p3 = -1;
+    if (scribe && cur < rounds) ccb_store_coherent(sc.slot(cur), witness(seed, (uint32_t)cur, (uint32_t)w));
+    ccb_wait_memory();
+    __syncthreads();
+    RowRead rowA, rowB;
+    auto work = [&](int32_t i, RowRead& into, RowRead& from) {
+        if (p1 >= 0) into.issue(sc.row(p1), sc.len(p1));
+        if (scribe && nxt < rounds)
+            ccb_store_coherent(sc.slot(nxt), witness(seed, (uint32_t)nxt, (uint32_t)w));
+        if (p2 >= 0) wave_partial(partials[i & 1], from.sum());
+        if (scribe && p3 >= 0)
+            FinishRound{partials[(i - 1) & 1], nWave, out + (size_t)p3 * nGrid + w}();
+    };
+    auto shift = [&]() {
+        p3 = p2;
+        p2 = p1;
+        p1 = cur;
+        cur = nxt;
+        nxt = nxt < rounds ? sc.next(nxt) : rounds;
+    };
+    auto round = [&](int32_t i, RowRead& into, RowRead& from) {
+        const int32_t q = cur;
+        int32_t before = 0;
+        if (leader()) before = ccb_arrive<K, V>(sc.counter(q), sc.member(q));
+        work(i, into, from);
+        if (threadIdx.x < kWave) {
+            const int32_t e = ccb_await<K, V>(sc.counter(q), sc.n(q), sc.member(q), before, maxPoll, err);
+            if (leader()) result[i & 1] = e;
+        }
+        ccb_wait_memory();  // this round's loads and stores, before the next arrival
+        __syncthreads();
+        shift();
+        return result[i & 1];
+    };
+    int32_t rc = CCB_OK;
+    int32_t i = 0;
+    while (cur < rounds) {
+        if ((rc = round(i++, rowA, rowB)) != CCB_OK || cur >= rounds) break;
+        if ((rc = round(i++, rowB, rowA)) != CCB_OK) break;
+    }
+    if (rc == CCB_OK) {
+        // the last three rounds' reads, sums and stores, with no barrier left
+        for (int d = 0; d < 3; ++d, ++i) {
+            if ((i & 1) == 0) work(i, rowA, rowB);
+            else work(i, rowB, rowA);
+            ccb_wait_memory();
+            __syncthreads();
+            shift();
+        }
+    }
+    return rc;
+}
 
 }  // namespace
 
@@ -181,26 +320,21 @@ __global__ __launch_bounds__(1024) void ccb_k_slot_rounds(int32_t* ws, uint32_t*
             if (leader()) out[(size_t)r * nGrid + w] = s;
         }
     } else {
-        if (leader() && rounds > 0) ccb_store_coherent(slots + w, witness(seed, 0u, (uint32_t)w));
-        ccb_wait_memory();
-        uint32_t* pending = nullptr;  // out entry of the round whose partials are in LDS
-        for (int32_t r = 0; r < rounds; ++r) {
-            rc = ccb_barrier<K, V, false>(ws, nMembers, w, maxPoll, err,
-                                          FinishRound{partial, nWave, pending});
-            if (rc != CCB_OK) break;
-            const uint32_t* row = slots + (size_t)(r % kRing) * nGrid;
-            if (leader() && r + 1 < rounds)
-                ccb_store_coherent(slots + (size_t)((r + 1) % kRing) * nGrid + w,
-                                   witness(seed, (uint32_t)(r + 1), (uint32_t)w));
-            uint32_t s = 0;
-            for (int32_t i = threadIdx.x; i < nMembers; i += blockDim.x) s += ccb_load_coherent(row + i);
-            s = wave_sum(s);
-            ccb_wait_memory();  // the witness store above is complete
-            if ((threadIdx.x % kWave) == 0) partial[threadIdx.x / kWave] = s;
-            pending = out + (size_t)r * nGrid + w;
-        }
-        __syncthreads();
-        if (leader() && rc == CCB_OK) FinishRound{partial, nWave, pending}();
+        struct Whole {
+            int32_t* ws;
+            uint32_t* slots;
+            int32_t nGrid, nMembers, w;
+            __device__ int32_t first() const { return 0; }
+            __device__ int32_t next(int32_t q) const { return q + 1; }
+            __device__ int32_t* counter(int32_t) const { return ws; }
+            __device__ int32_t n(int32_t) const { return nMembers; }
+            __device__ int32_t member(int32_t) const { return w; }
+            __device__ const uint32_t* row(int32_t q) const { return slots + (size_t)(q % kRing) * nGrid; }
+            __device__ int32_t len(int32_t) const { return nMembers; }
+            __device__ uint32_t* slot(int32_t q) const { return slots + (size_t)(q % kRing) * nGrid + w; }
+        };
+        rc = witness_pipeline<K, V>(Whole{ws, slots, nGrid, nMembers, w}, rounds, out, nGrid, w,
+                                    seed, maxPoll, err);
     }
     if (wgStatus != nullptr && leader()) wgStatus[w] = rc == CCB_OK ? 1 : 3;
 }
@@ -211,9 +345,10 @@ __global__ __launch_bounds__(1024) void ccb_k_slot_rounds(int32_t* ws, uint32_t*
 // members enter it in the same order the same number of times (SYNCALL
 // guide §6.2).  Slots are stored group-major (even ids first) so a group's
 // slots are contiguous; the sum does not depend on the layout.  With
-// CCB_VIS_ORDER the rounds are pipelined as in the witness rounds above: a
-// member stores the witness of the next round it belongs to right after
-// passing a barrier.
+// CCB_VIS_ORDER the rounds are pipelined two deep as in the witness rounds
+// above, counted in the member's own rounds: after passing the barrier of
+// its round m_i a member reads row m_i, stores the witness of m_{i+2} and
+// sums row m_{i-1} before arriving at m_{i+1}.
 // ---------------------------------------------------------------------------
 template <int K, ccbVisibility V>
 __global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32_t* slots,
@@ -248,37 +383,30 @@ __global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32
             if (leader()) out[(size_t)r * nGrid + w] = s;
         }
     } else {
-        int32_t r = 0;
-        while (r < rounds && !member_of(r)) ++r;
-        if (leader() && r < rounds)
-            ccb_store_coherent(slots + (size_t)(r % kRing) * nGrid + pos,
-                               witness(seed, (uint32_t)r, (uint32_t)w));
-        ccb_wait_memory();
-        uint32_t* pending = nullptr;
-        for (; r < rounds;) {
-            const int32_t kind = r % 3;
-            const int32_t n = kind == 2 ? nGrid : half;
-            const int32_t member = kind == 2 ? w : (w >> 1);
-            rc = ccb_barrier<K, V, false>(ws + kind * CCB_STRIPES * CCB_LINE_WORDS, n, member,
-                                          maxPoll, err, FinishRound{partial, nWave, pending});
-            if (rc != CCB_OK) break;
-            int32_t next = r + 1;
-            while (next < rounds && !member_of(next)) ++next;
-            if (leader() && next < rounds)
-                ccb_store_coherent(slots + (size_t)(next % kRing) * nGrid + pos,
-                                   witness(seed, (uint32_t)next, (uint32_t)w));
-            const uint32_t* row = slots + (size_t)(r % kRing) * nGrid;
-            const int32_t first = kind == 2 ? 0 : kind * half;
-            uint32_t s = 0;
-            for (int32_t i = threadIdx.x; i < n; i += blockDim.x) s += ccb_load_coherent(row + first + i);
-            s = wave_sum(s);
-            ccb_wait_memory();
-            if ((threadIdx.x % kWave) == 0) partial[threadIdx.x / kWave] = s;
-            pending = out + (size_t)r * nGrid + w;
-            r = next;
-        }
-        __syncthreads();
-        if (leader() && rc == CCB_OK) FinishRound{partial, nWave, pending}();
+        struct Grouped {
+            int32_t* ws;
+            uint32_t* slots;
+            int32_t nGrid, half, w, parity, pos, rounds;
+            __device__ bool member_of(int32_t q) const { return (q % 3) == 2 || (q % 3) == parity; }
+            __device__ int32_t next(int32_t q) const
+            {
+                ++q;
+                while (q < rounds && !member_of(q)) ++q;
+                return q;
+            }
+            __device__ int32_t first() const { return member_of(0) ? 0 : next(0); }
+            __device__ int32_t* counter(int32_t q) const { return ws + (q % 3) * CCB_STRIPES * CCB_LINE_WORDS; }
+            __device__ int32_t n(int32_t q) const { return (q % 3) == 2 ? nGrid : half; }
+            __device__ int32_t member(int32_t q) const { return (q % 3) == 2 ? w : (w >> 1); }
+            __device__ const uint32_t* row(int32_t q) const
+            {
+                return slots + (size_t)(q % kRing) * nGrid + ((q % 3) == 2 ? 0 : (q % 3) * half);
+            }
+            __device__ int32_t len(int32_t q) const { return n(q); }
+            __device__ uint32_t* slot(int32_t q) const { return slots + (size_t)(q % kRing) * nGrid + pos; }
+        };
+        rc = witness_pipeline<K, V>(Grouped{ws, slots, nGrid, half, w, parity, pos, rounds}, rounds,
+                                    out, nGrid, w, seed, maxPoll, err);
     }
     if (wgStatus != nullptr && leader()) wgStatus[w] = rc == CCB_OK ? 1 : 3;
 }

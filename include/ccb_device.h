@@ -108,7 +108,77 @@ struct ccb_no_overlap {
     __device__ __forceinline__ void operator()() const {}
 };
 
-/* The barrier proper.
+/* Split-phase form of the barrier, for callers that order their own
+ * workgroup around it (one workgroup barrier per round where back-to-back
+ * rounds leave nothing to do between them).
+ *
+ * ccb_arrive: called by ONE lane of wave 0 (linear thread 0) once every
+ * access of the workgroup that the round must publish is complete and
+ * ordered before it (for CCB_VIS_ORDER: each thread waited for its own
+ * accesses, then a workgroup barrier).  Issues the arrival -- the pages'
+ * atomic add of one that returns the old value -- on stripe member mod K
+ * and returns that old value; nothing waits for it here, so the caller may
+ * issue more memory operations while the arrival is in flight.
+ *
+ * ccb_await: called by every lane of wave 0 with lane 0's `before`.  Derives
+ * the round from it, epoch = before / n_s + 1 with n_s the stripe's member
+ * count, and polls until every stripe l in use holds at least epoch * n_l
+ * arrivals (for K = 1: the counter reaches (before / n + 1) * n, the
+ * pages' target).  At most maxPoll polls; past that it stores
+ * CCB_ERR_DEADLOCK in the error word and returns it.  Every 64th poll it
+ * also reads the error word and returns its value when another member has
+ * failed.  For CCB_VIS_FULL it ends with an agent-scope acquire fence.  The
+ * caller then releases the rest of its workgroup (a workgroup barrier). */
+template <int K, ccbVisibility kVis>
+__device__ __forceinline__ int32_t ccb_arrive(int32_t* ctr, int32_t member)
+{
+    static_assert(K >= 1 && K <= 64, "stripes are polled by one wave");
+    // release: the workgroup's earlier global stores become visible at agent
+    // scope before the arrival can be observed
+    if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    return __hip_atomic_fetch_add(ctr + (member % K) * CCB_LINE_WORDS, 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int K, ccbVisibility kVis>
+__device__ __forceinline__ int32_t ccb_await(const int32_t* ctr, int32_t n, int32_t member,
+                                             int32_t before, uint32_t maxPoll, int32_t* err)
+{
+    const int lane = (int)__lane_id();
+    const int32_t ks = n < K ? n : K;  // stripes in use
+    const int32_t s = member % K;
+    const int32_t epoch = __shfl(before / ((n - s + K - 1) / K) + 1, 0, 64);
+    // stripe `lane` is complete for this round at epoch * n_lane arrivals;
+    // lanes past the stripes in use re-read stripe 0 and always agree
+    const int32_t need = lane < ks ? epoch * ((n - lane + K - 1) / K) : INT32_MIN;
+    int32_t* mine = const_cast<int32_t*>(ctr) + (lane < ks ? lane : 0) * CCB_LINE_WORDS;
+    int32_t rc = CCB_OK;
+    uint32_t polls = 0;
+    for (;;) {
+        const int32_t v = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__all(v >= need)) break;
+        if (++polls >= maxPoll) {
+            if (lane == 0)
+                __hip_atomic_store(err, (int32_t)CCB_ERR_DEADLOCK, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            rc = CCB_ERR_DEADLOCK;
+            break;
+        }
+        if ((polls % CCB_ERR_CHECK_EVERY) == 0) {
+            const int32_t e = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (e != CCB_OK) {
+                rc = e;
+                break;
+            }
+        }
+        if (CCB_POLL_SLEEP > 0) __builtin_amdgcn_s_sleep(CCB_POLL_SLEEP);
+    }
+    // acquire: loads after the barrier see every member's released stores
+    if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return rc;
+}
+
+/* The barrier proper (both phases with the workgroup barriers around them).
  *   ctr      K stripe lines (stripe s: int32 at ctr[s * CCB_LINE_WORDS])
  *   n        participant count (> 0)
  *   member   this workgroup's index among the participants, 0..n-1
@@ -127,56 +197,18 @@ __device__ __forceinline__ int32_t ccb_barrier(int32_t* ctr, int32_t n, int32_t 
                                                uint32_t maxPoll, int32_t* err,
                                                Overlap overlap = Overlap())
 {
-    static_assert(K >= 1 && K <= 64, "stripes are polled by one wave");
     __shared__ int32_t ccb_result;
     if (kVis == CCB_VIS_ORDER && kPreWait) ccb_wait_memory();  // this thread's accesses are done
     __syncthreads();
     const uint32_t tid = threadIdx.x + blockDim.x * (threadIdx.y + blockDim.y * threadIdx.z);
     if (tid < 64) {  // wave 0
-        const int lane = (int)tid;
-        const int32_t ks = n < K ? n : K;  // stripes in use
-        int32_t epoch = 0;
-        if (lane == 0) {
-            // release: the workgroup's earlier global stores become visible at
-            // agent scope before the arrival can be observed
-            if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            const int32_t s = member % K;
-            const int32_t ns = (n - s + K - 1) / K;
-            const int32_t before = __hip_atomic_fetch_add(ctr + s * CCB_LINE_WORDS, 1,
-                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int32_t before = 0;
+        if (tid == 0) {
+            before = ccb_arrive<K, kVis>(ctr, member);
             overlap();
-            epoch = before / ns + 1;
         }
-        epoch = __shfl(epoch, 0, 64);
-        // stripe `lane` is complete for this round at epoch * n_lane arrivals
-        const int32_t need = lane < ks ? epoch * ((n - lane + K - 1) / K) : 0;
-        int32_t* mine = ctr + (lane < ks ? lane : 0) * CCB_LINE_WORDS;
-        int32_t rc = CCB_OK;
-        uint32_t polls = 0;
-        for (;;) {
-            const int32_t v = lane < ks ? __hip_atomic_load(mine, __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_AGENT)
-                                        : 0;
-            if (__all(v >= need)) break;
-            if (++polls >= maxPoll) {
-                if (lane == 0)
-                    __hip_atomic_store(err, (int32_t)CCB_ERR_DEADLOCK, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                rc = CCB_ERR_DEADLOCK;
-                break;
-            }
-            if ((polls % CCB_ERR_CHECK_EVERY) == 0) {
-                const int32_t e = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (e != CCB_OK) {
-                    rc = CCB_ERR_DEADLOCK;
-                    break;
-                }
-            }
-            if (CCB_POLL_SLEEP > 0) __builtin_amdgcn_s_sleep(CCB_POLL_SLEEP);
-        }
-        // acquire: loads after the barrier see every member's released stores
-        if (kVis == CCB_VIS_FULL && lane == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        if (lane == 0) ccb_result = rc;
+        const int32_t rc = ccb_await<K, kVis>(ctr, n, member, before, maxPoll, err);
+        if (tid == 0) ccb_result = rc;
     }
     __syncthreads();
     return ccb_result;

@@ -76,15 +76,22 @@ class Result:
 
 def _programs(rounds: Sequence[RoundSpec], n_participants: int,
               skip: Sequence[Tuple[int, int]] = (),
-              early_write: bool = False) -> List[List[Tuple[int, int]]]:
+              early_write: bool = False, write_lead: int = 0,
+              read_lag: int = 0) -> List[List[Tuple[int, int]]]:
     """Per participant: the flat list of (step kind, round) it executes.
 
     In the plain schedule every member round is WRITE, ARRIVE, POLL, READ.
-    With early_write the member writes the witness of its NEXT member round
-    right after passing a barrier, before reading the current round (the
-    pipelined order the GPU kernels use); its first round's witness is
-    written before its first barrier.  A skipped barrier drops that round's
-    ARRIVE and POLL."""
+    A pipelined schedule (write_lead = a >= 1) counts in the participant's
+    own member rounds m_0, m_1, ...: the witnesses of m_0 .. m_{a-1} are
+    written before the first barrier, the witness of m_{i+a} right after
+    passing the barrier of m_i, and the read of m_i may still be in flight
+    until the participant arrives at m_{i+b} (b = read_lag >= 1).  The READ
+    step sits at that latest point: a slot that still holds round m_i there
+    held it since the barrier of m_i (a slot is only ever overwritten by a
+    later round), so this placement covers every earlier one.  early_write
+    is a = b = 1.  A skipped barrier drops that round's ARRIVE and POLL."""
+    if early_write:
+        write_lead, read_lag = max(write_lead, 1), max(read_lag, 1)
     skipped = set(skip)
     member_rounds: List[List[int]] = [[] for _ in range(n_participants)]
     for r, spec in enumerate(rounds):
@@ -94,17 +101,25 @@ def _programs(rounds: Sequence[RoundSpec], n_participants: int,
     for p in range(n_participants):
         mine = member_rounds[p]
         steps: List[Tuple[int, int]] = []
-        if early_write and mine:
-            steps.append((WRITE, mine[0]))
-        for i, r in enumerate(mine):
-            if not early_write:
+        if write_lead <= 0:
+            for r in mine:
                 steps.append((WRITE, r))
-            if (p, r) not in skipped:
-                steps.append((ARRIVE, r))
-                steps.append((POLL, r))
-            if early_write and i + 1 < len(mine):
-                steps.append((WRITE, mine[i + 1]))
-            steps.append((READ, r))
+                if (p, r) not in skipped:
+                    steps.append((ARRIVE, r))
+                    steps.append((POLL, r))
+                steps.append((READ, r))
+        else:
+            a, b = write_lead, max(read_lag, 1)
+            steps.extend((WRITE, mine[j]) for j in range(min(a, len(mine))))
+            for i, r in enumerate(mine):
+                if i - b >= 0:
+                    steps.append((READ, mine[i - b]))
+                if (p, r) not in skipped:
+                    steps.append((ARRIVE, r))
+                    steps.append((POLL, r))
+                if i + a < len(mine):
+                    steps.append((WRITE, mine[i + a]))
+            steps.extend((READ, mine[j]) for j in range(max(0, len(mine) - b), len(mine)))
         progs.append(steps)
     return progs
 
@@ -114,6 +129,7 @@ def enumerate_schedules(rounds: Sequence[RoundSpec], n_participants: int, *,
                         counter_init: Optional[Sequence[int]] = None,
                         skip: Sequence[Tuple[int, int]] = (),
                         early_write: bool = False, stripes: int = 1,
+                        write_lead: int = 0, read_lag: int = 0,
                         max_states: int = 5_000_000) -> Result:
     """Explore every interleaving of the participants' steps.
 
@@ -123,7 +139,8 @@ def enumerate_schedules(rounds: Sequence[RoundSpec], n_participants: int, *,
     counter_init  starting value of each counter (default all zero)
     skip          (participant, round) pairs whose barrier is left out
                   (the participant still writes and reads)
-    early_write   use the pipelined step order (see _programs)
+    early_write   the pipelined step order with a = b = 1 (see _programs)
+    write_lead    a, read_lag b: a pipelined step order (see _programs)
     stripes       K: each counter is split into K stripes; the member with
                   index m in its round's member list arrives on stripe m mod K,
                   whose member count is n_s = ceil((N - s) / K), derives its
@@ -140,7 +157,7 @@ def enumerate_schedules(rounds: Sequence[RoundSpec], n_participants: int, *,
         ctr0 = tuple(v if s == 0 else 0 for v in counter_init for s in range(K))
     else:
         ctr0 = (0,) * (n_counters * K)
-    progs = _programs(rounds, n_participants, skip, early_write)
+    progs = _programs(rounds, n_participants, skip, early_write, write_lead, read_lag)
     res = Result()
 
     # state = (pcs, counters, targets, slots)

@@ -88,6 +88,9 @@ def test_constants_match_pages(ccb):
     text = open(os.path.join(INCLUDE, "ccb.h")).read()
     m = re.search(r"#define CCB_SOFT_MAX_POLL (\d+)u", text)
     assert int(m.group(1)) == consts["soft_max_poll_iterations"] == ccb.CCB_SOFT_MAX_POLL
+    for name in ("CCB_STRIPES", "CCB_SLOT_ROWS", "CCB_LINE_BYTES"):
+        m = re.search(r"#define %s (\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(ccb, name), name
     assert ccb.ccb_syncall_workspace_bytes(1) == (ccb.CCB_STRIPES + 1) * 128
     assert ccb.ccb_syncall_workspace_bytes(3) == (3 * ccb.CCB_STRIPES + 1) * 128
     # 2^26 elements in chunks of 1024, 1024 workgroups: 64 chunks each

@@ -65,6 +65,9 @@ def _oracle_grouped(seed, rounds, n_grid):
     (3, 50, 1, 64, 0, 0),           # single participant
     (5, 0, 16, 64, 0, 0),           # zero rounds
     (6, 200, 100, 64, 67, 0),       # stripes with 2 and 3 members
+    (8, 91, 300, 64, 0, 0),         # more members than 4 slots per thread
+    (9, 2, 5, 64, 0, 0),            # two rounds: the pipeline's prologue and drain only
+    (10, 1, 5, 64, 0, 0),           # one round
 ])
 def test_slot_rounds_small(wl, seed, rounds, n_grid, threads, used, wpc, mode):
     _say(f"slot_rounds mode={mode} seed={seed} rounds={rounds} grid={n_grid}x{threads} used={used}")
@@ -95,7 +98,9 @@ def test_slot_rounds_grid_full(wl, used, mode):
 
 @pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
 @pytest.mark.parametrize("seed,rounds,n_grid,threads", [(4, 60, 6, 64), (9, 301, 34, 192),
-                                                        (2, 150, 130, 64)])
+                                                        (2, 150, 130, 64), (3, 77, 300, 64),
+                                                        (5, 1, 4, 64), (6, 2, 4, 64),
+                                                        (7, 4, 2, 64)])
 def test_grouped_small(wl, seed, rounds, n_grid, threads, mode):
     _say(f"grouped mode={mode} seed={seed} rounds={rounds} grid={n_grid}x{threads}")
     res = wl.grouped_rounds(seed, rounds, n_grid, threads, mode=mode)

@@ -298,3 +298,46 @@ def test_enumerator_early_write_ring_depths(k):
 def test_enumerator_early_write_grouped_longer():
     res = en.enumerate_schedules(en.grouped(4, 9), 4, stripes=2, early_write=True, ring_depth=4)
     assert not res.deadlock and res.violations == [] and res.final_counters == {(6, 6, 12)}
+
+
+# The two-deep pipeline of the ordered witness kernels: a member writes the
+# witness of its own round i + 2 right after passing round i's barrier, and
+# may still be reading round i's row until it arrives at round i + 2.  A ring
+# of D rows is safe exactly when the writer cannot reach a row again while a
+# reader is still on it; the brute force fixes the smallest D for each
+# pattern (the kernels use six rows for both).
+
+@pytest.mark.parametrize("k", [1, 2])
+def test_enumerator_two_deep_pipeline_whole_grid(k):
+    for p, r in ((3, 4), (4, 6)):
+        res = en.enumerate_schedules(en.whole_grid(p, r), p, stripes=k, write_lead=2, read_lag=2,
+                                     ring_depth=4)
+        assert not res.deadlock and res.violations == [] and res.final_counters == {(p * r,)}
+        assert en.enumerate_schedules(en.whole_grid(p, r), p, stripes=k, write_lead=2,
+                                      read_lag=2, ring_depth=3).violations != []
+    res = en.enumerate_schedules(en.whole_grid(3, 4, used_cores=2, n_members=2), 3, stripes=k,
+                                 write_lead=2, read_lag=2, ring_depth=4)
+    assert not res.deadlock and res.violations == [] and res.final_counters == {(8,)}
+
+
+@pytest.mark.parametrize("k", [1, 2])
+def test_enumerator_two_deep_pipeline_grouped(k):
+    for p, r in ((4, 9), (4, 12), (5, 9)):
+        g = en.grouped(p, r)
+        res = en.enumerate_schedules(g, p, stripes=k, write_lead=2, read_lag=2, ring_depth=6)
+        assert not res.deadlock and res.violations == []
+        assert res.final_counters == {en.expected_final_counters(g)}
+    g = en.grouped(4, 12)
+    assert en.enumerate_schedules(g, 4, stripes=k, write_lead=2, read_lag=2,
+                                  ring_depth=5).violations != []
+
+
+def test_enumerator_lead_plus_lag_bound():
+    # whole grid: safe exactly when write lead + read lag <= D
+    for a in (1, 2, 3):
+        for b in (1, 2, 3):
+            for d in (a + b - 1, a + b):
+                # enough rounds for the writer to come back to the same row
+                res = en.enumerate_schedules(en.whole_grid(3, d + 2), 3, write_lead=a,
+                                             read_lag=b, ring_depth=d)
+                assert (res.violations == []) == (d >= a + b), (a, b, d)
