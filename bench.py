@@ -126,7 +126,7 @@ class Bench:
         cfg = self.inputs.WITNESS_GRID
         n_grid, threads, rounds = cfg["n_wg"], cfg["threads"], cfg["rounds"]
         ws, stream, mode = self.ws, self.stream, self.mode
-        slots = torch.zeros(ccb.CCB_SLOT_ROWS * n_grid, dtype=torch.int32, device=self.dev)
+        slots = torch.zeros(ccb.CCB_SLOT_ROWS * ccb.CCB_SLOT_WORDS * n_grid, dtype=torch.int32, device=self.dev)
         out = torch.zeros((rounds, n_grid), dtype=torch.int32, device=self.dev)
 
         def step():
@@ -219,7 +219,7 @@ class Bench:
         torch, ccb, ws, stream = self.torch, self.ccb, self.ws, self.stream
         g = self.inputs.GROUPED
         gout = torch.zeros((g["rounds"], g["n_wg"]), dtype=torch.int32, device=self.dev)
-        gslots = torch.zeros(ccb.CCB_SLOT_ROWS * g["n_wg"], dtype=torch.int32, device=self.dev)
+        gslots = torch.zeros(ccb.CCB_SLOT_ROWS * ccb.CCB_SLOT_WORDS * g["n_wg"], dtype=torch.int32, device=self.dev)
 
         def run():
             ccb.check(ccb.ccb_syncall_workspace_reset(ws, 3, stream), "reset")

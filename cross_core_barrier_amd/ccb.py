@@ -43,6 +43,7 @@ CCB_SOFT_MAX_POLL = 1_000_000
 CCB_LINE_BYTES = 128
 CCB_STRIPES = 64
 CCB_SLOT_ROWS = 6
+CCB_SLOT_WORDS = 4
 CCB_CNT_NOTIFY_POOL = 1024
 
 CCB_BARRIER_STRIPED, CCB_BARRIER_FLAT = 0, 1

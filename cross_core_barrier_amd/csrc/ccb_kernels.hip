@@ -22,6 +22,7 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kRing = CCB_SLOT_ROWS;  // witness slot rows reused round-robin
+constexpr int kSlot = CCB_SLOT_WORDS;  // words from one slot to the next
 
 __device__ __forceinline__ bool leader() { return threadIdx.x == 0; }
 
@@ -148,7 +149,11 @@ __global__ __launch_bounds__(1024) void ccb_k_barrier_only(int32_t* ws, uint32_t
 // its own and a row may be read until the member arrives two rounds after
 // it; the brute-force enumerator shows that this needs D >= 4 slot rows
 // for the whole grid and D >= 6 for the grouped pattern below, and
-// D = CCB_SLOT_ROWS = 6 is used for both.  The member's last wave does the
+// D = CCB_SLOT_ROWS = 6 is used for both.  Slots sit CCB_SLOT_WORDS = 4
+// words apart: with packed slots all members' stores of a round land on a
+// few lines, whose partial-line writes are merged one after another, and a
+// slot store then outlasts the barrier; four words apart (eight writers per
+// line) it does not.  The member's last wave does the
 // witness and output stores, so wave 0's poll does not wait for them.
 // ---------------------------------------------------------------------------
 namespace {
@@ -179,11 +184,12 @@ struct RowRead {
             const int32_t i = (int32_t)threadIdx.x + j * (int32_t)blockDim.x;
             // wave-uniform test; lanes past the end reload slot 0 and are
             // left out of the sum
-            if (j * (int32_t)blockDim.x < count) v[j] = ccb_load_coherent(row + (i < count ? i : 0));
+            if (j * (int32_t)blockDim.x < count)
+                v[j] = ccb_load_coherent(row + (size_t)(i < count ? i : 0) * kSlot);
         }
         tail = 0;
         for (int32_t i = threadIdx.x + kRowRegs * blockDim.x; i < count; i += blockDim.x)
-            tail += ccb_load_coherent(row + i);
+            tail += ccb_load_coherent(row + (size_t)i * kSlot);
     }
 
     // This thread's share of the row sum (mod 2^32).
@@ -310,12 +316,13 @@ __global__ __launch_bounds__(1024) void ccb_k_slot_rounds(int32_t* ws, uint32_t*
     int32_t rc = CCB_OK;
     if constexpr (V == CCB_VIS_FULL) {
         for (int32_t r = 0; r < rounds; ++r) {
-            uint32_t* row = slots + (size_t)(r % kRing) * nGrid;
-            if (leader()) shared_store<V>(row + w, witness(seed, (uint32_t)r, (uint32_t)w));
+            uint32_t* row = slots + (size_t)(r % kRing) * nGrid * kSlot;
+            if (leader()) shared_store<V>(row + (size_t)w * kSlot, witness(seed, (uint32_t)r, (uint32_t)w));
             rc = ccb_barrier<K, V>(ws, nMembers, w, maxPoll, err);
             if (rc != CCB_OK) break;
             uint32_t s = 0;
-            for (int32_t i = threadIdx.x; i < nMembers; i += blockDim.x) s += shared_load<V>(row + i);
+            for (int32_t i = threadIdx.x; i < nMembers; i += blockDim.x)
+                s += shared_load<V>(row + (size_t)i * kSlot);
             s = block_sum(s, partial);
             if (leader()) out[(size_t)r * nGrid + w] = s;
         }
@@ -329,9 +336,12 @@ __global__ __launch_bounds__(1024) void ccb_k_slot_rounds(int32_t* ws, uint32_t*
             __device__ int32_t* counter(int32_t) const { return ws; }
             __device__ int32_t n(int32_t) const { return nMembers; }
             __device__ int32_t member(int32_t) const { return w; }
-            __device__ const uint32_t* row(int32_t q) const { return slots + (size_t)(q % kRing) * nGrid; }
+            __device__ const uint32_t* row(int32_t q) const { return slots + (size_t)(q % kRing) * nGrid * kSlot; }
             __device__ int32_t len(int32_t) const { return nMembers; }
-            __device__ uint32_t* slot(int32_t q) const { return slots + (size_t)(q % kRing) * nGrid + w; }
+            __device__ uint32_t* slot(int32_t q) const
+            {
+                return slots + ((size_t)(q % kRing) * nGrid + w) * kSlot;
+            }
         };
         rc = witness_pipeline<K, V>(Whole{ws, slots, nGrid, nMembers, w}, rounds, out, nGrid, w,
                                     seed, maxPoll, err);
@@ -370,15 +380,16 @@ __global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32
         for (int32_t r = 0; r < rounds; ++r) {
             const int32_t kind = r % 3;
             if (!member_of(r)) continue;
-            uint32_t* row = slots + (size_t)(r % kRing) * nGrid;
-            if (leader()) shared_store<V>(row + pos, witness(seed, (uint32_t)r, (uint32_t)w));
+            uint32_t* row = slots + (size_t)(r % kRing) * nGrid * kSlot;
+            if (leader()) shared_store<V>(row + (size_t)pos * kSlot, witness(seed, (uint32_t)r, (uint32_t)w));
             const int32_t n = kind == 2 ? nGrid : half;
             const int32_t member = kind == 2 ? w : (w >> 1);
             rc = ccb_barrier<K, V>(ws + kind * CCB_STRIPES * CCB_LINE_WORDS, n, member, maxPoll, err);
             if (rc != CCB_OK) break;
             const int32_t first = kind == 2 ? 0 : kind * half;
             uint32_t s = 0;
-            for (int32_t i = threadIdx.x; i < n; i += blockDim.x) s += shared_load<V>(row + first + i);
+            for (int32_t i = threadIdx.x; i < n; i += blockDim.x)
+                s += shared_load<V>(row + (size_t)(first + i) * kSlot);
             s = block_sum(s, partial);
             if (leader()) out[(size_t)r * nGrid + w] = s;
         }
@@ -400,10 +411,13 @@ __global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32
             __device__ int32_t member(int32_t q) const { return (q % 3) == 2 ? w : (w >> 1); }
             __device__ const uint32_t* row(int32_t q) const
             {
-                return slots + (size_t)(q % kRing) * nGrid + ((q % 3) == 2 ? 0 : (q % 3) * half);
+                return slots + ((size_t)(q % kRing) * nGrid + ((q % 3) == 2 ? 0 : (q % 3) * half)) * kSlot;
             }
             __device__ int32_t len(int32_t q) const { return n(q); }
-            __device__ uint32_t* slot(int32_t q) const { return slots + (size_t)(q % kRing) * nGrid + pos; }
+            __device__ uint32_t* slot(int32_t q) const
+            {
+                return slots + ((size_t)(q % kRing) * nGrid + pos) * kSlot;
+            }
         };
         rc = witness_pipeline<K, V>(Grouped{ws, slots, nGrid, half, w, parity, pos, rounds}, rounds,
                                     out, nGrid, w, seed, maxPoll, err);

@@ -43,7 +43,7 @@ def slot_rounds(seed: int, rounds: int, n_grid: int, threads: int, used_cores: i
                 mode: int = 0) -> RoundsResult:
     d = _dev(device)
     ws = workspace(1, d)
-    slots = torch.zeros(ccb.CCB_SLOT_ROWS * n_grid, dtype=torch.int32, device=d)
+    slots = torch.zeros(ccb.CCB_SLOT_ROWS * ccb.CCB_SLOT_WORDS * n_grid, dtype=torch.int32, device=d)
     if out is None:
         out = torch.zeros((rounds, n_grid), dtype=torch.int32, device=d)
     wg = torch.zeros(n_grid, dtype=torch.int32, device=d)
@@ -61,7 +61,7 @@ def grouped_rounds(seed: int, rounds: int, n_grid: int, threads: int, wgs_per_cu
                    max_poll: int = 0, stream=None, device=None, mode: int = 0) -> RoundsResult:
     d = _dev(device)
     ws = workspace(3, d)
-    slots = torch.zeros(ccb.CCB_SLOT_ROWS * n_grid, dtype=torch.int32, device=d)
+    slots = torch.zeros(ccb.CCB_SLOT_ROWS * ccb.CCB_SLOT_WORDS * n_grid, dtype=torch.int32, device=d)
     out = torch.zeros((rounds, n_grid), dtype=torch.int32, device=d)
     wg = torch.zeros(n_grid, dtype=torch.int32, device=d)
     st = ccb.ccb_run_grouped_rounds(ws, slots, out, wg, seed, rounds, n_grid, threads, wgs_per_cu,

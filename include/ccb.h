@@ -183,9 +183,12 @@ CCB_API ccbStatus ccb_run_barrier_only(int32_t* ws, uint32_t* placement, int32_t
                                        int32_t usedCores, int32_t wgsPerCu, uint32_t maxPoll,
                                        int32_t mode, ccbStream stream);
 
-/* Rows of the witness slot ring of the two witness workloads: a slots
- * buffer holds CCB_SLOT_ROWS * nGrid uint32. */
+/* The witness slots of the two witness workloads: a ring of CCB_SLOT_ROWS
+ * rows of nGrid slots, one slot every CCB_SLOT_WORDS uint32.  Slot p of
+ * ring row q is word ((q mod CCB_SLOT_ROWS) * nGrid + p) * CCB_SLOT_WORDS;
+ * a slots buffer holds CCB_SLOT_ROWS * nGrid * CCB_SLOT_WORDS uint32. */
 #define CCB_SLOT_ROWS 6
+#define CCB_SLOT_WORDS 4
 
 /* Witness rounds on one counter ([SYNCALL] §6.1's pattern of slots written
  * before a barrier and read after it).  For r = 0..rounds-1 every member w
@@ -196,8 +199,8 @@ CCB_API ccbStatus ccb_run_barrier_only(int32_t* ws, uint32_t* placement, int32_t
  * usedCores as in ccb_run_barrier_only; non-members write no slot and no
  * output.
  *   ws        device, workspace of 1 barrier (zeroed)
- *   slots     device, CCB_SLOT_ROWS * nGrid uint32 scratch (contents on
- *             entry ignored)
+ *   slots     device, CCB_SLOT_ROWS * nGrid * CCB_SLOT_WORDS uint32
+ *             scratch (contents on entry ignored)
  *   out       device, rounds * nGrid uint32; entries of non-members untouched
  *   wgStatus  device, nGrid int32 (see ccb_run_barrier_only), may be NULL
  * Errors: as ccb_run_barrier_only, plus NULL_POINTER for slots/out (which
@@ -217,7 +220,7 @@ CCB_API ccbStatus ccb_run_slot_rounds(int32_t* ws, uint32_t* slots, uint32_t* ou
  * Every member enters each counter's barriers in the same order the same
  * number of times ([SYNCALL] §6.2).
  *   ws     device, workspace of 3 barriers (zeroed)
- *   slots  device, CCB_SLOT_ROWS * nGrid uint32 scratch
+ *   slots  device, CCB_SLOT_ROWS * nGrid * CCB_SLOT_WORDS uint32 scratch
  *   out    device, rounds * nGrid uint32
  * Errors: as ccb_run_slot_rounds; nGrid must be even. */
 CCB_API ccbStatus ccb_run_grouped_rounds(int32_t* ws, uint32_t* slots, uint32_t* out,

@@ -88,7 +88,7 @@ def test_constants_match_pages(ccb):
     text = open(os.path.join(INCLUDE, "ccb.h")).read()
     m = re.search(r"#define CCB_SOFT_MAX_POLL (\d+)u", text)
     assert int(m.group(1)) == consts["soft_max_poll_iterations"] == ccb.CCB_SOFT_MAX_POLL
-    for name in ("CCB_STRIPES", "CCB_SLOT_ROWS", "CCB_LINE_BYTES"):
+    for name in ("CCB_STRIPES", "CCB_SLOT_ROWS", "CCB_SLOT_WORDS", "CCB_LINE_BYTES"):
         m = re.search(r"#define %s (\d+)" % name, text)
         assert m and int(m.group(1)) == getattr(ccb, name), name
     assert ccb.ccb_syncall_workspace_bytes(1) == (ccb.CCB_STRIPES + 1) * 128
