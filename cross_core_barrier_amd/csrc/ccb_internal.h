@@ -17,7 +17,8 @@ namespace ccb {
 #endif
 constexpr bool kStencilNT = CCB_STENCIL_NT_STORE != 0;      // non-temporal stores of the output
 constexpr bool kStencilNTLoad = CCB_STENCIL_NT_LOAD != 0;   // non-temporal loads of the input
-constexpr int kCntUnroll = 2;       // ops loaded ahead per thread in the batch engine
+constexpr int kCntUnroll = 4;       // ops loaded ahead per thread in the batch engine
+constexpr bool kCntNTLoad = true;   // non-temporal loads of the op stream (read once)
 
 enum class KernelId { BarrierOnly, SlotRounds, GroupedRounds, Stencil };
 

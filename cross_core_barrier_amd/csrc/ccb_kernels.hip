@@ -21,6 +21,7 @@
 namespace {
 
 constexpr int kWave = 64;
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 constexpr int kRing = CCB_SLOT_ROWS;  // witness slot rows reused round-robin
 constexpr int kSlot = CCB_SLOT_WORDS;  // words from one slot to the next
 
@@ -307,7 +308,6 @@ __global__ __launch_bounds__(1024) void ccb_k_slot_rounds(int32_t* ws, uint32_t*
     __shared__ uint32_t partial[1024 / kWave];
     const int32_t w = blockIdx.x;
     const int32_t nGrid = gridDim.x;
-    const int nWave = blockDim.x / kWave;
     if (w >= nMembers) {
         if (wgStatus != nullptr && leader()) wgStatus[w] = 2;
         return;
@@ -372,7 +372,6 @@ __global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32
     const int32_t half = nGrid / 2;
     const int32_t parity = w & 1;
     const int32_t pos = parity * half + (w >> 1);
-    const int nWave = blockDim.x / kWave;
     int32_t* err = ws + 3 * CCB_STRIPES * CCB_LINE_WORDS;
     int32_t rc = CCB_OK;
     auto member_of = [&](int32_t r) { return (r % 3) == 2 || (r % 3) == parity; };
@@ -827,8 +826,16 @@ __global__ __launch_bounds__(256) void ccb_k_cnt_batch4(const uint32_t* __restri
         uint4 v4[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            m4[u] = *reinterpret_cast<const uint32_t*>(meta + (int64_t)(k + u) * nCounters + c0);
-            v4[u] = *reinterpret_cast<const uint4*>(val + (int64_t)(k + u) * nCounters + c0);
+            const uint32_t* mp = reinterpret_cast<const uint32_t*>(meta + (int64_t)(k + u) * nCounters + c0);
+            const uint32_t* vp = val + (int64_t)(k + u) * nCounters + c0;
+            if constexpr (ccb::kCntNTLoad) {
+                m4[u] = __builtin_nontemporal_load(mp);
+                const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(vp));
+                v4[u] = make_uint4(t[0], t[1], t[2], t[3]);
+            } else {
+                m4[u] = *mp;
+                v4[u] = *reinterpret_cast<const uint4*>(vp);
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) apply(m4[u], v4[u]);
