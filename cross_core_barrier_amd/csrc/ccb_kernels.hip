@@ -1000,7 +1000,7 @@ __global__ void ccb_k_atomic_contended(int32_t* line, uint64_t* ticks, int32_t i
 
 // Streaming copy: every thread moves one 16-byte vector per step and the
 // whole grid advances through memory together (the access order that gets
-// the most out of HBM on this GPU), loads non-temporal.
+// the most out of HBM on this GPU), loads and stores non-temporal.
 __global__ __launch_bounds__(256) void ccb_k_copy(int4* __restrict__ dst,
                                                   const int4* __restrict__ src, int64_t n16)
 {
@@ -1008,7 +1008,7 @@ __global__ __launch_bounds__(256) void ccb_k_copy(int4* __restrict__ dst,
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
         const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + i));
-        dst[i] = make_int4(v.x, v.y, v.z, v.w);
+        __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(dst + i));
     }
 }
 

@@ -38,6 +38,10 @@ MODE_IDS = ["striped-order", "flat-order", "striped-full", "flat-full"]
     (1024 * 2000 + 5, 3, 1, 256),  # one workgroup, more chunks than the LDS staging holds
     (123457, 7, 37, 192),          # ragged everything, odd iteration count
     (4096, 0, 4, 64),              # zero iterations: result is the input
+    (256 * 100, 10, 2, 64),        # one wave per workgroup
+    (256 * 64 * 4, 7, 8, 256),     # all chunks full, several per workgroup
+    (1024 * 3, 4, 5, 256),         # workgroups without chunks
+    (1024 * 64, 2, 16, 1024),      # 1024-thread workgroups, two iterations
 ])
 def test_stencil_small(wl, n, iters, n_grid, threads, mode):
     _say(f"stencil mode={mode} n={n} iters={iters} grid={n_grid}x{threads}")
