@@ -231,6 +231,17 @@ __device__ __forceinline__ int32_t ccb_syncall_soft(int32_t* ws, int32_t usedCor
                                                   ws + CCB_STRIPES * CCB_LINE_WORDS);
 }
 
+/* ccb_syncall_soft with a caller-chosen poll bound instead of
+ * CCB_SOFT_MAX_POLL (a test hook: a small bound turns a deliberately
+ * broken round into a prompt CCB_ERR_DEADLOCK). */
+__device__ __forceinline__ int32_t ccb_syncall_soft_bounded(int32_t* ws, int32_t usedCores,
+                                                            uint32_t maxPoll)
+{
+    const int32_t n = usedCores != 0 ? usedCores : (int32_t)(gridDim.x * gridDim.y * gridDim.z);
+    return ccb_barrier<CCB_STRIPES, CCB_VIS_FULL>(ws, n, ccb_block_linear(), maxPoll,
+                                                  ws + CCB_STRIPES * CCB_LINE_WORDS);
+}
+
 /* The same barrier with the pages' arrival-only contract (CCB_VIS_ORDER). */
 __device__ __forceinline__ int32_t ccb_syncall_soft_ordered(int32_t* ws, int32_t usedCores)
 {

@@ -132,3 +132,17 @@ def test_validation_before_device_work(ccb):
     assert ccb.ccb_cnt_notify_batch(None, None, -1, 1, None, None, 1) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_cnt_notify_batch(None, None, 0, 1, None, None, 1) == ccb.CCB_OK
     assert ccb.ccb_cnt_notify_batch(None, None, 4, 1, 256, 256, 1) == ccb.CCB_ERR_NULL_POINTER
+
+
+def test_device_api_test_kernels_built():
+    """The device-API test kernels (tests/devapi) are built and export their
+    launcher; the header they include is the public in-kernel API."""
+    import ctypes
+    lib_path = os.path.join(os.path.dirname(__file__), "devapi", "libccb_devapi.so")
+    assert os.path.exists(lib_path), "run __graft_entry__.build()"
+    lib = ctypes.CDLL(lib_path)
+    assert hasattr(lib, "devapi_run")
+    text = open(os.path.join(INCLUDE, "ccb_device.h")).read()
+    for name in ("ccb_syncall_soft", "ccb_syncall_soft_ordered", "ccb_syncall_soft_flat",
+                 "ccb_syncall_soft_bounded", "ccb_arrive", "ccb_await", "ccb_barrier"):
+        assert name + "(" in text, name

@@ -1,0 +1,89 @@
+"""GPU parity of the in-kernel barrier API (include/ccb_device.h) used as a
+caller's own kernel would use it: ccb_syncall_soft / _ordered / _flat /
+_bounded inside the flag-slot pattern of the SYNCALL guide §6.1, on 2-D
+grids, with and without a usedCores subset.  The test kernels live in
+tests/devapi (built by __graft_entry__.build()); the expected sums come from
+the oracle's witness rounds."""
+
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+LIB = os.path.join(os.path.dirname(__file__), "devapi", "libccb_devapi.so")
+VARIANTS = {0: "soft", 1: "soft_ordered", 2: "soft_flat", 3: "soft_bounded"}
+
+
+def _say(msg):
+    print(f"[gpu case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def devapi():
+    if not os.path.exists(LIB):
+        raise RuntimeError(f"{LIB} is missing; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB)
+    V, I32, U32, U64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64
+    lib.devapi_run.restype = ctypes.c_int
+    lib.devapi_run.argtypes = [ctypes.c_int, V, V, V, V, U64, I32, I32, I32, I32, I32, U32, V]
+    return lib
+
+
+def _run(lib, variant, gx, gy, threads, used, rounds, seed, max_poll=0, preset=None):
+    from cross_core_barrier_amd import ccb, workloads
+    n_grid = gx * gy
+    ws = workloads.workspace(1)
+    if preset is not None:
+        ws[0] = preset
+    slots = torch.zeros(2 * n_grid, dtype=torch.int32, device="cuda")
+    out = torch.zeros(max(rounds, 1) * n_grid, dtype=torch.int32, device="cuda")
+    status = torch.zeros(n_grid, dtype=torch.int32, device="cuda")
+    rc = lib.devapi_run(variant, ws.data_ptr(), slots.data_ptr(), out.data_ptr(), status.data_ptr(),
+                        seed, rounds, gx, gy, threads, used, max_poll, None)
+    assert rc == 0, rc
+    torch.cuda.synchronize()
+    st, ctrs = ccb.ccb_syncall_status(ws, 1, None)
+    return st, ctrs, out.cpu().numpy().view(np.uint32).reshape(-1, n_grid)[:rounds], status.cpu().numpy()
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS), ids=list(VARIANTS.values()))
+@pytest.mark.parametrize("gx,gy,threads,used,rounds,seed", [
+    (8, 4, 64, 0, 60, 11),       # 2-D grid, whole grid
+    (5, 3, 128, 7, 41, 12),      # leading subset of a 2-D grid, idle workgroups
+    (16, 16, 256, 0, 30, 13),    # 256 workgroups, more than the stripes
+    (3, 1, 1024, 0, 25, 14),     # 1024-thread workgroups
+    (1, 1, 64, 0, 10, 15),       # a single participant
+])
+def test_device_api_witness_rounds(devapi, variant, gx, gy, threads, used, rounds, seed):
+    _say(f"device api {VARIANTS[variant]} grid={gx}x{gy}x{threads} used={used} rounds={rounds}")
+    st, ctrs, out, status = _run(devapi, variant, gx, gy, threads, used, rounds, seed,
+                                 max_poll=1_000_000)
+    n_grid = gx * gy
+    members = used if used else n_grid
+    want_out, want_status, want_ctr, rc = oracle.slot_rounds(seed, rounds, n_grid, used)
+    assert rc == 0 and st == 0
+    assert ctrs == [want_ctr] == [rounds * members]
+    np.testing.assert_array_equal(out[:, :members], want_out[:, :members])
+    np.testing.assert_array_equal(status, want_status)
+
+
+def test_device_api_bounded_reports_deadlock(devapi):
+    """Stripe 0 preset to 1 (not a multiple of its one member): the last round's
+    target is never reached; the small poll bound ends it with DEADLOCK."""
+    from cross_core_barrier_amd import ccb
+    _say("device api soft_bounded, stripe 0 preset 1, 4x1x64, maxPoll 2000")
+    st, _, _, status = _run(devapi, 3, 4, 1, 64, 0, 5, 1, max_poll=2000, preset=1)
+    assert st == ccb.CCB_ERR_DEADLOCK
+    assert (status == 3).any() and set(status.tolist()) <= {1, 3}
+
+
+def test_device_api_rejects_bad_launch(devapi):
+    assert devapi.devapi_run(4, None, None, None, None, 0, 1, 1, 1, 64, 0, 0, None) != 0
+    assert devapi.devapi_run(0, None, None, None, None, 0, 1, 2, 1, 64, 3, 0, None) != 0
