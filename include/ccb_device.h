@@ -124,7 +124,9 @@ struct ccb_no_overlap {
  * the round from it, epoch = before / n_s + 1 with n_s the stripe's member
  * count, and polls until every stripe l in use holds at least epoch * n_l
  * arrivals (for K = 1: the counter reaches (before / n + 1) * n, the
- * pages' target).  At most maxPoll polls; past that it stores
+ * pages' target); the first poll is issued before `before` is waited for,
+ * and the arrival's own stripe also counts as complete once before + 1
+ * reaches its target.  At most maxPoll polls; past that it stores
  * CCB_ERR_DEADLOCK in the error word and returns it.  Every 64th poll it
  * also reads the error word and returns its value when another member has
  * failed.  For CCB_VIS_FULL it ends with an agent-scope acquire fence.  The
@@ -147,13 +149,21 @@ __device__ __forceinline__ int32_t ccb_await(const int32_t* ctr, int32_t n, int3
     const int lane = (int)__lane_id();
     const int32_t ks = n < K ? n : K;  // stripes in use
     const int32_t s = member % K;
-    const int32_t epoch = __shfl(before / ((n - s + K - 1) / K) + 1, 0, 64);
+    int32_t* mine = const_cast<int32_t*>(ctr) + (lane < ks ? lane : 0) * CCB_LINE_WORDS;
+    // The first poll goes out before the arrival's reply is used, so the two
+    // round trips overlap; the reply itself then says whether this arrival
+    // completed its own stripe.  Counters only grow, so any value read that
+    // meets the target proves that stripe complete.
+    const int32_t v0 = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int32_t b = __shfl(before, 0, 64);
+    const int32_t epoch = b / ((n - s + K - 1) / K) + 1;
     // stripe `lane` is complete for this round at epoch * n_lane arrivals;
     // lanes past the stripes in use re-read stripe 0 and always agree
     const int32_t need = lane < ks ? epoch * ((n - lane + K - 1) / K) : INT32_MIN;
-    int32_t* mine = const_cast<int32_t*>(ctr) + (lane < ks ? lane : 0) * CCB_LINE_WORDS;
     int32_t rc = CCB_OK;
     uint32_t polls = 0;
+    const bool own = lane == s && b + 1 >= need;
+    if (!__all(v0 >= need || own))
     for (;;) {
         const int32_t v = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (__all(v >= need)) break;
