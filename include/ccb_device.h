@@ -162,26 +162,34 @@ __device__ __forceinline__ int32_t ccb_await(const int32_t* ctr, int32_t n, int3
     const int32_t need = lane < ks ? epoch * ((n - lane + K - 1) / K) : INT32_MIN;
     int32_t rc = CCB_OK;
     uint32_t polls = 0;
-    const bool own = lane == s && b + 1 >= need;
-    if (!__all(v0 >= need || own))
-    for (;;) {
-        const int32_t v = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (__all(v >= need)) break;
-        if (++polls >= maxPoll) {
-            if (lane == 0)
-                __hip_atomic_store(err, (int32_t)CCB_ERR_DEADLOCK, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            rc = CCB_ERR_DEADLOCK;
-            break;
-        }
-        if ((polls % CCB_ERR_CHECK_EVERY) == 0) {
-            const int32_t e = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (e != CCB_OK) {
-                rc = e;
+    // A stripe seen complete stays complete, so later polls read only the
+    // unfinished ones: lanes that are done re-read the first unfinished
+    // stripe, which adds no line to the gather.
+    int32_t* const base = const_cast<int32_t*>(ctr);
+    bool done = v0 >= need || (lane == s && b + 1 >= need);
+    if (!__all(done)) {
+        for (;;) {
+            const uint64_t pending = __ballot(!done);
+            int32_t* const addr = done ? base + __builtin_ctzll(pending) * CCB_LINE_WORDS : mine;
+            const int32_t v = __hip_atomic_load(addr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            done = done || v >= need;
+            if (__all(done)) break;
+            if (++polls >= maxPoll) {
+                if (lane == 0)
+                    __hip_atomic_store(err, (int32_t)CCB_ERR_DEADLOCK, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                rc = CCB_ERR_DEADLOCK;
                 break;
             }
+            if ((polls % CCB_ERR_CHECK_EVERY) == 0) {
+                const int32_t e = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (e != CCB_OK) {
+                    rc = e;
+                    break;
+                }
+            }
+            if (CCB_POLL_SLEEP > 0) __builtin_amdgcn_s_sleep(CCB_POLL_SLEEP);
         }
-        if (CCB_POLL_SLEEP > 0) __builtin_amdgcn_s_sleep(CCB_POLL_SLEEP);
     }
     // acquire: loads after the barrier see every member's released stores
     if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
