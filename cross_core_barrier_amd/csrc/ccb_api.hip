@@ -504,11 +504,13 @@ CCB_API ccbStatus ccb_cnt_notify_batch(const uint32_t* val, const uint8_t* meta,
     if (!aligned(final_, 4) || (val != nullptr && !aligned(val, 4))) return CCB_ERR_INVALID_VALUE;
     ccbStatus st = current_device(nullptr, nullptr);
     if (st != CCB_OK) return st;
-    const bool vec4 = (nCounters % 4) == 0 && (val == nullptr || aligned(val, 16)) &&
-                      (meta == nullptr || aligned(meta, 4)) && aligned(final_, 16) &&
-                      (rel == nullptr || aligned(rel, 4));
+    // the vector form moves kCntPerThread adjacent counters per thread
+    constexpr int C = ccb::kCntPerThread;
+    const bool vec = (nCounters % C) == 0 && (val == nullptr || aligned(val, 4 * C)) &&
+                     (meta == nullptr || aligned(meta, C)) && aligned(final_, 4 * C) &&
+                     (rel == nullptr || aligned(rel, C));
     return from_hip(ccb::launch_cnt_batch(val, meta, nCounters, nOps, final_, rel, nRelRows, err,
-                                          vec4, (hipStream_t)stream));
+                                          vec, (hipStream_t)stream));
 }
 
 }  // extern "C"

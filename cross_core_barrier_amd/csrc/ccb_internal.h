@@ -17,7 +17,8 @@ namespace ccb {
 #endif
 constexpr bool kStencilNT = CCB_STENCIL_NT_STORE != 0;      // non-temporal stores of the output
 constexpr bool kStencilNTLoad = CCB_STENCIL_NT_LOAD != 0;   // non-temporal loads of the input
-constexpr int kCntUnroll = 4;       // ops loaded ahead per thread in the batch engine
+constexpr int kCntPerThread = 2;   // adjacent counters per thread in the batch engine (2 or 4)
+constexpr int kCntUnroll = 2;      // ops loaded ahead per thread in the batch engine
 constexpr bool kCntNTLoad = true;   // non-temporal loads of the op stream (read once)
 
 enum class KernelId { BarrierOnly, SlotRounds, GroupedRounds, Stencil };
@@ -46,7 +47,7 @@ hipError_t launch_stencil(const LaunchShape& ls, int32_t* bufA, int32_t* bufB, i
                           uint32_t maxPoll);
 hipError_t launch_cnt_batch(const uint32_t* val, const uint8_t* meta, int64_t nCounters,
                             int32_t nOps, uint32_t* finalOut, uint8_t* rel, int32_t nRelRows,
-                            int32_t* err, bool vec4, hipStream_t s);
+                            int32_t* err, bool vec, hipStream_t s);
 hipError_t launch_cnt_record(uint32_t* line, int32_t mode, uint32_t value, hipStream_t s);
 hipError_t launch_cnt_wait(uint32_t* line, int32_t mode, uint32_t value, int32_t isClear,
                            uint64_t timeoutTicks, hipStream_t s);

@@ -726,19 +726,6 @@ __global__ __launch_bounds__(1024) void ccb_k_stencil(int32_t* bufA, int32_t* bu
 // ---------------------------------------------------------------------------
 namespace {
 
-// Record: returns the new count; *bad set for a code outside {0,1,2,4}.
-__device__ __forceinline__ uint32_t cnt_record(uint32_t c, uint32_t mode, uint32_t v, bool& bad)
-{
-    bad = !(mode == CCB_CNT_RECORD_SET_VALUE || mode == CCB_CNT_RECORD_ADD ||
-            mode == CCB_CNT_RECORD_BIT_OR || mode == CCB_CNT_RECORD_BIT_AND);
-    uint32_t r = c;
-    r = mode == CCB_CNT_RECORD_SET_VALUE ? v : r;
-    r = mode == CCB_CNT_RECORD_ADD ? c + v : r;
-    r = mode == CCB_CNT_RECORD_BIT_OR ? (c | v) : r;
-    r = mode == CCB_CNT_RECORD_BIT_AND ? (c & v) : r;
-    return r;
-}
-
 // Wait predicate; *bad set for a code above 4.
 __device__ __forceinline__ bool cnt_holds(uint32_t c, uint32_t mode, uint32_t v, bool& bad)
 {
@@ -752,100 +739,135 @@ __device__ __forceinline__ bool cnt_holds(uint32_t c, uint32_t mode, uint32_t v,
     return h;
 }
 
-// One op of the batched engine on one counter.  Returns true when the op is
-// a wait (its release flag in flag).  rowOk: the wait has an output row; a
-// wait without one is malformed and leaves the count alone.
+// One op of the batched engine on one counter (meta byte m: bits 0-2 mode,
+// bit 3 isClear, bits 4-6 reserved, bit 7 wait).  Returns true when the op
+// is a wait (its release flag in flag).  rowOk: the wait has an output row;
+// a wait without one is malformed and leaves the count alone.  Written for
+// the vector ALU, which bounds this engine about as much as HBM does: a
+// record compares its low seven bits with the four record codes directly
+// (a set clear or reserved bit, or the missing code 3, matches none of them
+// and keeps the count), so the same comparisons give the result and the
+// validity.
 __device__ __forceinline__ bool cnt_step(uint32_t& c, uint32_t m, uint32_t v, bool rowOk,
                                          bool& bad, uint8_t& flag)
 {
-    const uint32_t mode = m & 7u;
-    const uint32_t clear = (m >> 3) & 1u;
-    const uint32_t reserved = (m >> 4) & 7u;
-    const bool isWait = (m & 0x80u) != 0;
-    if (isWait) {
-        bool b;
-        const bool h = cnt_holds(c, mode, v, b);
-        b = b || reserved != 0 || !rowOk;
-        const bool rel = h && !b;
+    if ((m & 0x80u) != 0) {
+        const uint32_t mode = m & 0x77u;  // mode and reserved bits
+        bool h = false;
+        h = mode == CCB_CNT_WAIT_LESS ? (c < v) : h;
+        h = mode == CCB_CNT_WAIT_EQUAL ? (c == v) : h;
+        h = mode == CCB_CNT_WAIT_BIGGER ? (c > v) : h;
+        h = mode == CCB_CNT_WAIT_BIGGER_OR_EQUAL ? (c >= v) : h;
+        h = mode == CCB_CNT_WAIT_EQUAL_WITH_BITMASK ? ((c & v) == v) : h;
+        const bool ok = mode <= CCB_CNT_WAIT_EQUAL_WITH_BITMASK && rowOk;
+        const bool rel = h && ok;
         // the clear follows the release (CntNotify interfaces §3.3, §7)
-        c = (rel && clear) ? 0u : c;
+        c = (rel && (m & 8u) != 0) ? 0u : c;
         flag = rel ? 1 : 0;
-        bad = bad || b;
-    } else {
-        bool b;
-        const uint32_t r = cnt_record(c, mode, v, b);
-        b = b || reserved != 0 || clear != 0;
-        c = b ? c : r;
-        bad = bad || b;
+        bad = bad || !ok;
+        return true;
     }
-    return isWait;
+    const uint32_t op = m & 0x7Fu;
+    const bool set = op == CCB_CNT_RECORD_SET_VALUE, add = op == CCB_CNT_RECORD_ADD;
+    const bool bor = op == CCB_CNT_RECORD_BIT_OR, band = op == CCB_CNT_RECORD_BIT_AND;
+    uint32_t r = c;
+    r = set ? v : r;
+    r = add ? c + v : r;
+    r = bor ? (c | v) : r;
+    r = band ? (c & v) : r;
+    c = r;
+    bad = bad || !(set || add || bor || band);
+    return false;
 }
 
 }  // namespace
 
-// Four adjacent counters per thread: 4-byte meta loads and 16-byte operand
-// loads per op; nCounters must be a multiple of 4.
-template <int U>
-__global__ __launch_bounds__(256) void ccb_k_cnt_batch4(const uint32_t* __restrict__ val,
-                                                        const uint8_t* __restrict__ meta,
-                                                        int64_t nCounters, int32_t nOps,
-                                                        uint32_t* __restrict__ finalOut,
-                                                        uint8_t* __restrict__ rel,
-                                                        int32_t nRelRows, int32_t* err)
+// C adjacent counters per thread (C = 2 or 4): C-byte meta loads and
+// 4C-byte operand loads per op; nCounters must be a multiple of C.
+template <int C> struct CntVec;
+template <> struct CntVec<4> {
+    typedef unsigned int val __attribute__((ext_vector_type(4)));
+    typedef uint32_t meta;
+};
+template <> struct CntVec<2> {
+    typedef unsigned int val __attribute__((ext_vector_type(2)));
+    typedef uint16_t meta;
+};
+
+template <int C, int U>
+__global__ __launch_bounds__(256) void ccb_k_cnt_batch(const uint32_t* __restrict__ val,
+                                                       const uint8_t* __restrict__ meta,
+                                                       int64_t nCounters, int32_t nOps,
+                                                       uint32_t* __restrict__ finalOut,
+                                                       uint8_t* __restrict__ rel,
+                                                       int32_t nRelRows, int32_t* err)
 {
-    const int64_t c0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    typedef typename CntVec<C>::val VT;
+    typedef typename CntVec<C>::meta MT;
+    const int64_t c0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * C;
     if (c0 >= nCounters) return;
-    uint32_t c[4] = {0u, 0u, 0u, 0u};
-    int32_t j[4] = {0, 0, 0, 0};
-    bool bad = false;
-    int32_t k = 0;
-    auto apply = [&](uint32_t m4, uint4 v4) {
-        const uint32_t vv[4] = {v4.x, v4.y, v4.z, v4.w};
-        uint8_t f[4] = {0, 0, 0, 0};
-        bool w[4];
+    uint32_t c[C];
+    int32_t j[C];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            w[i] = cnt_step(c[i], (m4 >> (8 * i)) & 0xffu, vv[i], j[i] < nRelRows, bad, f[i]);
-        const bool allWait = w[0] && w[1] && w[2] && w[3];
-        if (allWait && j[0] == j[1] && j[0] == j[2] && j[0] == j[3] && j[0] < nRelRows) {
-            const uint32_t packed = (uint32_t)f[0] | ((uint32_t)f[1] << 8) |
-                                    ((uint32_t)f[2] << 16) | ((uint32_t)f[3] << 24);
-            *reinterpret_cast<uint32_t*>(rel + (int64_t)j[0] * nCounters + c0) = packed;
-            j[0]++; j[1]++; j[2]++; j[3]++;
+    for (int i = 0; i < C; ++i) c[i] = 0u, j[i] = 0;
+    bool bad = false;
+    auto apply = [&](uint32_t m, VT v) {
+        uint8_t f[C];
+        bool w[C];
+        bool allWait = true, sameRow = true;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            f[i] = 0;
+            w[i] = cnt_step(c[i], (m >> (8 * i)) & 0xffu, v[i], j[i] < nRelRows, bad, f[i]);
+            allWait = allWait && w[i];
+            sameRow = sameRow && j[i] == j[0];
+        }
+        if (allWait && sameRow && j[0] < nRelRows) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int i = 0; i < C; ++i) packed |= (uint32_t)f[i] << (8 * i);
+            *reinterpret_cast<MT*>(rel + (int64_t)j[0] * nCounters + c0) = (MT)packed;
+#pragma unroll
+            for (int i = 0; i < C; ++i) j[i]++;
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < C; ++i) {
                 if (!w[i]) continue;
                 if (j[i] < nRelRows) rel[(int64_t)j[i] * nCounters + c0 + i] = f[i];
                 j[i]++;
             }
         }
     };
-    for (; k + U <= nOps; k += U) {
-        uint32_t m4[U];
-        uint4 v4[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t* mp = reinterpret_cast<const uint32_t*>(meta + (int64_t)(k + u) * nCounters + c0);
-            const uint32_t* vp = val + (int64_t)(k + u) * nCounters + c0;
-            if constexpr (ccb::kCntNTLoad) {
-                m4[u] = __builtin_nontemporal_load(mp);
-                const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(vp));
-                v4[u] = make_uint4(t[0], t[1], t[2], t[3]);
-            } else {
-                m4[u] = *mp;
-                v4[u] = *reinterpret_cast<const uint4*>(vp);
-            }
+    auto load = [&](int32_t k, uint32_t& m, VT& v) {
+        const MT* mp = reinterpret_cast<const MT*>(meta + (int64_t)k * nCounters + c0);
+        const VT* vp = reinterpret_cast<const VT*>(val + (int64_t)k * nCounters + c0);
+        if constexpr (ccb::kCntNTLoad) {
+            m = __builtin_nontemporal_load(mp);
+            v = __builtin_nontemporal_load(vp);
+        } else {
+            m = *mp;
+            v = *vp;
         }
+    };
+    int32_t k = 0;
+    for (; k + U <= nOps; k += U) {
+        uint32_t m[U];
+        VT v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) apply(m4[u], v4[u]);
+        for (int u = 0; u < U; ++u) load(k + u, m[u], v[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) apply(m[u], v[u]);
     }
     for (; k < nOps; ++k) {
-        const uint32_t m4 = *reinterpret_cast<const uint32_t*>(meta + (int64_t)k * nCounters + c0);
-        const uint4 v4 = *reinterpret_cast<const uint4*>(val + (int64_t)k * nCounters + c0);
-        apply(m4, v4);
+        uint32_t m;
+        VT v;
+        load(k, m, v);
+        apply(m, v);
     }
-    *reinterpret_cast<uint4*>(finalOut + c0) = make_uint4(c[0], c[1], c[2], c[3]);
+    VT out;
+#pragma unroll
+    for (int i = 0; i < C; ++i) out[i] = c[i];
+    *reinterpret_cast<VT*>(finalOut + c0) = out;
     if (bad && err != nullptr)
         __hip_atomic_store(err, (int32_t)CCB_ERR_INVALID_VALUE, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -1077,13 +1099,14 @@ hipError_t launch_stencil(const LaunchShape& ls, int32_t* bufA, int32_t* bufB, i
 
 hipError_t launch_cnt_batch(const uint32_t* val, const uint8_t* meta, int64_t nCounters,
                             int32_t nOps, uint32_t* finalOut, uint8_t* rel, int32_t nRelRows,
-                            int32_t* err, bool vec4, hipStream_t s)
+                            int32_t* err, bool vec, hipStream_t s)
 {
     constexpr int kThreads = 256;
-    if (vec4) {
-        const int64_t nThreads = nCounters / 4;
+    if (vec) {
+        constexpr int C = ccb::kCntPerThread;
+        const int64_t nThreads = nCounters / C;
         const int64_t nBlocks = (nThreads + kThreads - 1) / kThreads;
-        hipLaunchKernelGGL((ccb_k_cnt_batch4<kCntUnroll>), dim3((unsigned)nBlocks), dim3(kThreads),
+        hipLaunchKernelGGL((ccb_k_cnt_batch<C, kCntUnroll>), dim3((unsigned)nBlocks), dim3(kThreads),
                            0, s, val, meta, nCounters, nOps, finalOut, rel, nRelRows, err);
     } else {
         const int64_t nBlocks = (nCounters + kThreads - 1) / kThreads;

@@ -41,7 +41,7 @@ def _run_batch(wl, val, meta, rows):
 
 @pytest.mark.parametrize("n_counters,n_ops,small", [
     (1024, 64, False), (1027, 64, False), (4096, 13, True), (4100, 64, True), (1, 8, True),
-    (3, 0, False),
+    (3, 0, False), (1026, 64, True), (2, 17, True),
 ])
 def test_batch_small(wl, n_counters, n_ops, small):
     _say(f"cnt_batch n={n_counters} ops={n_ops} small_values={small}")
@@ -77,6 +77,30 @@ def test_batch_malformed(wl, n_counters):
     err, final, rel = _run_batch(wl, val, meta, rows)
     f2, r2, rc = oracle.cnt_batch(val, meta, rows)
     assert rc == oracle.INVALID_VALUE and err == oracle.INVALID_VALUE
+    np.testing.assert_array_equal(final, f2)
+    np.testing.assert_array_equal(rel, r2)
+
+
+@pytest.mark.parametrize("n_counters", [4096, 4097])
+def test_batch_waits_at_different_ops(wl, n_counters):
+    """Each counter has its own wait positions, so neighbouring counters
+    wait at different ops and their release flags land in different rows."""
+    _say(f"cnt_batch per-counter wait positions n={n_counters}")
+    n_ops = 48
+    val, meta, _ = inputs.cnt_batch_input(13, n_counters, n_ops, small_values=True)
+    meta = meta.copy()
+    rng = np.random.default_rng(14)
+    is_wait = rng.random((n_ops, n_counters)) < 0.2
+    modes = rng.integers(0, 5, size=(n_ops, n_counters))
+    clear = rng.random((n_ops, n_counters)) < 0.5
+    wait_meta = (0x80 | modes | (clear.astype(np.int64) << 3)).astype(np.uint8)
+    meta[is_wait] = wait_meta[is_wait]
+    rec = (meta & 0x80) == 0
+    meta[rec] = np.array([0, 1, 2, 4], np.uint8)[rng.integers(0, 4, size=rec.sum())]
+    rows = int(((meta & 0x80) != 0).sum(axis=0).max())
+    err, final, rel = _run_batch(wl, val, meta, rows)
+    f2, r2, rc = oracle.cnt_batch(val, meta, rows)
+    assert rc == 0 and err == 0
     np.testing.assert_array_equal(final, f2)
     np.testing.assert_array_equal(rel, r2)
 
