@@ -335,6 +335,50 @@ class Bench:
                                          "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
                                          "ops_per_s": round(CNT_COUNTERS * CNT_OPS / (bms / 1e3), 0)}
 
+    # ------------------------------------------------------------ stream-to-stream notify
+    def cnt_stream_latency(self):
+        """CntNotify §5's pattern on streams: the consumer stream waits GE N
+        (isClear) while N producer streams each record ADD 1 after a short
+        spin (so the wait is usually polling already).  Latency = the last
+        record's completion to the wait's completion, from HIP events on the
+        streams; rounds are separated on the host.  The records are enqueued
+        before the wait, so that a wait never sits in a hardware queue in
+        front of the records it waits for (streams share the box's few
+        queues); N = 1 and 2."""
+        ccb, torch = self.ccb, self.torch
+        out = {}
+        for n in (1, 2):
+            prods = [torch.cuda.Stream() for _ in range(n)]
+            cons = torch.cuda.Stream()
+            st, h = ccb.ccb_cnt_notify_create(0)
+            ccb.check(st, "create")
+            lat = []
+            for r in range(100):
+                evs = []
+                for s in prods:  # producers first: see the docstring
+                    with torch.cuda.stream(s):
+                        torch.cuda._sleep(50000)
+                    ccb.check(ccb.ccb_cnt_notify_record(
+                        h, s, ccb.record_info(ccb.CCB_CNT_RECORD_ADD, 1)), "record")
+                    e = torch.cuda.Event(enable_timing=True)
+                    e.record(s)
+                    evs.append(e)
+                ccb.check(ccb.ccb_cnt_notify_wait(
+                    h, cons, ccb.wait_info(ccb.CCB_CNT_WAIT_BIGGER_OR_EQUAL, n, 2, 1)), "wait")
+                ev_c = torch.cuda.Event(enable_timing=True)
+                ev_c.record(cons)
+                torch.cuda.synchronize()
+                st, v, last = ccb.ccb_cnt_notify_query(h, cons)
+                assert (st, v, last) == (0, 0, ccb.CCB_OK), (r, st, v, last)
+                if r >= 10:
+                    lat.append(min(e.elapsed_time(ev_c) for e in evs) * 1e3)
+            ccb.check(ccb.ccb_cnt_notify_destroy(h), "destroy")
+            lat.sort()
+            out[f"producers_{n}"] = {"median_us": round(lat[len(lat) // 2], 2),
+                                     "p90_us": round(lat[int(len(lat) * 0.9)], 2)}
+        self.extra["cntnotify_stream_notify_latency"] = out
+        log(f"cntnotify stream notify latency: {out}")
+
     # ------------------------------------------------------------ CPU baseline
     def cpu_baseline(self):
         import oracle
@@ -350,6 +394,40 @@ class Bench:
                 "kind": "oracle",
                 "sample": f"{reps} full runs of the 256-workgroup, 10000-round witness simulation "
                           f"({t_cpu:.1f} s on one thread; the host has {os.cpu_count()} cores)"}
+
+
+    def cpu_context(self):
+        """Context beside the GPU figures (not baselines): the epoch barrier on
+        host threads, and the oracle's stencil and batch engine on one core."""
+        import oracle
+        nproc = os.cpu_count() or 1
+        model = ""
+        try:
+            with open("/proc/cpuinfo") as f:
+                model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+        except OSError:
+            pass
+        threads = min(16, nproc)  # this GPU's share of the host
+        _, ns, rc = oracle.host_barrier(threads, 20_000, 1)
+        assert rc == 0
+        x = self.inputs.stencil_input(self.inputs.STENCIL["seed"], STENCIL_N)
+        t1 = time.perf_counter()
+        oracle.stencil(x, 1)
+        st_s = time.perf_counter() - t1
+        c = self.inputs.CNT_BATCH
+        val, meta, rows = self.inputs.cnt_batch_input(c["seed"], CNT_COUNTERS, CNT_OPS)
+        t1 = time.perf_counter()
+        _, _, rc = oracle.cnt_batch(val, meta, rows)
+        cb_s = time.perf_counter() - t1
+        assert rc == 0
+        cnt_bytes = val.nbytes + meta.nbytes + CNT_COUNTERS * 4 + rows * CNT_COUNTERS
+        self.extra["cpu_context"] = {
+            "host": {"nproc": nproc, "cpu_model": model},
+            "host_thread_barrier": {"threads": threads, "ns_per_barrier": round(ns, 1),
+                                    "rounds": 20_000},
+            "oracle_stencil_one_iteration_GBs": round(STENCIL_BYTES_PER_ITER / st_s / 1e9, 3),
+            "oracle_cnt_batch_GBs": round(cnt_bytes / cb_s / 1e9, 3)}
+        log(f"cpu context: {self.extra['cpu_context']}")
 
 
 def main():
@@ -376,8 +454,10 @@ def main():
         gbs = b.copy_ceiling()
         roofline = b.stencil(gbs)
         b.cnt_batch()
+        b.cnt_stream_latency()
         if not args.no_cpu:
             cpu = b.cpu_baseline()
+            b.cpu_context()
 
     line = {
         "metric": "grid barriers/s (ns/barrier) at 256 WGs; data-phase HBM GB/s vs peak",

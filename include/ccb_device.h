@@ -268,6 +268,28 @@ __device__ __forceinline__ int32_t ccb_syncall_soft_ordered(int32_t* ws, int32_t
                                                    ws + CCB_STRIPES * CCB_LINE_WORDS);
 }
 
+/* [SYNCALL] §4.2's mixed-role participant count, for workgroups in role
+ * groups: one leading workgroup with `ratio` companions (the analog of one
+ * cube core with its `ratio` vector cores).  The participants are the first
+ * groups * (1 + ratio) workgroups in linear order (group g is workgroups
+ * g * (1 + ratio) .. g * (1 + ratio) + ratio, the leader first); groups == 0
+ * means the whole grid.  ratio >= 0 (the pages default it to 1). */
+__host__ __device__ __forceinline__ int32_t ccb_mix_participants(int32_t groups, int32_t ratio,
+                                                                 int32_t gridSize)
+{
+    return groups != 0 ? groups * (1 + ratio) : gridSize;
+}
+
+/* ccb_syncall_soft over a mixed-role group set (see ccb_mix_participants):
+ * every participant calls it, non-participants never do. */
+__device__ __forceinline__ int32_t ccb_syncall_soft_mix(int32_t* ws, int32_t groups, int32_t ratio)
+{
+    const int32_t n =
+        ccb_mix_participants(groups, ratio, (int32_t)(gridDim.x * gridDim.y * gridDim.z));
+    return ccb_barrier<CCB_STRIPES, CCB_VIS_FULL>(ws, n, ccb_block_linear(), CCB_SOFT_MAX_POLL,
+                                                  ws + CCB_STRIPES * CCB_LINE_WORDS);
+}
+
 /* The pages' single-counter barrier exactly (one counter line, full
  * visibility); same workspace layout, only stripe 0 is used. */
 __device__ __forceinline__ int32_t ccb_syncall_soft_flat(int32_t* ws, int32_t usedCores)

@@ -5,6 +5,8 @@ baseline leg of bench.py may import this package.  The product path (the
 HIP library and its Python binding) never touches it, and it shares no code
 with that path: the arithmetic lives in oracle/ccb_oracle.c (plain C, built
 with gcc) and in the pure-Python enumerator and handle model beside it.
+oracle/host_barrier.c runs the same arrival rule on host threads (a
+concurrency check of the method and the CPU context figure).
 
 Parity pins (what checks each oracle function against something other than
 itself; see tests/test_oracle_*.py):
@@ -12,6 +14,8 @@ itself; see tests/test_oracle_*.py):
   witness_hash       SplitMix64 published output sequences (seed 0 and seed
                      1234567) -- pins the generator; the (seed, round, wg)
                      keying is this build's convention, not the pages'.
+  mix_participants   the SYNCALL guide's §4.2 formula (blocks x (1 + ratio))
+                     on its 1:1 and 1:2 cases, whole launch for 0.
   epoch_target       the SYNCALL guide's §5.2 prose (next multiple of N above
                      the old count), checked by brute force over small
                      (before, N) against a search for that multiple.
@@ -23,6 +27,8 @@ itself; see tests/test_oracle_*.py):
                      against an independent numpy formulation, fixed points
                      (constants, x[i] = i in the interior), the max principle
                      and an exact mass identity.
+  host_barrier       (not a reference for the GPU: the method on real host
+                     threads) must reproduce slot_rounds' sums exactly.
   cnt_record,        the pages' mode tables (tests/golden), an exhaustive
   cnt_wait,          4-bit table against a set-of-bits restatement, 32-bit
   cnt_batch          edge cases (wrap, unsigned order), the pages' worked
@@ -42,6 +48,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ccb_oracle.c")
+_SRC_HOST_BARRIER = os.path.join(_HERE, "host_barrier.c")
 _LIB_PATH = os.path.join(_HERE, "libccb_oracle.so")
 _lib = None
 
@@ -51,10 +58,11 @@ OK, INVALID_VALUE, DEADLOCK = 0, 1, 6
 def build(force: bool = True) -> str:
     """Compile the C oracle with gcc into oracle/libccb_oracle.so."""
     if force or not os.path.exists(_LIB_PATH) or \
-            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            os.path.getmtime(_LIB_PATH) < max(os.path.getmtime(_SRC),
+                                              os.path.getmtime(_SRC_HOST_BARRIER)):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-std=c11", "-O2", "-fPIC", "-shared",
-                               "-Wall", "-Wextra", "-o", tmp, _SRC])
+        subprocess.check_call(["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-pthread",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, _SRC_HOST_BARRIER])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -75,6 +83,8 @@ def _load():
     lib.ccbo_epoch_target.restype = i32
     lib.ccbo_participants.argtypes = [i32, i32]
     lib.ccbo_participants.restype = i32
+    lib.ccbo_mix_participants.argtypes = [i32, i32, i32]
+    lib.ccbo_mix_participants.restype = i32
     lib.ccbo_slot_rounds.argtypes = [u64, i32, i32, i32, P, P, P]
     lib.ccbo_slot_rounds.restype = ctypes.c_int
     lib.ccbo_grouped_rounds.argtypes = [u64, i32, i32, P, P, P]
@@ -89,6 +99,8 @@ def _load():
     lib.ccbo_cnt_wait_apply.restype = ctypes.c_int
     lib.ccbo_cnt_batch.argtypes = [P, P, i64, i32, P, P, i32]
     lib.ccbo_cnt_batch.restype = ctypes.c_int
+    lib.ccbo_host_barrier.argtypes = [i32, i32, u64, u64, P, ctypes.POINTER(ctypes.c_double)]
+    lib.ccbo_host_barrier.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -128,6 +140,20 @@ def slot_rounds(seed: int, rounds: int, n_grid: int, used_cores: int = 0,
     rc = _load().ccbo_slot_rounds(seed, rounds, n_grid, used_cores, _ptr(out), _ptr(status),
                                   _ptr(ctr))
     return out, status, int(ctr[0]), int(rc)
+
+
+def mix_participants(groups: int, ratio: int, n_launched: int) -> int:
+    return int(_load().ccbo_mix_participants(groups, ratio, n_launched))
+
+
+def host_barrier(threads: int, rounds: int, seed: int, max_poll: int = 1 << 40
+                 ) -> Tuple[np.ndarray, float, int]:
+    """The flag-slot rounds on `threads` host threads through the epoch
+    barrier.  Returns (out[rounds, threads] uint32, ns per barrier, rc)."""
+    out = np.zeros((max(rounds, 0), max(threads, 1)), dtype=np.uint32)
+    ns = ctypes.c_double(0.0)
+    rc = _load().ccbo_host_barrier(threads, rounds, seed, max_poll, _ptr(out), ctypes.byref(ns))
+    return out, float(ns.value), int(rc)
 
 
 def grouped_rounds(seed: int, rounds: int, n_grid: int, counters0=(0, 0, 0)

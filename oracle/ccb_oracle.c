@@ -94,6 +94,19 @@ int32_t ccbo_participants(int32_t usedCores, int32_t nLaunched)
     return usedCores != 0 ? usedCores : nLaunched;
 }
 
+/* Mixed-role participant count.  [SYNCALL] §4.2: in Mix mode the count is  */
+/* the number of cube blocks times (1 + the vector-core ratio).  Here a      */
+/* "block" is a group of one leading workgroup and `ratio` companions;       */
+/* groups == 0 takes the whole launch.  Rejected (pages silent): negative    */
+/* groups or ratio, and a count above the launch.                            */
+int32_t ccbo_mix_participants(int32_t groups, int32_t ratio, int32_t nLaunched)
+{
+    if (groups < 0 || ratio < 0 || nLaunched <= 0) return -1;
+    if (groups == 0) return nLaunched;
+    if ((int64_t)groups * (1 + ratio) > nLaunched) return -1;
+    return groups * (1 + ratio);
+}
+
 /* ------------------------------------------------------------------------ */
 /* One barrier round, simulated sequentially.                                */
 /*                                                                           */

@@ -2,7 +2,9 @@
 // the way a caller's own kernel would use it: the flag-slot pattern of the
 // SYNCALL guide §6.1 (write own slot, barrier, read every member's slot)
 // over a 2-D grid, with ccb_syncall_soft, ccb_syncall_soft_ordered,
-// ccb_syncall_soft_flat or ccb_syncall_soft_bounded.  Test code only: the
+// ccb_syncall_soft_flat, ccb_syncall_soft_bounded or ccb_syncall_soft_mix
+// (role groups of one leader and 1 or 2 companions; usedCores then counts
+// groups).  Test code only: the
 // GPU tests compare its output with the oracle's witness rounds.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -30,7 +32,9 @@ __global__ __launch_bounds__(1024) void devapi_rounds(int32_t* ws, uint32_t* slo
     __shared__ uint32_t partial[16];
     const int32_t nGrid = (int32_t)(gridDim.x * gridDim.y * gridDim.z);
     const int32_t w = ccb_block_linear();
-    const int32_t n = usedCores != 0 ? usedCores : nGrid;
+    const int32_t ratio = kVariant == 4 ? 1 : 2;  // variants 4 and 5: role groups
+    const int32_t n = kVariant >= 4 ? ccb_mix_participants(usedCores, ratio, nGrid)
+                                    : (usedCores != 0 ? usedCores : nGrid);
     const uint32_t tid = threadIdx.x;
     if (w >= n) {  // non-members never call the barrier
         if (tid == 0) status[w] = 2;
@@ -47,7 +51,8 @@ __global__ __launch_bounds__(1024) void devapi_rounds(int32_t* ws, uint32_t* slo
         if (kVariant == 0) rc = ccb_syncall_soft(ws, usedCores);
         else if (kVariant == 1) rc = ccb_syncall_soft_ordered(ws, usedCores);
         else if (kVariant == 2) rc = ccb_syncall_soft_flat(ws, usedCores);
-        else rc = ccb_syncall_soft_bounded(ws, usedCores, maxPoll);
+        else if (kVariant == 3) rc = ccb_syncall_soft_bounded(ws, usedCores, maxPoll);
+        else rc = ccb_syncall_soft_mix(ws, usedCores, ratio);
         if (rc != CCB_OK) break;
         uint32_t s = 0;
         for (int32_t i = (int32_t)tid; i < n; i += (int32_t)blockDim.x)
@@ -67,20 +72,23 @@ __global__ __launch_bounds__(1024) void devapi_rounds(int32_t* ws, uint32_t* slo
 
 }  // namespace
 
-// Launches variant 0..3 cooperatively on a gx x gy grid of `threads`
+// Launches variant 0..5 cooperatively on a gx x gy grid of `threads`
 // threads (a multiple of 64, at most 1024).  slots: 2 * gx * gy uint32;
 // out: rounds * gx * gy uint32; status: gx * gy int32.  Returns a hipError_t.
 extern "C" int devapi_run(int variant, int32_t* ws, uint32_t* slots, uint32_t* out, int32_t* status,
                           uint64_t seed, int32_t rounds, int32_t gx, int32_t gy, int32_t threads,
                           int32_t usedCores, uint32_t maxPoll, hipStream_t stream)
 {
-    if (variant < 0 || variant > 3 || threads < 64 || threads > 1024 || threads % 64 != 0 ||
-        gx < 1 || gy < 1 || usedCores < 0 || usedCores > gx * gy)
+    const int32_t members = variant >= 4 ? ccb_mix_participants(usedCores, variant == 4 ? 1 : 2, gx * gy)
+                                         : usedCores;
+    if (variant < 0 || variant > 5 || threads < 64 || threads > 1024 || threads % 64 != 0 ||
+        gx < 1 || gy < 1 || usedCores < 0 || members > gx * gy)
         return (int)hipErrorInvalidValue;
     void* args[] = {&ws, &slots, &out, &status, &seed, &rounds, &usedCores, &maxPoll};
-    const void* fn = variant == 0   ? reinterpret_cast<const void*>(&devapi_rounds<0>)
-                     : variant == 1 ? reinterpret_cast<const void*>(&devapi_rounds<1>)
-                     : variant == 2 ? reinterpret_cast<const void*>(&devapi_rounds<2>)
-                                    : reinterpret_cast<const void*>(&devapi_rounds<3>);
+    const void* const fns[6] = {
+        reinterpret_cast<const void*>(&devapi_rounds<0>), reinterpret_cast<const void*>(&devapi_rounds<1>),
+        reinterpret_cast<const void*>(&devapi_rounds<2>), reinterpret_cast<const void*>(&devapi_rounds<3>),
+        reinterpret_cast<const void*>(&devapi_rounds<4>), reinterpret_cast<const void*>(&devapi_rounds<5>)};
+    const void* fn = fns[variant];
     return (int)hipLaunchCooperativeKernel(fn, dim3(gx, gy), dim3(threads), args, 0, stream);
 }

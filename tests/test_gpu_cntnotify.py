@@ -159,6 +159,31 @@ def test_n_producers(ccb):
     assert ccb.ccb_cnt_notify_destroy(h) == 0
 
 
+def test_rounds_reuse_with_clear(ccb):
+    """CntNotify §5/§7: the same counter reused round after round -- N producer
+    streams ADD 1, the consumer waits GE N with isClear -- each round released
+    and cleared back to 0 (rounds separated on the host, as a real producer
+    would wait for the consumer before its next record)."""
+    n, rounds = 2, 20
+    _say(f"cntnotify {rounds} rounds: {n} producers ADD 1, consumer GE {n} with clear")
+    prods = [torch.cuda.Stream() for _ in range(n)]
+    cons = torch.cuda.Stream()
+    h = _mk(ccb)
+    for r in range(rounds):
+        # producers first: a wait never sits in a hardware queue in front of
+        # the records it waits for; their short spin lets the wait start first
+        for s in prods:
+            with torch.cuda.stream(s):
+                torch.cuda._sleep(50000)
+            assert ccb.ccb_cnt_notify_record(h, s, ccb.record_info(ccb.CCB_CNT_RECORD_ADD, 1)) == 0
+        assert ccb.ccb_cnt_notify_wait(
+            h, cons, ccb.wait_info(ccb.CCB_CNT_WAIT_BIGGER_OR_EQUAL, n, 2, 1)) == 0
+        torch.cuda.synchronize()
+        st, v, last = ccb.ccb_cnt_notify_query(h, cons)
+        assert (st, v, last) == (0, 0, ccb.CCB_OK), r
+    assert ccb.ccb_cnt_notify_destroy(h) == 0
+
+
 def test_wait_timeout(ccb):
     _say("cntnotify wait GE 5 with 1 s timeout and no record: expect TIMEOUT")
     s = torch.cuda.Stream()

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 LIB = os.path.join(os.path.dirname(__file__), "devapi", "libccb_devapi.so")
-VARIANTS = {0: "soft", 1: "soft_ordered", 2: "soft_flat", 3: "soft_bounded"}
+VARIANTS = {0: "soft", 1: "soft_ordered", 2: "soft_flat", 3: "soft_bounded"}  # 4, 5: mix 1:1, 1:2
 
 
 def _say(msg):
@@ -74,6 +74,28 @@ def test_device_api_witness_rounds(devapi, variant, gx, gy, threads, used, round
     np.testing.assert_array_equal(status, want_status)
 
 
+@pytest.mark.parametrize("variant,ratio", [(4, 1), (5, 2)], ids=["mix_1_1", "mix_1_2"])
+@pytest.mark.parametrize("gx,gy,groups,rounds,seed", [
+    (8, 2, 5, 40, 16),     # 5 groups, idle workgroups after them
+    (12, 1, 0, 33, 17),    # groups == 0: the whole grid
+    (9, 3, 4, 20, 18),
+])
+def test_device_api_mixed_roles(devapi, variant, ratio, gx, gy, groups, rounds, seed):
+    """Role groups (one leader and `ratio` companions, [SYNCALL] §4.2's
+    groups x (1 + ratio) participants): the sums over the participants match
+    the oracle's witness rounds with that many members."""
+    n_grid = gx * gy
+    members = oracle.mix_participants(groups, ratio, n_grid)
+    _say(f"device api soft_mix 1:{ratio} grid={gx}x{gy} groups={groups} members={members}")
+    st, ctrs, out, status = _run(devapi, variant, gx, gy, 64, groups, rounds, seed)
+    want_out, want_status, want_ctr, rc = oracle.slot_rounds(seed, rounds, n_grid,
+                                                             members if groups else 0)
+    assert rc == 0 and st == 0
+    assert ctrs == [want_ctr] == [rounds * members]
+    np.testing.assert_array_equal(out[:, :members], want_out[:, :members])
+    np.testing.assert_array_equal(status, want_status)
+
+
 def test_device_api_bounded_reports_deadlock(devapi):
     """Stripe 0 preset to 1 (not a multiple of its one member): the last round's
     target is never reached; the small poll bound ends it with DEADLOCK."""
@@ -85,5 +107,6 @@ def test_device_api_bounded_reports_deadlock(devapi):
 
 
 def test_device_api_rejects_bad_launch(devapi):
-    assert devapi.devapi_run(4, None, None, None, None, 0, 1, 1, 1, 64, 0, 0, None) != 0
+    assert devapi.devapi_run(6, None, None, None, None, 0, 1, 1, 1, 64, 0, 0, None) != 0
+    assert devapi.devapi_run(5, None, None, None, None, 0, 1, 4, 1, 64, 2, 0, None) != 0  # 6 > 4
     assert devapi.devapi_run(0, None, None, None, None, 0, 1, 2, 1, 64, 3, 0, None) != 0

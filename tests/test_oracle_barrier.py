@@ -85,6 +85,19 @@ def test_participants_rule():
     assert oracle.participants(257, 256) == -1
 
 
+def test_mix_participants_rule():
+    # SYNCALL guide §4.2: Mix count = blocks x (1 + ratio); the ratios the
+    # pages' Mix tests use and the default ratio come from the golden file.
+    g = _golden_constants()
+    for ratio in (g["mix_test_ratio_a"], g["mix_test_ratio_b"], g["mix_default_aiv_ratio"]):
+        for groups in (1, 3, 8):
+            assert oracle.mix_participants(groups, ratio, 64) == groups + groups * ratio
+        assert oracle.mix_participants(0, ratio, 48) == 48          # whole launch
+        assert oracle.mix_participants(64, ratio, 64) == -1         # more than launched
+    assert oracle.mix_participants(-1, 1, 8) == -1
+    assert oracle.mix_participants(1, -1, 8) == -1
+
+
 def test_golden_constants_present():
     c = _golden_constants()
     assert c["soft_max_poll_iterations"] == 1_000_000
@@ -341,3 +354,16 @@ def test_enumerator_lead_plus_lag_bound():
                 res = en.enumerate_schedules(en.whole_grid(3, d + 2), 3, write_lead=a,
                                              read_lag=b, ring_depth=d)
                 assert (res.violations == []) == (d >= a + b), (a, b, d)
+
+
+# The method on real host threads: T threads write, pass the epoch barrier
+# (acq_rel add, acquire poll) and sum every slot; the sums must equal the
+# sequential simulator's for every round.
+
+@pytest.mark.parametrize("threads,rounds", [(1, 50), (2, 2000), (4, 3000), (7, 500)])
+def test_host_threads_match_simulator(threads, rounds):
+    out, ns, rc = oracle.host_barrier(threads, rounds, 21)
+    assert rc == 0 and ns > 0
+    want, _, ctr, rc2 = oracle.slot_rounds(21, rounds, threads, 0)
+    assert rc2 == 0 and ctr == rounds * threads
+    np.testing.assert_array_equal(out, want)
