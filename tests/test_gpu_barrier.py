@@ -68,6 +68,7 @@ def _oracle_grouped(seed, rounds, n_grid):
     (8, 91, 300, 64, 0, 0),         # more members than 4 slots per thread
     (9, 2, 5, 64, 0, 0),            # two rounds: the pipeline's prologue and drain only
     (10, 1, 5, 64, 0, 0),           # one round
+    (11, 40, 256, 1024, 0, 1),      # 1024-thread workgroups, one per CU
 ])
 def test_slot_rounds_small(wl, seed, rounds, n_grid, threads, used, wpc, mode):
     _say(f"slot_rounds mode={mode} seed={seed} rounds={rounds} grid={n_grid}x{threads} used={used}")
@@ -137,6 +138,18 @@ def test_barrier_only_counts_and_placement(wl, mode):
     key = set(zip(p[:, 1].tolist(), se.tolist(), sh.tolist(), cu.tolist()))
     print(f"distinct CUs used by 256 WGs: {len(key)}; XCDs: {sorted(set(p[:, 1].tolist()))}")
     assert len(set(p[:, 1].tolist())) == 8
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+@pytest.mark.parametrize("n_grid,threads,wpc,rounds", [
+    (4096, 64, 16, 200),   # 16 workgroups per CU: 64 members on every stripe
+    (256, 1024, 1, 300),   # the largest workgroups, one per CU
+])
+def test_barrier_only_large_grids(wl, n_grid, threads, wpc, rounds, mode):
+    _say(f"barrier_only {n_grid}x{threads} rounds={rounds} wgsPerCu={wpc} mode={mode}")
+    st, ctrs, wg, _ = wl.barrier_only(rounds, n_grid, threads, wgs_per_cu=wpc, mode=mode)
+    assert st == 0 and ctrs == [rounds * n_grid]
+    assert (wg.cpu().numpy() == 1).all()
 
 
 @pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
