@@ -9,14 +9,10 @@
 namespace ccb {
 
 // Tuning constants of the kernels.
-#ifndef CCB_STENCIL_NT_STORE
-#define CCB_STENCIL_NT_STORE 0
-#endif
-#ifndef CCB_STENCIL_NT_LOAD
-#define CCB_STENCIL_NT_LOAD 1
-#endif
-constexpr bool kStencilNT = CCB_STENCIL_NT_STORE != 0;      // non-temporal stores of the output
-constexpr bool kStencilNTLoad = CCB_STENCIL_NT_LOAD != 0;   // non-temporal loads of the input
+// Stencil: non-temporal loads of the input (+7%); plain stores of the output
+// (non-temporal stores measured 4% slower, in both barrier variants).
+constexpr bool kStencilNT = false;
+constexpr bool kStencilNTLoad = true;
 constexpr int kCntPerThread = 2;   // adjacent counters per thread in the batch engine (2 or 4)
 constexpr int kCntUnroll = 2;      // ops loaded ahead per thread in the batch engine
 constexpr bool kCntNTLoad = true;   // non-temporal loads of the op stream (read once)

@@ -21,7 +21,6 @@
 namespace {
 
 constexpr int kWave = 64;
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 constexpr int kRing = CCB_SLOT_ROWS;  // witness slot rows reused round-robin
 constexpr int kSlot = CCB_SLOT_WORDS;  // words from one slot to the next
 
