@@ -42,6 +42,12 @@ MODE_IDS = ["striped-order", "flat-order", "striped-full", "flat-full"]
     (256 * 64 * 4, 7, 8, 256),     # all chunks full, several per workgroup
     (1024 * 3, 4, 5, 256),         # workgroups without chunks
     (1024 * 64, 2, 16, 1024),      # 1024-thread workgroups, two iterations
+    # full chunks split evenly, 17 to 33 per workgroup
+    (1024 * 17 * 4, 5, 4, 256),
+    (256 * 20 * 3, 6, 3, 64),      # one wave per workgroup
+    (1024 * 20, 4, 1, 256),        # a single workgroup
+    (4096 * 18 * 2, 3, 2, 1024),   # 1024-thread workgroups
+    (1024 * 33 * 8, 2, 8, 256),    # two iterations
 ])
 def test_stencil_small(wl, n, iters, n_grid, threads, mode):
     _say(f"stencil mode={mode} n={n} iters={iters} grid={n_grid}x{threads}")
