@@ -116,6 +116,18 @@ ccbStatus plan_persistent(ccb::KernelId id, int32_t mode, int32_t nGrid, int32_t
 
 inline uint32_t poll_bound(uint32_t maxPoll) { return maxPoll == 0 ? CCB_SOFT_MAX_POLL : maxPoll; }
 
+// The counters are int32 (SYNCALL guide §4.1): a stripe stays valid while
+// its arrivals since the reset plus its participant count stay below 2^31.
+// Member m arrives on stripe m mod CCB_STRIPES, so the fullest stripe takes
+// ceil(N / 64) arrivals per barrier; the single-counter variant takes N.
+// Checked for a launch that starts from a zeroed workspace.
+inline bool counts_fit(int64_t barriers, int64_t members, int32_t mode)
+{
+    const int64_t perStripe =
+        (mode & CCB_BARRIER_FLAT) ? members : (members + CCB_STRIPES - 1) / CCB_STRIPES;
+    return barriers <= 0 || perStripe <= INT32_MAX / (barriers + 1);
+}
+
 // ---------------------------------------------------------------------------
 // CntNotify handle table (CntNotify interfaces §4.1, §4.5, §4.6, §6.1).
 // A handle value encodes (generation << 20) | (index + 1); it is never
@@ -255,7 +267,8 @@ CCB_API ccbStatus ccb_run_barrier_only(int32_t* ws, uint32_t* placement, int32_t
 {
     if (ws == nullptr) return CCB_ERR_NULL_POINTER;
     if (!aligned(ws, CCB_LINE_BYTES) || rounds < 0 || nGrid < 1 || !valid_threads(threads) ||
-        usedCores < 0 || usedCores > nGrid || wgsPerCu < 0 || !valid_mode(mode))
+        usedCores < 0 || usedCores > nGrid || wgsPerCu < 0 || !valid_mode(mode) ||
+        !counts_fit(rounds, usedCores != 0 ? usedCores : nGrid, mode))
         return CCB_ERR_INVALID_VALUE;
     ccb::LaunchShape ls;
     ccbStatus st = plan_persistent(ccb::KernelId::BarrierOnly, mode, nGrid, threads, wgsPerCu,
@@ -275,7 +288,8 @@ CCB_API ccbStatus ccb_run_slot_rounds(int32_t* ws, uint32_t* slots, uint32_t* ou
     if (ws == nullptr || (rounds > 0 && (slots == nullptr || out == nullptr)))
         return CCB_ERR_NULL_POINTER;
     if (!aligned(ws, CCB_LINE_BYTES) || rounds < 0 || nGrid < 1 || !valid_threads(threads) ||
-        usedCores < 0 || usedCores > nGrid || wgsPerCu < 0 || !valid_mode(mode))
+        usedCores < 0 || usedCores > nGrid || wgsPerCu < 0 || !valid_mode(mode) ||
+        !counts_fit(rounds, usedCores != 0 ? usedCores : nGrid, mode))
         return CCB_ERR_INVALID_VALUE;
     ccb::LaunchShape ls;
     ccbStatus st = plan_persistent(ccb::KernelId::SlotRounds, mode, nGrid, threads, wgsPerCu,
@@ -294,7 +308,8 @@ CCB_API ccbStatus ccb_run_grouped_rounds(int32_t* ws, uint32_t* slots, uint32_t*
     if (ws == nullptr || (rounds > 0 && (slots == nullptr || out == nullptr)))
         return CCB_ERR_NULL_POINTER;
     if (!aligned(ws, CCB_LINE_BYTES) || rounds < 0 || nGrid < 2 || (nGrid % 2) != 0 ||
-        !valid_threads(threads) || wgsPerCu < 0 || !valid_mode(mode))
+        !valid_threads(threads) || wgsPerCu < 0 || !valid_mode(mode) ||
+        !counts_fit(((int64_t)rounds + 2) / 3, nGrid, mode))  // the mix counter fills first
         return CCB_ERR_INVALID_VALUE;
     ccb::LaunchShape ls;
     ccbStatus st = plan_persistent(ccb::KernelId::GroupedRounds, mode, nGrid, threads, wgsPerCu,
@@ -324,7 +339,8 @@ CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32
     if (needHalo && halo == nullptr) return CCB_ERR_NULL_POINTER;
     if (n < 1 || iters < 0 || !aligned(ws, CCB_LINE_BYTES) || !aligned(bufA, 16) ||
         !aligned(bufB, 16) || nGrid < 1 || !valid_threads(threads) || wgsPerCu < 0 ||
-        !valid_mode(mode) || (halo != nullptr && !aligned(halo, 4)))
+        !valid_mode(mode) || (halo != nullptr && !aligned(halo, 4)) ||
+        !counts_fit((int64_t)iters - 1, nGrid, mode))
         return CCB_ERR_INVALID_VALUE;
     if (needHalo && haloBytes < ccb_stencil_halo_bytes(n, threads, nGrid)) return CCB_ERR_INVALID_VALUE;
     const uintptr_t a0 = (uintptr_t)bufA, a1 = a0 + (uintptr_t)n * 4;

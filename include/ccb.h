@@ -131,7 +131,10 @@ CCB_API ccbStatus ccb_device_info(int32_t* numCUs, int32_t* ldsPerCU, int32_t* w
  * Every stripe must be zero (or a multiple of its participant count) when a
  * launch starts ([SYNCALL] §4.1); ccb_syncall_workspace_reset zeroes the
  * workspace.  A stripe stays valid while the number of arrivals on it since
- * the last reset plus the participant count stays below 2^31.
+ * the last reset plus the participant count stays below 2^31; the launchers
+ * below return CCB_ERR_INVALID_VALUE for a launch that would break this when
+ * started from a zeroed workspace (striped: ceil(N / CCB_STRIPES) arrivals
+ * per stripe and barrier; FLAT: N).
  *
  * Every workload launcher below runs one persistent grid in which each
  * workgroup is resident for the whole launch ([SYNCALL] §6.3: the

@@ -126,6 +126,16 @@ def test_validation_before_device_work(ccb):
     assert ccb.ccb_run_stencil(4096, 8192, 10, 1, 128, None, 0, 1, 64) == ccb.CCB_ERR_NULL_POINTER
     assert ccb.ccb_run_stencil(4096, 8192, 10, 1, 128, 512, 8, 1, 64) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_run_barrier_only(128, None, None, 1, 8, 64, mode=9) == ccb.CCB_ERR_INVALID_VALUE
+    # int32 stripes: (barriers + 1) * arrivals per stripe and barrier must stay below 2^31
+    big = 2**31 // 4  # 256 members: 4 per stripe striped, 256 flat
+    assert ccb.ccb_run_barrier_only(128, None, None, big, 256, 64) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_barrier_only(128, None, None, 2**31 // 256, 256, 64,
+                                    mode=ccb.CCB_BARRIER_FLAT) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_slot_rounds(128, 256, 256, None, 0, big, 256, 64) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_grouped_rounds(128, 256, 256, None, 0, 3 * (2**31 // 8), 512, 64) \
+        == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_stencil(4096, 8192, 10, big + 1, 128, 512, 2**20, 256, 64) \
+        == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_bench_atomic_chain(None, 256, 1) == ccb.CCB_ERR_NULL_POINTER
     assert ccb.ccb_bench_atomic_chain(128, 256, 0) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_bench_copy(256, 512, 17) == ccb.CCB_ERR_INVALID_VALUE
