@@ -512,7 +512,9 @@ CCB_API ccbStatus ccb_cnt_notify_batch(const uint32_t* val, const uint8_t* meta,
                                        uint8_t* rel, int32_t nRelRows, int32_t* err,
                                        ccbStream stream)
 {
-    if (nCounters < 0 || nOps < 0 || nRelRows < 0) return CCB_ERR_INVALID_VALUE;
+    // one counter per thread at most 256 per workgroup: the grid holds < 2^31 workgroups
+    if (nCounters < 0 || nOps < 0 || nRelRows < 0 || nCounters > CCB_CNT_BATCH_MAX_COUNTERS)
+        return CCB_ERR_INVALID_VALUE;
     if (nCounters == 0) return CCB_OK;
     if (final_ == nullptr) return CCB_ERR_NULL_POINTER;
     if (nOps > 0 && (val == nullptr || meta == nullptr)) return CCB_ERR_NULL_POINTER;

@@ -76,5 +76,48 @@ def cnt_batch_input(seed: int, n_counters: int, n_ops: int, wait_every: int = 8,
     return np.ascontiguousarray(val), np.ascontiguousarray(meta), n_rel_rows
 
 
+# --- device-drawn inputs for sizes beyond a few GiB -------------------------
+# The same recipes drawn by torch's generator on the device, where numpy would
+# take minutes; seeded, so the same call gives the same tensor.
+
+def stencil_input_device(seed: int, n: int, device="cuda", hi: int = 1 << 20):
+    """int32 tensor of n values uniform in [0, hi), on the device."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randint(0, hi, (n,), generator=g, device=device, dtype=torch.int32)
+
+
+def cnt_batch_input_device(seed: int, n_counters: int, n_ops: int, device="cuda",
+                           wait_every: int = 8):
+    """cnt_batch_input's recipe (without small_values) as device tensors:
+    (val int32 bit patterns [n_ops, n_counters], meta uint8, wait rows)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    shape = (n_ops, n_counters)
+    k = torch.arange(n_ops, device=device)[:, None]
+    is_wait = ((k % wait_every) == (wait_every - 1)).expand(shape)
+    rec = torch.as_tensor(RECORD_CODES, device=device)
+    wt = torch.as_tensor(WAIT_CODES, device=device)
+    rec_mode = rec[torch.randint(0, len(RECORD_CODES), shape, generator=g, device=device,
+                                 dtype=torch.int32)]
+    wait_mode = wt[torch.randint(0, len(WAIT_CODES), shape, generator=g, device=device,
+                                 dtype=torch.int32)]
+    mode = torch.where(is_wait, wait_mode, rec_mode)
+    del rec_mode, wait_mode
+    is_clear = is_wait & (torch.randint(0, 2, shape, generator=g, device=device,
+                                        dtype=torch.uint8) == 1)
+    val = torch.randint(0, 256, (n_ops, n_counters * 4), generator=g, device=device,
+                        dtype=torch.uint8).view(torch.int32)
+    add_vals = torch.randint(0, 16, shape, generator=g, device=device, dtype=torch.int32)
+    val = torch.where((~is_wait) & (mode == ADD_CODE), add_vals, val)
+    del add_vals
+    meta = (mode | (is_clear.to(torch.uint8) << META_CLEAR_SHIFT)
+            | (is_wait.to(torch.uint8) * META_WAIT_BIT)).to(torch.uint8)
+    n_rel_rows = int(((np.arange(n_ops) % wait_every) == (wait_every - 1)).sum())
+    return val.contiguous(), meta.contiguous(), n_rel_rows
+
+
 def sha256(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()

@@ -391,7 +391,9 @@ CCB_API ccbStatus ccb_cnt_notify_query(ccbCntNotify h, uint32_t* value, ccbStatu
  * row, and sets *err (device int32, may be NULL) to CCB_ERR_INVALID_VALUE;
  * *err is not written otherwise, so the caller zeroes it first.
  * val, final must be 4-B aligned; nCounters * nOps may be 0.
- * Errors: NULL_POINTER, INVALID_VALUE (negative sizes). */
+ * Errors: NULL_POINTER, INVALID_VALUE (negative sizes, or nCounters above
+ * CCB_CNT_BATCH_MAX_COUNTERS). */
+#define CCB_CNT_BATCH_MAX_COUNTERS (((int64_t)1 << 31) * 256 - 256)
 CCB_API ccbStatus ccb_cnt_notify_batch(const uint32_t* val, const uint8_t* meta,
                                        int64_t nCounters, int32_t nOps, uint32_t* final_,
                                        uint8_t* rel, int32_t nRelRows, int32_t* err,

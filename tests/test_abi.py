@@ -141,6 +141,8 @@ def test_validation_before_device_work(ccb):
     assert ccb.ccb_bench_copy(256, 512, 17) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_cnt_notify_batch(None, None, -1, 1, None, None, 1) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_cnt_notify_batch(None, None, 0, 1, None, None, 1) == ccb.CCB_OK
+    # one workgroup of 256 threads per 256 counters, fewer than 2^31 workgroups
+    assert ccb.ccb_cnt_notify_batch(256, 256, 2**39, 1, 256, 256, 1) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_cnt_notify_batch(None, None, 4, 1, 256, 256, 1) == ccb.CCB_ERR_NULL_POINTER
 
 
