@@ -81,11 +81,56 @@ inline bool valid_threads(int32_t threads)
 // that nGrid workgroups fit on the device at once (SYNCALL guide §6.3).
 inline bool valid_mode(int32_t mode) { return mode >= 0 && mode <= 3; }
 
+// Waves per SIMD that a persistent kernel's SGPR allocation allows.  The
+// occupancy API counts only the kernel's own SGPRs.  On MI355X each wave also
+// holds 16 trap-handler SGPRs, out of 800 per SIMD.  Measured with a spin
+// kernel: allocations of 80 / 96 / 112 SGPRs fit 8 / 7 / 6 waves per SIMD,
+// where the API reports 8 / 8 / 7.  The allocation is read once per kernel and
+// device from HW_REG_GPR_ALLOC (SGPR_SIZE, bits 27:24, in 16-register granules
+// minus one) by a one-workgroup query launch on a private stream.
+constexpr int kSgprPerSimd = 800;
+constexpr int kTrapSgprs = 16;
+constexpr int kKernelIds = 4;
+
+struct RegQuery {
+    int32_t* buf = nullptr;       // 4 bytes of device memory, kept for the process
+    hipStream_t stream = nullptr;  // non-blocking, default priority, kept for the process
+    int8_t waves[kKernelIds][4] = {};  // 0 = not queried yet
+};
+std::mutex g_query_mu;
+RegQuery g_query[kMaxDevices];
+
+ccbStatus sgpr_waves(int dev, ccb::KernelId id, int32_t mode, int* waves)
+{
+    std::lock_guard<std::mutex> lk(g_query_mu);
+    RegQuery& q = g_query[dev];
+    int8_t& cached = q.waves[(int)id][mode];
+    if (cached == 0) {
+        if (q.buf == nullptr) {
+            if (hipMalloc(&q.buf, sizeof(int32_t)) != hipSuccess) return CCB_ERR_HIP;
+            if (hipStreamCreateWithFlags(&q.stream, hipStreamNonBlocking) != hipSuccess)
+                return CCB_ERR_HIP;
+        }
+        int32_t alloc = 0;
+        if (ccb::launch_register_query(id, mode, q.buf, q.stream) != hipSuccess ||
+            hipMemcpyAsync(&alloc, q.buf, sizeof(alloc), hipMemcpyDeviceToHost, q.stream) !=
+                hipSuccess ||
+            hipStreamSynchronize(q.stream) != hipSuccess)
+            return CCB_ERR_HIP;
+        const int sgprs = ((((uint32_t)alloc >> 24) & 0xF) + 1) * 16;
+        int w = kSgprPerSimd / (sgprs + kTrapSgprs);
+        cached = (int8_t)(w < 1 ? 1 : (w > 8 ? 8 : w));
+    }
+    *waves = cached;
+    return CCB_OK;
+}
+
 ccbStatus plan_persistent(ccb::KernelId id, int32_t mode, int32_t nGrid, int32_t threads,
                           int32_t wgsPerCu, hipStream_t stream, ccb::LaunchShape* ls)
 {
     DeviceInfo info;
-    ccbStatus st = current_device(nullptr, &info);
+    int dev = 0;
+    ccbStatus st = current_device(&dev, &info);
     if (st != CCB_OK) return st;
     const void* fn = ccb::kernel_ptr(id, mode);
     hipFuncAttributes attr;
@@ -105,6 +150,12 @@ ccbStatus plan_persistent(ccb::KernelId id, int32_t mode, int32_t nGrid, int32_t
     int perCU = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&perCU, fn, threads, lds) != hipSuccess)
         return CCB_ERR_HIP;
+    // the SGPR limit the occupancy API misses: 4 SIMDs per CU, threads / 64
+    // waves per workgroup spread over them
+    int waves = 0;
+    if ((st = sgpr_waves(dev, id, mode, &waves)) != CCB_OK) return st;
+    const int bySgpr = 4 * waves / ((threads + 63) / 64);
+    if (bySgpr < perCU) perCU = bySgpr;
     if ((long)perCU * info.numCUs < nGrid) return CCB_ERR_NOT_CORESIDENT;
     ls->fn = fn;
     ls->nGrid = nGrid;

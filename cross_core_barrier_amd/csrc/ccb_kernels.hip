@@ -57,6 +57,19 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* partial)
     return s;
 }
 
+// Register query of a persistent kernel: a launch with maxPoll == 0 (a real
+// launch never has it: the API turns 0 into the default bound) stores the
+// HW_REG_GPR_ALLOC value of the kernel's waves in *out (thread 0 of
+// workgroup 0) and returns at once in every thread.  The launcher reads the
+// SGPR allocation from it to check co-residency.
+__device__ __forceinline__ bool register_query(uint32_t maxPoll, int32_t* out)
+{
+    if (maxPoll != 0) return false;
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        *out = (int32_t)__builtin_amdgcn_s_getreg((31 << 11) | 5);  // HW_REG_GPR_ALLOC
+    return true;
+}
+
 __device__ __forceinline__ void record_placement(uint32_t* placement)
 {
     if (placement != nullptr && leader()) {
@@ -101,6 +114,7 @@ __global__ __launch_bounds__(1024) void ccb_k_barrier_only(int32_t* ws, uint32_t
                                                             int32_t nMembers, uint32_t maxPoll)
 {
     __shared__ int32_t result[2];
+    if (register_query(maxPoll, ws)) return;
     record_placement(placement);
     const int32_t w = blockIdx.x;
     if (w >= nMembers) {
@@ -305,6 +319,7 @@ __global__ __launch_bounds__(1024) void ccb_k_slot_rounds(int32_t* ws, uint32_t*
                                                            int32_t nMembers, uint32_t maxPoll)
 {
     __shared__ uint32_t partial[1024 / kWave];
+    if (register_query(maxPoll, ws)) return;
     const int32_t w = blockIdx.x;
     const int32_t nGrid = gridDim.x;
     if (w >= nMembers) {
@@ -366,6 +381,7 @@ __global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32
                                                               uint32_t maxPoll)
 {
     __shared__ uint32_t partial[1024 / kWave];
+    if (register_query(maxPoll, ws)) return;
     const int32_t w = blockIdx.x;
     const int32_t nGrid = gridDim.x;
     const int32_t half = nGrid / 2;
@@ -640,6 +656,7 @@ __global__ __launch_bounds__(1024) void ccb_k_stencil(int32_t* bufA, int32_t* bu
 {
     __shared__ int32_t inLeft[kHaloLds], inRight[kHaloLds];   // neighbours of my chunks
     __shared__ int32_t outFirst[kHaloLds], outLast[kHaloLds]; // my chunks' end outputs
+    if (register_query(maxPoll, ws)) return;
     StencilGeom g;
     g.n = n;
     g.chunk = 4 * (int64_t)blockDim.x;
@@ -1094,6 +1111,35 @@ hipError_t launch_stencil(const LaunchShape& ls, int32_t* bufA, int32_t* bufB, i
 {
     void* args[] = {&bufA, &bufB, &n, &iters, &ws, &halo, &timeline, &maxPoll};
     return coop(ls.fn, ls.nGrid, ls.threads, ls.lds, ls.stream, args);
+}
+
+hipError_t launch_register_query(KernelId id, int32_t mode, int32_t* out, hipStream_t s)
+{
+    const void* fn = kernel_ptr(id, mode);
+    void* none = nullptr;
+    int64_t zero64 = 0;
+    int32_t zero = 0;
+    uint64_t seed = 0;
+    uint32_t query = 0;  // maxPoll == 0: the register query
+    switch (id) {
+    case KernelId::BarrierOnly: {
+        void* args[] = {&out, &none, &none, &zero, &zero, &query};
+        return hipLaunchKernel(fn, dim3(1), dim3(kWave), args, 0, s);
+    }
+    case KernelId::SlotRounds: {
+        void* args[] = {&out, &none, &none, &none, &seed, &zero, &zero, &query};
+        return hipLaunchKernel(fn, dim3(1), dim3(kWave), args, 0, s);
+    }
+    case KernelId::GroupedRounds: {
+        void* args[] = {&out, &none, &none, &none, &seed, &zero, &query};
+        return hipLaunchKernel(fn, dim3(1), dim3(kWave), args, 0, s);
+    }
+    case KernelId::Stencil: {
+        void* args[] = {&none, &none, &zero64, &zero, &out, &none, &none, &query};
+        return hipLaunchKernel(fn, dim3(1), dim3(kWave), args, 0, s);
+    }
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_cnt_batch(const uint32_t* val, const uint8_t* meta, int64_t nCounters,

@@ -140,7 +140,13 @@ CCB_API ccbStatus ccb_device_info(int32_t* numCUs, int32_t* ldsPerCU, int32_t* w
  * workgroup is resident for the whole launch ([SYNCALL] §6.3: the
  * participant set is fixed by the launch).  The launcher checks the
  * occupancy first and returns CCB_ERR_NOT_CORESIDENT when nGrid workgroups of
- * `threads` threads cannot all be resident at once.  `wgsPerCu` > 0 also
+ * `threads` threads cannot all be resident at once: the smaller of the
+ * occupancy API's count and the count the kernel's SGPRs allow, at 800 SGPRs
+ * per SIMD and 16 trap-handler SGPRs per wave beyond the kernel's own
+ * allocation (which the API leaves out).  The first launch of each kernel
+ * variant on a device reads that allocation once with a one-workgroup query
+ * launch on a private stream (4 bytes of device memory, kept, and a host
+ * wait for that launch only).  `wgsPerCu` > 0 also
  * sizes each workgroup's LDS so that at most that many share a compute unit
  * (0 = no shaping).  `maxPoll` bounds each barrier's poll loop (0 = the
  * default CCB_SOFT_MAX_POLL); a member that exhausts it sets the error word

@@ -95,6 +95,66 @@ def test_slot_rounds_grid_full(wl, used, mode):
     np.testing.assert_array_equal(_u32(res.out), want_out)
 
 
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_slot_rounds_largest_coresident_grid(ccb, wl, mode):
+    """The largest grid of 64-thread workgroups that the launcher accepts
+    (found by bisection: a refused size launches nothing) runs the witness
+    rounds bit-exactly, and one workgroup more is refused."""
+    n_cu = ccb.ccb_device_info()[1]
+    lo, hi = 1, n_cu * 64  # hi: more than any CU holds
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        st = wl.slot_rounds(20, 1, mid, 64, check_launch=False, mode=mode).status
+        assert st in (ccb.CCB_OK, ccb.CCB_ERR_NOT_CORESIDENT)
+        if st == ccb.CCB_OK:
+            lo = mid
+        else:
+            hi = mid
+    _say(f"slot_rounds largest grid {lo}x64 rounds=20 mode={mode}")
+    assert lo >= n_cu * 8
+    res = wl.slot_rounds(20, 20, lo, 64, mode=mode)
+    want_out, want_status, want_ctr, rc = _oracle_slot(20, 20, lo, 0)
+    assert rc == 0 and res.status == 0
+    assert res.counters == [want_ctr] == [20 * lo]
+    np.testing.assert_array_equal(res.wg_status.cpu().numpy(), want_status)
+    np.testing.assert_array_equal(_u32(res.out), want_out)
+    assert wl.slot_rounds(20, 20, lo + 1, 64, check_launch=False, mode=mode).status == \
+        ccb.CCB_ERR_NOT_CORESIDENT
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_grouped_largest_coresident_grid(ccb, wl, mode):
+    """As above for the grouped rounds (even grids of 64-thread workgroups)."""
+    n_cu = ccb.ccb_device_info()[1]
+    lo, hi = 1, n_cu * 32  # in pairs of workgroups
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        ws = wl.workspace(3)
+        slots = torch.zeros(ccb.CCB_SLOT_ROWS * ccb.CCB_SLOT_WORDS * 2 * mid, dtype=torch.int32,
+                            device="cuda")
+        out = torch.zeros(2 * mid, dtype=torch.int32, device="cuda")
+        st = ccb.ccb_run_grouped_rounds(ws, slots, out, None, 4, 1, 2 * mid, 64, 0, 0, mode, None)
+        assert st in (ccb.CCB_OK, ccb.CCB_ERR_NOT_CORESIDENT)
+        if st == ccb.CCB_OK:
+            assert ccb.ccb_syncall_status(ws, 3, None)[0] == ccb.CCB_OK
+            lo = mid
+        else:
+            hi = mid
+    n_grid = 2 * lo
+    _say(f"grouped largest grid {n_grid}x64 rounds=30 mode={mode}")
+    res = wl.grouped_rounds(4, 30, n_grid, 64, mode=mode)
+    want_out, want_status, want_ctrs, rc = _oracle_grouped(4, 30, n_grid)
+    assert rc == 0 and res.status == 0
+    assert tuple(res.counters) == want_ctrs
+    np.testing.assert_array_equal(_u32(res.out), want_out)
+    ws = wl.workspace(3)
+    slots = torch.zeros(ccb.CCB_SLOT_ROWS * ccb.CCB_SLOT_WORDS * (n_grid + 2), dtype=torch.int32,
+                        device="cuda")
+    out = torch.zeros(n_grid + 2, dtype=torch.int32, device="cuda")
+    assert ccb.ccb_run_grouped_rounds(ws, slots, out, None, 4, 1, n_grid + 2, 64, 0, 0, mode,
+                                      None) == ccb.CCB_ERR_NOT_CORESIDENT
+
+
 # --- grouped rounds -----------------------------------------------------------
 
 @pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)

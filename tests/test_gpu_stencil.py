@@ -74,6 +74,38 @@ def test_stencil_full(wl, mode):
     np.testing.assert_array_equal(y.cpu().numpy(), _full_cache["want"])
 
 
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_stencil_largest_coresident_grid(wl, mode):
+    """1024-thread workgroups: the largest grid the launcher accepts (found by
+    bisection; a refused size launches nothing) runs bit-exactly, and one
+    workgroup more is refused."""
+    from cross_core_barrier_amd import ccb
+    a = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    b = torch.zeros_like(a)
+    lo, hi = 1, 256 * 64
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        ws = wl.workspace(1)
+        halo = wl.halo_scratch(1024, 1024, mid)
+        st = ccb.ccb_run_stencil(a, b, 1024, 1, ws, halo, None, mid, 1024, 0, 0, mode, None)
+        assert st in (ccb.CCB_OK, ccb.CCB_ERR_NOT_CORESIDENT)
+        torch.cuda.synchronize()
+        if st == ccb.CCB_OK:
+            lo = mid
+        else:
+            hi = mid
+    n, iters = 4096 * lo * 2 + 3, 3
+    _say(f"stencil largest grid {lo}x1024 n={n} iters={iters} mode={mode}")
+    x = inputs.stencil_input(21, n)
+    st, y = wl.stencil(torch.from_numpy(x).cuda(), iters, lo, 1024, mode=mode)
+    assert st == 0
+    np.testing.assert_array_equal(y.cpu().numpy(), oracle.stencil(x, iters))
+    ws = wl.workspace(1)
+    halo = wl.halo_scratch(1024, 1024, lo + 1)
+    assert ccb.ccb_run_stencil(a, b, 1024, 1, ws, halo, None, lo + 1, 1024, 0, 0, mode, None) \
+        == ccb.CCB_ERR_NOT_CORESIDENT
+
+
 def test_stencil_invalid(wl):
     from cross_core_barrier_amd import ccb
     a = torch.zeros(1024, dtype=torch.int32, device="cuda")
