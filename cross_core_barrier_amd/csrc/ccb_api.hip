@@ -93,7 +93,7 @@ constexpr int kTrapSgprs = 16;
 constexpr int kKernelIds = 4;
 
 struct RegQuery {
-    int32_t* buf = nullptr;       // 4 bytes of device memory, kept for the process
+    int32_t* buf = nullptr;        // the library's query word on this device
     hipStream_t stream = nullptr;  // non-blocking, default priority, kept for the process
     int8_t waves[kKernelIds][4] = {};  // 0 = not queried yet
 };
@@ -107,7 +107,7 @@ ccbStatus sgpr_waves(int dev, ccb::KernelId id, int32_t mode, int* waves)
     int8_t& cached = q.waves[(int)id][mode];
     if (cached == 0) {
         if (q.buf == nullptr) {
-            if (hipMalloc(&q.buf, sizeof(int32_t)) != hipSuccess) return CCB_ERR_HIP;
+            if (ccb::register_query_word(&q.buf) != hipSuccess) return CCB_ERR_HIP;
             if (hipStreamCreateWithFlags(&q.stream, hipStreamNonBlocking) != hipSuccess)
                 return CCB_ERR_HIP;
         }

@@ -31,6 +31,8 @@ const void* kernel_ptr(KernelId id, int32_t mode);
 
 // One workgroup of the kernel stores its waves' HW_REG_GPR_ALLOC in *out.
 hipError_t launch_register_query(KernelId id, int32_t mode, int32_t* out, hipStream_t s);
+// Device address (on the current device) of the word the query writes.
+hipError_t register_query_word(int32_t** out);
 
 hipError_t launch_barrier_only(const LaunchShape& ls, int32_t* ws, uint32_t* placement,
                                int32_t* wgStatus, int32_t rounds, int32_t nMembers,

@@ -1113,6 +1113,15 @@ hipError_t launch_stencil(const LaunchShape& ls, int32_t* bufA, int32_t* bufB, i
     return coop(ls.fn, ls.nGrid, ls.threads, ls.lds, ls.stream, args);
 }
 
+// Where the register query stores its answer: one word per device, so that
+// the query needs no allocation.
+__device__ __align__(128) int32_t g_register_query[32];
+
+hipError_t register_query_word(int32_t** out)
+{
+    return hipGetSymbolAddress(reinterpret_cast<void**>(out), HIP_SYMBOL(g_register_query));
+}
+
 hipError_t launch_register_query(KernelId id, int32_t mode, int32_t* out, hipStream_t s)
 {
     const void* fn = kernel_ptr(id, mode);
