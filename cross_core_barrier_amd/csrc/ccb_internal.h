@@ -14,7 +14,7 @@ namespace ccb {
 constexpr bool kStencilNT = false;
 constexpr bool kStencilNTLoad = true;
 constexpr int kCntPerThread = 2;   // adjacent counters per thread in the batch engine (2 or 4)
-constexpr int kCntUnroll = 2;      // ops loaded ahead per thread in the batch engine
+constexpr int kCntUnroll = 1;      // ops per register set in the batch engine's two-set pipeline
 constexpr bool kCntNTLoad = true;   // non-temporal loads of the op stream (read once)
 
 enum class KernelId { BarrierOnly, SlotRounds, GroupedRounds, Stencil };

@@ -796,6 +796,54 @@ __device__ __forceinline__ bool cnt_step(uint32_t& c, uint32_t m, uint32_t v, bo
     return false;
 }
 
+// A record op in the form the fast path below uses: with the code clamped to
+// t <= 31, the new count is (c & X) + (v & Y), X = (v & A) ^ B, where A, B
+// and Y are bit t of three tables, sign-extended to 0 or ~0:
+//   SET (0): A = 0,  B = 0,  Y = ~0  ->  v
+//   ADD (1): A = 0,  B = ~0, Y = ~0  ->  c + v
+//   OR  (2): A = ~0, B = ~0, Y = ~0  ->  (c & ~v) + v = c | v
+//   AND (4): A = ~0, B = 0,  Y = 0   ->  c & v
+// and every other code (3, 5-7, or a clear or reserved bit set, which
+// clamps to a code of 8 or more) A = 0, B = ~0, Y = 0: the count is kept.
+// seen collects 1 << t, so that a code outside {0, 1, 2, 4} is reported
+// once at the end instead of being tested on every op.
+constexpr uint32_t kRecA = 0x14u, kRecB = 0xFFFFFFEEu, kRecY = 0x07u, kRecValid = 0x17u;
+
+__device__ __forceinline__ uint32_t cnt_record_fast(uint32_t c, uint32_t b, uint32_t v,
+                                                    uint32_t& seen)
+{
+    const uint32_t t = b < 31u ? b : 31u;
+    const uint32_t a = (uint32_t)__builtin_amdgcn_sbfe((int)kRecA, t, 1u);
+    const uint32_t bb = (uint32_t)__builtin_amdgcn_sbfe((int)kRecB, t, 1u);
+    const uint32_t y = (uint32_t)__builtin_amdgcn_sbfe((int)kRecY, t, 1u);
+    seen |= 1u << t;
+    return (c & ((v & a) ^ bb)) + (v & y);
+}
+
+// A wait op in the form the fast path below uses.  With
+// r = (c < v) | (c == v) << 1 | ((c & v) == v) << 2, the predicate of wait
+// code m is bit m * 8 + r of kWaitTable (LESS 0: r & 1; EQUAL 1: r & 2;
+// BIGGER 2: r & 3 == 0; GE 3: r & 1 == 0; BITMASK 4: r & 4).  A code above 4
+// or a reserved bit (clamped to 5) indexes zero bits: never released.
+// seen collects 1 << code for the validity check at the end; rowOk (the same
+// in every lane) says whether the wait has an output row.
+constexpr uint64_t kWaitTable =
+    0xAAull | (0xCCull << 8) | (0x11ull << 16) | (0x55ull << 24) | (0xF0ull << 32);
+constexpr uint32_t kWaitValid = 0x1Fu;
+
+__device__ __forceinline__ uint32_t cnt_wait_fast(uint32_t& c, uint32_t b, uint32_t v,
+                                                  bool rowOk, uint32_t& seen)
+{
+    const uint32_t mode = b & 0x77u;  // wait code and reserved bits
+    const uint32_t mc = mode < 5u ? mode : 5u;
+    const uint32_t r = (c < v ? 1u : 0u) | (c == v ? 2u : 0u) | ((c & v) == v ? 4u : 0u);
+    const uint32_t rel = rowOk ? (uint32_t)(kWaitTable >> (mc * 8u + r)) & 1u : 0u;
+    seen |= 1u << (mode < 31u ? mode : 31u);
+    // the clear follows the release (CntNotify interfaces §3.3, §7)
+    c = (rel & (b >> 3)) != 0 ? 0u : c;
+    return rel;
+}
+
 }  // namespace
 
 // C adjacent counters per thread (C = 2 or 4): C-byte meta loads and
@@ -827,7 +875,35 @@ __global__ __launch_bounds__(256) void ccb_k_cnt_batch(const uint32_t* __restric
 #pragma unroll
     for (int i = 0; i < C; ++i) c[i] = 0u, j[i] = 0;
     bool bad = false;
+    uint32_t seen[C], seenW[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) seen[i] = 1u, seenW[i] = 1u;
+    constexpr uint32_t kWaitBits = C == 4 ? 0x80808080u : 0x8080u;
     auto apply = [&](uint32_t m, VT v) {
+        const uint32_t waits = m & kWaitBits;
+        if (!__any(waits != 0)) {
+            // no wait in this op anywhere in the wave: records only
+#pragma unroll
+            for (int i = 0; i < C; ++i) c[i] = cnt_record_fast(c[i], (m >> (8 * i)) & 0xffu, v[i], seen[i]);
+            return;
+        }
+        bool oneRow = true;
+#pragma unroll
+        for (int i = 1; i < C; ++i) oneRow = oneRow && j[i] == j[0];
+        const int32_t jr = __builtin_amdgcn_readfirstlane(j[0]);
+        if (__all(waits == kWaitBits && oneRow && j[0] == jr)) {
+            // every counter of the wave waits, all on output row jr
+            const bool rowOk = jr < nRelRows;
+            uint32_t packed = 0;
+#pragma unroll
+            for (int i = 0; i < C; ++i)
+                packed |= cnt_wait_fast(c[i], (m >> (8 * i)) & 0xffu, v[i], rowOk, seenW[i]) << (8 * i);
+            if (rowOk) *reinterpret_cast<MT*>(rel + (int64_t)jr * nCounters + c0) = (MT)packed;
+            else bad = true;
+#pragma unroll
+            for (int i = 0; i < C; ++i) j[i]++;
+            return;
+        }
         uint8_t f[C];
         bool w[C];
         bool allWait = true, sameRow = true;
@@ -865,14 +941,32 @@ __global__ __launch_bounds__(256) void ccb_k_cnt_batch(const uint32_t* __restric
             v = *vp;
         }
     };
+    // Two register sets of U ops, A and B: one set's loads are in flight
+    // while the other set is applied, so the vector ALU work of an op
+    // overlaps the memory latency of the next.
     int32_t k = 0;
-    for (; k + U <= nOps; k += U) {
-        uint32_t m[U];
-        VT v[U];
+    uint32_t mA[U], mB[U];
+    VT vA[U], vB[U];
+    if (k + U <= nOps) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) load(k + u, m[u], v[u]);
+        for (int u = 0; u < U; ++u) load(k + u, mA[u], vA[u]);
+    }
+    for (; k + 2 * U <= nOps; k += 2 * U) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) apply(m[u], v[u]);
+        for (int u = 0; u < U; ++u) load(k + U + u, mB[u], vB[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) apply(mA[u], vA[u]);
+        if (k + 3 * U <= nOps) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) load(k + 2 * U + u, mA[u], vA[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) apply(mB[u], vB[u]);
+    }
+    if (k + U <= nOps) {  // set A holds ops k .. k + U - 1
+#pragma unroll
+        for (int u = 0; u < U; ++u) apply(mA[u], vA[u]);
+        k += U;
     }
     for (; k < nOps; ++k) {
         uint32_t m;
@@ -882,7 +976,10 @@ __global__ __launch_bounds__(256) void ccb_k_cnt_batch(const uint32_t* __restric
     }
     VT out;
 #pragma unroll
-    for (int i = 0; i < C; ++i) out[i] = c[i];
+    for (int i = 0; i < C; ++i) {
+        out[i] = c[i];
+        bad = bad || (seen[i] & ~kRecValid) != 0 || (seenW[i] & ~kWaitValid) != 0;
+    }
     *reinterpret_cast<VT*>(finalOut + c0) = out;
     if (bad && err != nullptr)
         __hip_atomic_store(err, (int32_t)CCB_ERR_INVALID_VALUE, __ATOMIC_RELAXED,

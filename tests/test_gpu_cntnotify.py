@@ -81,6 +81,25 @@ def test_batch_malformed(wl, n_counters):
     np.testing.assert_array_equal(rel, r2)
 
 
+@pytest.mark.parametrize("n_counters", [4096, 4098])
+def test_batch_malformed_in_uniform_rows(wl, n_counters):
+    """Random op bytes (any code, clear and reserved bits) in 3% of the
+    entries, keeping each op's wait bit, so that every op stays all-record or
+    all-wait across the wave and malformed ops go through those rows' paths."""
+    _say(f"cnt_batch random malformed ops in uniform rows n={n_counters}")
+    val, meta, rows = inputs.cnt_batch_input(15, n_counters, 32, small_values=True)
+    meta = meta.copy()
+    rng = np.random.default_rng(16)
+    hit = rng.random(meta.shape) < 0.03
+    junk = rng.integers(0, 128, size=meta.shape).astype(np.uint8) | (meta & 0x80)
+    meta[hit] = junk[hit]
+    err, final, rel = _run_batch(wl, val, meta, rows)
+    f2, r2, rc = oracle.cnt_batch(val, meta, rows)
+    assert rc == oracle.INVALID_VALUE and err == oracle.INVALID_VALUE
+    np.testing.assert_array_equal(final, f2)
+    np.testing.assert_array_equal(rel, r2)
+
+
 @pytest.mark.parametrize("n_counters", [4096, 4097])
 def test_batch_waits_at_different_ops(wl, n_counters):
     """Each counter has its own wait positions, so neighbouring counters
