@@ -85,17 +85,20 @@ inline bool valid_mode(int32_t mode) { return mode >= 0 && mode <= 3; }
 // occupancy API counts only the kernel's own SGPRs.  On MI355X each wave also
 // holds 16 trap-handler SGPRs, out of 800 per SIMD.  Measured with a spin
 // kernel: allocations of 80 / 96 / 112 SGPRs fit 8 / 7 / 6 waves per SIMD,
-// where the API reports 8 / 8 / 7.  The allocation is read once per kernel and
-// device from HW_REG_GPR_ALLOC (SGPR_SIZE, bits 27:24, in 16-register granules
-// minus one) by a one-workgroup query launch on a private stream.
+// where the API reports 8 / 8 / 7.  The allocations are read from
+// HW_REG_GPR_ALLOC (SGPR_SIZE, bits 27:24, in 16-register granules minus
+// one) by one-workgroup query launches of every persistent kernel variant,
+// all at the first persistent launch on a device.  They run on the default
+// stream, so the library never creates a stream (a new stream would take one
+// of the process's few hardware queues and could change how the caller's
+// streams share them); the host waits for them once.
 constexpr int kSgprPerSimd = 800;
 constexpr int kTrapSgprs = 16;
 constexpr int kKernelIds = 4;
 
 struct RegQuery {
-    int32_t* buf = nullptr;        // the library's query word on this device
-    hipStream_t stream = nullptr;  // non-blocking, default priority, kept for the process
-    int8_t waves[kKernelIds][4] = {};  // 0 = not queried yet
+    bool done = false;
+    int8_t waves[kKernelIds][4] = {};
 };
 std::mutex g_query_mu;
 RegQuery g_query[kMaxDevices];
@@ -104,24 +107,22 @@ ccbStatus sgpr_waves(int dev, ccb::KernelId id, int32_t mode, int* waves)
 {
     std::lock_guard<std::mutex> lk(g_query_mu);
     RegQuery& q = g_query[dev];
-    int8_t& cached = q.waves[(int)id][mode];
-    if (cached == 0) {
-        if (q.buf == nullptr) {
-            if (ccb::register_query_word(&q.buf) != hipSuccess) return CCB_ERR_HIP;
-            if (hipStreamCreateWithFlags(&q.stream, hipStreamNonBlocking) != hipSuccess)
-                return CCB_ERR_HIP;
-        }
-        int32_t alloc = 0;
-        if (ccb::launch_register_query(id, mode, q.buf, q.stream) != hipSuccess ||
-            hipMemcpyAsync(&alloc, q.buf, sizeof(alloc), hipMemcpyDeviceToHost, q.stream) !=
-                hipSuccess ||
-            hipStreamSynchronize(q.stream) != hipSuccess)
-            return CCB_ERR_HIP;
-        const int sgprs = ((((uint32_t)alloc >> 24) & 0xF) + 1) * 16;
-        int w = kSgprPerSimd / (sgprs + kTrapSgprs);
-        cached = (int8_t)(w < 1 ? 1 : (w > 8 ? 8 : w));
+    if (!q.done) {
+        int32_t* word = nullptr;
+        if (ccb::register_query_word(&word) != hipSuccess) return CCB_ERR_HIP;
+        for (int k = 0; k < kKernelIds; ++k)
+            for (int m = 0; m < 4; ++m) {
+                int32_t alloc = 0;
+                if (ccb::launch_register_query((ccb::KernelId)k, m, word, nullptr) != hipSuccess ||
+                    hipMemcpy(&alloc, word, sizeof(alloc), hipMemcpyDeviceToHost) != hipSuccess)
+                    return CCB_ERR_HIP;
+                const int sgprs = ((((uint32_t)alloc >> 24) & 0xF) + 1) * 16;
+                const int w = kSgprPerSimd / (sgprs + kTrapSgprs);
+                q.waves[k][m] = (int8_t)(w < 1 ? 1 : (w > 8 ? 8 : w));
+            }
+        q.done = true;
     }
-    *waves = cached;
+    *waves = q.waves[(int)id][mode];
     return CCB_OK;
 }
 

@@ -143,10 +143,10 @@ CCB_API ccbStatus ccb_device_info(int32_t* numCUs, int32_t* ldsPerCU, int32_t* w
  * `threads` threads cannot all be resident at once: the smaller of the
  * occupancy API's count and the count the kernel's SGPRs allow, at 800 SGPRs
  * per SIMD and 16 trap-handler SGPRs per wave beyond the kernel's own
- * allocation (which the API leaves out).  The first launch of each kernel
- * variant on a device reads that allocation once with a one-workgroup query
- * launch on a private stream (it allocates no memory; the host waits for that
- * launch only; make that first call outside stream capture).  `wgsPerCu` > 0 also
+ * allocation (which the API leaves out).  The first persistent launch on a
+ * device reads every kernel variant's allocation with one-workgroup query
+ * launches on the default stream and waits for them (no allocation, no new
+ * stream); make that first call outside stream capture.  `wgsPerCu` > 0 also
  * sizes each workgroup's LDS so that at most that many share a compute unit
  * (0 = no shaping).  `maxPoll` bounds each barrier's poll loop (0 = the
  * default CCB_SOFT_MAX_POLL); a member that exhausts it sets the error word
