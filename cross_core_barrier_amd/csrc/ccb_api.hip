@@ -392,6 +392,7 @@ CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32
     if (n < 1 || iters < 0 || !aligned(ws, CCB_LINE_BYTES) || !aligned(bufA, 16) ||
         !aligned(bufB, 16) || nGrid < 1 || !valid_threads(threads) || wgsPerCu < 0 ||
         !valid_mode(mode) || (halo != nullptr && !aligned(halo, 4)) ||
+        (timeline != nullptr && !aligned(timeline, 8)) ||
         !counts_fit((int64_t)iters - 1, nGrid, mode))
         return CCB_ERR_INVALID_VALUE;
     if (needHalo && haloBytes < ccb_stencil_halo_bytes(n, threads, nGrid)) return CCB_ERR_INVALID_VALUE;
@@ -402,7 +403,6 @@ CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32
     ccbStatus st = plan_persistent(ccb::KernelId::Stencil, mode, nGrid, threads, wgsPerCu,
                                    (hipStream_t)stream, &ls);
     if (st != CCB_OK) return st;
-    if (timeline != nullptr && !aligned(timeline, 8)) return CCB_ERR_INVALID_VALUE;
     return from_hip(ccb::launch_stencil(ls, bufA, bufB, n, iters, ws, halo, timeline,
                                         poll_bound(maxPoll)));
 }

@@ -125,6 +125,8 @@ def test_validation_before_device_work(ccb):
     assert ccb.ccb_run_stencil(4100, 8192, 10, 1, 128, 512, 64, 1, 64) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_run_stencil(4096, 8192, 10, 1, 128, None, 0, 1, 64) == ccb.CCB_ERR_NULL_POINTER
     assert ccb.ccb_run_stencil(4096, 8192, 10, 1, 128, 512, 8, 1, 64) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_run_stencil(4096, 8192, 10, 1, 128, 512, 64, 1, 64,
+                               timeline=4100) == ccb.CCB_ERR_INVALID_VALUE  # misaligned stamps
     assert ccb.ccb_run_barrier_only(128, None, None, 1, 8, 64, mode=9) == ccb.CCB_ERR_INVALID_VALUE
     # int32 stripes: (barriers + 1) * arrivals per stripe and barrier must stay below 2^31
     big = 2**31 // 4  # 256 members: 4 per stripe striped, 256 flat
