@@ -202,8 +202,10 @@ ccbCntNotify encode_handle(uint32_t idx, uint32_t gen)
     return reinterpret_cast<ccbCntNotify>(v);
 }
 
-// Looks a handle up; on success *line is its device line.
-ccbStatus resolve(ccbCntNotify h, uint32_t* idxOut, uint32_t** line)
+// Looks a handle up; on success *line is its device line.  `kill` also marks
+// the slot free, under the same lock as the check, so that of two concurrent
+// destroys of one handle only one succeeds.
+ccbStatus resolve(ccbCntNotify h, uint32_t* idxOut, uint32_t** line, bool kill = false)
 {
     const uintptr_t v = reinterpret_cast<uintptr_t>(h);
     if (v == 0) return CCB_ERR_INVALID_HANDLE;
@@ -212,11 +214,12 @@ ccbStatus resolve(ccbCntNotify h, uint32_t* idxOut, uint32_t** line)
     if (idx1 == 0 || idx1 > CCB_CNT_NOTIFY_POOL) return CCB_ERR_INVALID_HANDLE;
     const uint32_t idx = (uint32_t)(idx1 - 1);
     std::lock_guard<std::mutex> lk(g_cnt_mu);
-    const CntSlot& s = g_cnt[idx];
+    CntSlot& s = g_cnt[idx];
     if (!s.alive || s.gen != gen) return CCB_ERR_INVALID_HANDLE;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return CCB_ERR_HIP;
     if (dev != s.device) return CCB_ERR_INVALID_HANDLE;
+    if (kill) s.alive = false;
     if (idxOut) *idxOut = idx;
     if (line) *line = g_cnt_pool[s.device] + (size_t)idx * kLineWords;
     return CCB_OK;
@@ -536,12 +539,7 @@ CCB_API ccbStatus ccb_cnt_notify_get_id(ccbCntNotify h, uint32_t* id)
 
 CCB_API ccbStatus ccb_cnt_notify_destroy(ccbCntNotify h)
 {
-    uint32_t idx = 0;
-    ccbStatus st = resolve(h, &idx, nullptr);
-    if (st != CCB_OK) return st;
-    std::lock_guard<std::mutex> lk(g_cnt_mu);
-    g_cnt[idx].alive = false;
-    return CCB_OK;
+    return resolve(h, nullptr, nullptr, true);
 }
 
 CCB_API ccbStatus ccb_cnt_notify_query(ccbCntNotify h, uint32_t* value, ccbStatus* lastWait,

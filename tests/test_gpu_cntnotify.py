@@ -270,3 +270,48 @@ def test_handle_errors_and_pool(ccb):
     hs[5] = again
     for x in hs:
         assert ccb.ccb_cnt_notify_destroy(x) == 0
+
+
+def test_handle_table_under_threads(ccb):
+    """The handle table is shared by host threads ([CNTNOTIFY] §6.1: a handle
+    is either valid or an error): threads that create at once get distinct
+    lines, and of threads that destroy one handle at once exactly one
+    succeeds."""
+    import threading
+    _say("cntnotify handle table from 8 host threads")
+    torch.cuda.init()
+    made, lock = [], threading.Lock()
+
+    def create(k):
+        torch.cuda.set_device(0)
+        for _ in range(k):
+            st, h = ccb.ccb_cnt_notify_create(0)
+            assert st == 0
+            with lock:
+                made.append(h)
+
+    ts = [threading.Thread(target=create, args=(64,)) for _ in range(8)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert len(made) == 512
+    assert len({ccb.ccb_cnt_notify_get_id(h)[1] for h in made}) == 512
+    outcomes = []
+    go = threading.Barrier(8)
+
+    def destroy(h):
+        torch.cuda.set_device(0)
+        go.wait()
+        outcomes.append(ccb.ccb_cnt_notify_destroy(h))
+
+    for h in made[:16]:
+        outcomes.clear()
+        ts = [threading.Thread(target=destroy, args=(h,)) for _ in range(8)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        assert sorted(outcomes) == [0] + [ccb.CCB_ERR_INVALID_HANDLE] * 7
+    for h in made[16:]:
+        assert ccb.ccb_cnt_notify_destroy(h) == 0
