@@ -349,7 +349,11 @@ CCB_API ccbStatus ccb_cnt_notify_record(ccbCntNotify h, ccbStream stream,
  * is released and isClear is 1 the count is set to 0 atomically with the
  * check that released it (a concurrent record is never lost).  The outcome
  * (CCB_OK or CCB_ERR_TIMEOUT) is stored with the handle; read it with
- * ccb_cnt_notify_query.  A timed-out wait does not clear.
+ * ccb_cnt_notify_query.  A timed-out wait does not clear.  The wait is a
+ * one-lane polling kernel: streams share a few hardware queues, and a queue
+ * runs its kernels in order, so enqueue the records a wait depends on before
+ * the wait (or give the wait a timeout); a record queued behind a wait with
+ * no limit on the same hardware queue can never run.
  * Errors: INVALID_HANDLE, NULL_POINTER (info), INVALID_VALUE (mode,
  * isClear > 1, rev not zero). */
 CCB_API ccbStatus ccb_cnt_notify_wait(ccbCntNotify h, ccbStream stream,

@@ -315,3 +315,18 @@ def test_handle_table_under_threads(ccb):
         assert sorted(outcomes) == [0] + [ccb.CCB_ERR_INVALID_HANDLE] * 7
     for h in made[16:]:
         assert ccb.ccb_cnt_notify_destroy(h) == 0
+
+
+def test_wait_without_limit_already_satisfied(ccb):
+    """timeout 0 means no limit ([CNTNOTIFY] §4.3); a wait whose predicate
+    already holds when it starts is released at once, with its clear.  (The
+    record is complete before the wait is enqueued, so the wait cannot be
+    left waiting.)"""
+    _say("cntnotify wait with no time limit, predicate already true")
+    h = _mk(ccb)
+    s = torch.cuda.Stream()
+    assert ccb.ccb_cnt_notify_record(h, s, ccb.record_info(ccb.CCB_CNT_RECORD_SET_VALUE, 5)) == 0
+    torch.cuda.synchronize()
+    assert ccb.ccb_cnt_notify_wait(h, s, ccb.wait_info(ccb.CCB_CNT_WAIT_EQUAL, 5, 0, 1)) == 0
+    assert ccb.ccb_cnt_notify_query(h, s) == (0, 0, ccb.CCB_OK)
+    assert ccb.ccb_cnt_notify_destroy(h) == 0
