@@ -13,7 +13,7 @@ namespace ccb {
 // (non-temporal stores measured 4% slower, in both barrier variants).
 constexpr bool kStencilNT = false;
 constexpr bool kStencilNTLoad = true;
-constexpr int kCntPerThread = 2;   // adjacent counters per thread in the batch engine (2 or 4)
+constexpr int kCntPerThread = 4;   // adjacent counters per thread in the batch engine (2 or 4)
 constexpr int kCntUnroll = 1;      // ops per register set in the batch engine's two-set pipeline
 constexpr bool kCntNTLoad = true;   // non-temporal loads of the op stream (read once)
 

@@ -81,7 +81,7 @@ def test_batch_malformed(wl, n_counters):
     np.testing.assert_array_equal(rel, r2)
 
 
-@pytest.mark.parametrize("n_counters", [4096, 4098])
+@pytest.mark.parametrize("n_counters", [4096, 4100, 4098])
 def test_batch_malformed_in_uniform_rows(wl, n_counters):
     """Random op bytes (any code, clear and reserved bits) in 3% of the
     entries, keeping each op's wait bit, so that every op stays all-record or

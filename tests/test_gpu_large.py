@@ -73,7 +73,7 @@ def test_stencil_beyond_int32_offsets(mode):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("n_counters", [1 << 27, (1 << 27) + 1],
-                         ids=["two-per-lane", "one-per-lane"])
+                         ids=["vector", "one-per-lane"])
 def test_batch_beyond_4GiB(n_counters):
     from cross_core_barrier_amd import workloads as wl
     n_ops = 9  # op 8 of every counter lies past byte 2^32 of val
