@@ -572,13 +572,16 @@ CCB_API ccbStatus ccb_cnt_notify_batch(const uint32_t* val, const uint8_t* meta,
     if (!aligned(final_, 4) || (val != nullptr && !aligned(val, 4))) return CCB_ERR_INVALID_VALUE;
     ccbStatus st = current_device(nullptr, nullptr);
     if (st != CCB_OK) return st;
-    // the vector form moves kCntPerThread adjacent counters per thread
-    constexpr int C = ccb::kCntPerThread;
-    const bool vec = (nCounters % C) == 0 && (val == nullptr || aligned(val, 4 * C)) &&
-                     (meta == nullptr || aligned(meta, C)) && aligned(final_, 4 * C) &&
-                     (rel == nullptr || aligned(rel, C));
+    // C adjacent counters per thread: 4 when the count and the arrays allow
+    // 16-B operand and 4-B op-code accesses, else 2, else 1
+    auto fits = [&](int C) {
+        return (nCounters % C) == 0 && (val == nullptr || aligned(val, 4 * C)) &&
+               (meta == nullptr || aligned(meta, C)) && aligned(final_, 4 * C) &&
+               (rel == nullptr || aligned(rel, C));
+    };
+    const int perThread = fits(4) ? 4 : (fits(2) ? 2 : 1);
     return from_hip(ccb::launch_cnt_batch(val, meta, nCounters, nOps, final_, rel, nRelRows, err,
-                                          vec, (hipStream_t)stream));
+                                          perThread, (hipStream_t)stream));
 }
 
 }  // extern "C"

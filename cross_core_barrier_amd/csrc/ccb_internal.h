@@ -13,7 +13,6 @@ namespace ccb {
 // (non-temporal stores measured 4% slower, in both barrier variants).
 constexpr bool kStencilNT = false;
 constexpr bool kStencilNTLoad = true;
-constexpr int kCntPerThread = 4;   // adjacent counters per thread in the batch engine (2 or 4)
 constexpr int kCntUnroll = 1;      // ops per register set in the batch engine's two-set pipeline
 constexpr bool kCntNTLoad = true;   // non-temporal loads of the op stream (read once)
 
@@ -48,7 +47,7 @@ hipError_t launch_stencil(const LaunchShape& ls, int32_t* bufA, int32_t* bufB, i
                           uint32_t maxPoll);
 hipError_t launch_cnt_batch(const uint32_t* val, const uint8_t* meta, int64_t nCounters,
                             int32_t nOps, uint32_t* finalOut, uint8_t* rel, int32_t nRelRows,
-                            int32_t* err, bool vec, hipStream_t s);
+                            int32_t* err, int perThread, hipStream_t s);
 hipError_t launch_cnt_record(uint32_t* line, int32_t mode, uint32_t value, hipStream_t s);
 hipError_t launch_cnt_wait(uint32_t* line, int32_t mode, uint32_t value, int32_t isClear,
                            uint64_t timeoutTicks, hipStream_t s);

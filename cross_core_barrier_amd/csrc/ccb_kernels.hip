@@ -846,7 +846,7 @@ __device__ __forceinline__ uint32_t cnt_wait_fast(uint32_t& c, uint32_t b, uint3
 
 }  // namespace
 
-// C adjacent counters per thread (C = 2 or 4): C-byte meta loads and
+// C adjacent counters per thread (C = 1, 2 or 4): C-byte meta loads and
 // 4C-byte operand loads per op; nCounters must be a multiple of C.
 template <int C> struct CntVec;
 template <> struct CntVec<4> {
@@ -856,6 +856,10 @@ template <> struct CntVec<4> {
 template <> struct CntVec<2> {
     typedef unsigned int val __attribute__((ext_vector_type(2)));
     typedef uint16_t meta;
+};
+template <> struct CntVec<1> {
+    typedef unsigned int val __attribute__((ext_vector_type(1)));
+    typedef uint8_t meta;
 };
 
 template <int C, int U>
@@ -878,7 +882,7 @@ __global__ __launch_bounds__(256) void ccb_k_cnt_batch(const uint32_t* __restric
     uint32_t seen[C], seenW[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) seen[i] = 1u, seenW[i] = 1u;
-    constexpr uint32_t kWaitBits = C == 4 ? 0x80808080u : 0x8080u;
+    constexpr uint32_t kWaitBits = C == 4 ? 0x80808080u : (C == 2 ? 0x8080u : 0x80u);
     auto apply = [&](uint32_t m, VT v) {
         const uint32_t waits = m & kWaitBits;
         if (!__any(waits != 0)) {
@@ -981,34 +985,6 @@ __global__ __launch_bounds__(256) void ccb_k_cnt_batch(const uint32_t* __restric
         bad = bad || (seen[i] & ~kRecValid) != 0 || (seenW[i] & ~kWaitValid) != 0;
     }
     *reinterpret_cast<VT*>(finalOut + c0) = out;
-    if (bad && err != nullptr)
-        __hip_atomic_store(err, (int32_t)CCB_ERR_INVALID_VALUE, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// One counter per thread: any nCounters.
-__global__ __launch_bounds__(256) void ccb_k_cnt_batch1(const uint32_t* __restrict__ val,
-                                                        const uint8_t* __restrict__ meta,
-                                                        int64_t nCounters, int32_t nOps,
-                                                        uint32_t* __restrict__ finalOut,
-                                                        uint8_t* __restrict__ rel,
-                                                        int32_t nRelRows, int32_t* err)
-{
-    const int64_t cidx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (cidx >= nCounters) return;
-    uint32_t c = 0;
-    int32_t j = 0;
-    bool bad = false;
-    for (int32_t k = 0; k < nOps; ++k) {
-        const uint32_t m = meta[(int64_t)k * nCounters + cidx];
-        const uint32_t v = val[(int64_t)k * nCounters + cidx];
-        uint8_t f = 0;
-        if (cnt_step(c, m, v, j < nRelRows, bad, f)) {
-            if (j < nRelRows) rel[(int64_t)j * nCounters + cidx] = f;
-            ++j;
-        }
-    }
-    finalOut[cidx] = c;
     if (bad && err != nullptr)
         __hip_atomic_store(err, (int32_t)CCB_ERR_INVALID_VALUE, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -1250,20 +1226,20 @@ hipError_t launch_register_query(KernelId id, int32_t mode, int32_t* out, hipStr
 
 hipError_t launch_cnt_batch(const uint32_t* val, const uint8_t* meta, int64_t nCounters,
                             int32_t nOps, uint32_t* finalOut, uint8_t* rel, int32_t nRelRows,
-                            int32_t* err, bool vec, hipStream_t s)
+                            int32_t* err, int perThread, hipStream_t s)
 {
     constexpr int kThreads = 256;
-    if (vec) {
-        constexpr int C = ccb::kCntPerThread;
-        const int64_t nThreads = nCounters / C;
-        const int64_t nBlocks = (nThreads + kThreads - 1) / kThreads;
-        hipLaunchKernelGGL((ccb_k_cnt_batch<C, kCntUnroll>), dim3((unsigned)nBlocks), dim3(kThreads),
-                           0, s, val, meta, nCounters, nOps, finalOut, rel, nRelRows, err);
-    } else {
-        const int64_t nBlocks = (nCounters + kThreads - 1) / kThreads;
-        hipLaunchKernelGGL(ccb_k_cnt_batch1, dim3((unsigned)nBlocks), dim3(kThreads), 0, s, val,
-                           meta, nCounters, nOps, finalOut, rel, nRelRows, err);
-    }
+    const int64_t nThreads = nCounters / perThread;
+    const dim3 grid((unsigned)((nThreads + kThreads - 1) / kThreads));
+    if (perThread == 4)
+        hipLaunchKernelGGL((ccb_k_cnt_batch<4, kCntUnroll>), grid, dim3(kThreads), 0, s, val, meta,
+                           nCounters, nOps, finalOut, rel, nRelRows, err);
+    else if (perThread == 2)
+        hipLaunchKernelGGL((ccb_k_cnt_batch<2, kCntUnroll>), grid, dim3(kThreads), 0, s, val, meta,
+                           nCounters, nOps, finalOut, rel, nRelRows, err);
+    else
+        hipLaunchKernelGGL((ccb_k_cnt_batch<1, kCntUnroll>), grid, dim3(kThreads), 0, s, val, meta,
+                           nCounters, nOps, finalOut, rel, nRelRows, err);
     return hipGetLastError();
 }
 

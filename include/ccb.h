@@ -400,7 +400,11 @@ CCB_API ccbStatus ccb_cnt_notify_query(ccbCntNotify h, uint32_t* value, ccbStatu
  * nRelRows) leaves the count unchanged, writes rel 0 for a wait that has a
  * row, and sets *err (device int32, may be NULL) to CCB_ERR_INVALID_VALUE;
  * *err is not written otherwise, so the caller zeroes it first.
- * val, final must be 4-B aligned; nCounters * nOps may be 0.
+ * val, final must be 4-B aligned; nCounters * nOps may be 0.  Performance: a
+ * count that is a multiple of 32 (128-B operand rows) with 16-B aligned val
+ * and final runs 4 counters per lane at full speed; other counts run 2 or 1
+ * per lane, and rows that do not start on a 128-B line cost more lines per
+ * load (2^20 + 1 counters x 64 ops: about 93 us, against 55 us for 2^20).
  * Errors: NULL_POINTER, INVALID_VALUE (negative sizes, or nCounters above
  * CCB_CNT_BATCH_MAX_COUNTERS). */
 #define CCB_CNT_BATCH_MAX_COUNTERS (((int64_t)1 << 31) * 256 - 256)
