@@ -434,7 +434,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build runs on a single MI355X)", file=sys.stderr)
+              "(the library runs each grid on a single MI355X)", file=sys.stderr)
         sys.exit(2)
     b = Bench(args)
     if args.only == "stencil":

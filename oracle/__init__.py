@@ -13,7 +13,7 @@ itself; see tests/test_oracle_*.py):
 
   witness_hash       SplitMix64 published output sequences (seed 0 and seed
                      1234567) -- pins the generator; the (seed, round, wg)
-                     keying is this build's convention, not the pages'.
+                     keying is this library's convention, not the pages'.
   mix_participants   the SYNCALL guide's §4.2 formula (blocks x (1 + ratio))
                      on its 1:1 and 1:2 cases, whole launch for 0.
   epoch_target       the SYNCALL guide's §5.2 prose (next multiple of N above
