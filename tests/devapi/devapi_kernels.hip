@@ -4,7 +4,8 @@
 // over a 2-D grid, with ccb_syncall_soft, ccb_syncall_soft_ordered,
 // ccb_syncall_soft_flat, ccb_syncall_soft_bounded or ccb_syncall_soft_mix
 // (role groups of one leader and 1 or 2 companions; usedCores then counts
-// groups).  Test code only: the
+// groups), or the split-phase pair ccb_arrive / ccb_await with the kernel's
+// own workgroup barriers and work between the two halves.  Test code only: the
 // GPU tests compare its output with the oracle's witness rounds.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -32,9 +33,10 @@ __global__ __launch_bounds__(1024) void devapi_rounds(int32_t* ws, uint32_t* slo
     __shared__ uint32_t partial[16];
     const int32_t nGrid = (int32_t)(gridDim.x * gridDim.y * gridDim.z);
     const int32_t w = ccb_block_linear();
-    const int32_t ratio = kVariant == 4 ? 1 : 2;  // variants 4 and 5: role groups
-    const int32_t n = kVariant >= 4 ? ccb_mix_participants(usedCores, ratio, nGrid)
-                                    : (usedCores != 0 ? usedCores : nGrid);
+    const bool mix = kVariant == 4 || kVariant == 5;  // role groups
+    const int32_t ratio = kVariant == 4 ? 1 : 2;
+    const int32_t n = mix ? ccb_mix_participants(usedCores, ratio, nGrid)
+                          : (usedCores != 0 ? usedCores : nGrid);
     const uint32_t tid = threadIdx.x;
     if (w >= n) {  // non-members never call the barrier
         if (tid == 0) status[w] = 2;
@@ -45,18 +47,42 @@ __global__ __launch_bounds__(1024) void devapi_rounds(int32_t* ws, uint32_t* slo
         uint32_t* row = slots + (size_t)(r & 1) * nGrid;  // two rows suffice for this order
         if (tid == 0) {
             const uint32_t h = devapi_witness(seed, (uint32_t)r, (uint32_t)w);
-            if (kVariant == 1) ccb_store_coherent(row + w, h);
+            if (kVariant == 1 || kVariant == 6) ccb_store_coherent(row + w, h);
             else row[w] = h;
         }
         if (kVariant == 0) rc = ccb_syncall_soft(ws, usedCores);
         else if (kVariant == 1) rc = ccb_syncall_soft_ordered(ws, usedCores);
         else if (kVariant == 2) rc = ccb_syncall_soft_flat(ws, usedCores);
         else if (kVariant == 3) rc = ccb_syncall_soft_bounded(ws, usedCores, maxPoll);
-        else rc = ccb_syncall_soft_mix(ws, usedCores, ratio);
+        else if (kVariant == 6) {
+            // split phase, ordering-only: every thread's stores are complete,
+            // one lane arrives, wave 0 waits, the kernel's own barriers
+            // order the rest; the next round's witness is computed while the
+            // arrival is in flight
+            __shared__ int32_t result;
+            __shared__ uint32_t nextWitness;
+            ccb_wait_memory();
+            __syncthreads();
+            if (tid < 64) {
+                int32_t before = 0;
+                if (tid == 0) {
+                    before = ccb_arrive<CCB_STRIPES, CCB_VIS_ORDER>(ws, w);
+                    nextWitness = devapi_witness(seed, (uint32_t)(r + 1), (uint32_t)w);
+                }
+                const int32_t e = ccb_await<CCB_STRIPES, CCB_VIS_ORDER>(
+                    ws, n, w, before, maxPoll, ws + CCB_STRIPES * CCB_LINE_WORDS);
+                if (tid == 0) result = e;
+            }
+            __syncthreads();
+            rc = result;
+            if (rc == CCB_OK && tid == 0 && r + 1 < rounds &&
+                nextWitness != devapi_witness(seed, (uint32_t)(r + 1), (uint32_t)w))
+                rc = CCB_ERR_INVALID_VALUE;  // the overlapped work went wrong
+        } else rc = ccb_syncall_soft_mix(ws, usedCores, ratio);
         if (rc != CCB_OK) break;
         uint32_t s = 0;
         for (int32_t i = (int32_t)tid; i < n; i += (int32_t)blockDim.x)
-            s += kVariant == 1 ? ccb_load_coherent(row + i) : row[i];
+            s += (kVariant == 1 || kVariant == 6) ? ccb_load_coherent(row + i) : row[i];
         for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
         if ((tid % 64) == 0) partial[tid / 64] = s;
         __syncthreads();
@@ -72,23 +98,28 @@ __global__ __launch_bounds__(1024) void devapi_rounds(int32_t* ws, uint32_t* slo
 
 }  // namespace
 
-// Launches variant 0..5 cooperatively on a gx x gy grid of `threads`
+// Launches variant 0..6 cooperatively on a gx x gy grid of `threads`
 // threads (a multiple of 64, at most 1024).  slots: 2 * gx * gy uint32;
 // out: rounds * gx * gy uint32; status: gx * gy int32.  Returns a hipError_t.
 extern "C" int devapi_run(int variant, int32_t* ws, uint32_t* slots, uint32_t* out, int32_t* status,
                           uint64_t seed, int32_t rounds, int32_t gx, int32_t gy, int32_t threads,
                           int32_t usedCores, uint32_t maxPoll, hipStream_t stream)
 {
-    const int32_t members = variant >= 4 ? ccb_mix_participants(usedCores, variant == 4 ? 1 : 2, gx * gy)
-                                         : usedCores;
-    if (variant < 0 || variant > 5 || threads < 64 || threads > 1024 || threads % 64 != 0 ||
+    const bool mix = variant == 4 || variant == 5;
+    const int32_t members = mix ? ccb_mix_participants(usedCores, variant == 4 ? 1 : 2, gx * gy)
+                                : usedCores;
+    if (variant < 0 || variant > 6 || threads < 64 || threads > 1024 || threads % 64 != 0 ||
         gx < 1 || gy < 1 || usedCores < 0 || members > gx * gy)
         return (int)hipErrorInvalidValue;
+    // every buffer is written by the kernel: never launch with a missing one
+    if (ws == nullptr || slots == nullptr || out == nullptr || status == nullptr)
+        return (int)hipErrorInvalidValue;
     void* args[] = {&ws, &slots, &out, &status, &seed, &rounds, &usedCores, &maxPoll};
-    const void* const fns[6] = {
+    const void* const fns[7] = {
         reinterpret_cast<const void*>(&devapi_rounds<0>), reinterpret_cast<const void*>(&devapi_rounds<1>),
         reinterpret_cast<const void*>(&devapi_rounds<2>), reinterpret_cast<const void*>(&devapi_rounds<3>),
-        reinterpret_cast<const void*>(&devapi_rounds<4>), reinterpret_cast<const void*>(&devapi_rounds<5>)};
+        reinterpret_cast<const void*>(&devapi_rounds<4>), reinterpret_cast<const void*>(&devapi_rounds<5>),
+        reinterpret_cast<const void*>(&devapi_rounds<6>)};
     const void* fn = fns[variant];
     return (int)hipLaunchCooperativeKernel(fn, dim3(gx, gy), dim3(threads), args, 0, stream);
 }

@@ -160,3 +160,10 @@ def test_device_api_test_kernels_built():
     for name in ("ccb_syncall_soft", "ccb_syncall_soft_ordered", "ccb_syncall_soft_flat",
                  "ccb_syncall_soft_bounded", "ccb_arrive", "ccb_await", "ccb_barrier"):
         assert name + "(" in text, name
+    # the test launcher refuses unknown variants and missing buffers before any
+    # HIP call (hipErrorInvalidValue = 1; a launch attempt would report more)
+    V, I32, U32, U64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64
+    lib.devapi_run.restype = ctypes.c_int
+    lib.devapi_run.argtypes = [ctypes.c_int, V, V, V, V, U64, I32, I32, I32, I32, I32, U32, V]
+    for variant in range(8):
+        assert lib.devapi_run(variant, None, None, None, None, 0, 1, 1, 1, 64, 0, 0, None) == 1

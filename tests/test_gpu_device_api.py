@@ -1,6 +1,6 @@
 """GPU parity of the in-kernel barrier API (include/ccb_device.h) used as a
 caller's own kernel would use it: ccb_syncall_soft / _ordered / _flat /
-_bounded inside the flag-slot pattern of the SYNCALL guide §6.1, on 2-D
+_bounded / _mix and the split-phase ccb_arrive / ccb_await inside the flag-slot pattern of the SYNCALL guide §6.1, on 2-D
 grids, with and without a usedCores subset.  The test kernels live in
 tests/devapi (built by __graft_entry__.build()); the expected sums come from
 the oracle's witness rounds."""
@@ -18,7 +18,8 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 LIB = os.path.join(os.path.dirname(__file__), "devapi", "libccb_devapi.so")
-VARIANTS = {0: "soft", 1: "soft_ordered", 2: "soft_flat", 3: "soft_bounded"}  # 4, 5: mix 1:1, 1:2
+VARIANTS = {0: "soft", 1: "soft_ordered", 2: "soft_flat", 3: "soft_bounded",
+            6: "split_phase"}  # 4, 5: mix 1:1, 1:2
 
 
 def _say(msg):
@@ -107,6 +108,9 @@ def test_device_api_bounded_reports_deadlock(devapi):
 
 
 def test_device_api_rejects_bad_launch(devapi):
-    assert devapi.devapi_run(6, None, None, None, None, 0, 1, 1, 1, 64, 0, 0, None) != 0
+    """Refused before anything is launched (the launcher also refuses null
+    buffers, which every case below passes)."""
+    assert devapi.devapi_run(7, None, None, None, None, 0, 1, 1, 1, 64, 0, 0, None) != 0  # no variant 7
+    assert devapi.devapi_run(6, None, None, None, None, 0, 1, 1, 1, 64, 0, 0, None) != 0  # null buffers
     assert devapi.devapi_run(5, None, None, None, None, 0, 1, 4, 1, 64, 2, 0, None) != 0  # 6 > 4
     assert devapi.devapi_run(0, None, None, None, None, 0, 1, 2, 1, 64, 3, 0, None) != 0
