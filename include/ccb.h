@@ -146,7 +146,9 @@ CCB_API ccbStatus ccb_device_info(int32_t* numCUs, int32_t* ldsPerCU, int32_t* w
  * allocation (which the API leaves out).  The first persistent launch on a
  * device reads every kernel variant's allocation with one-workgroup query
  * launches on the default stream and waits for them (no allocation, no new
- * stream); make that first call outside stream capture.  `wgsPerCu` > 0 also
+ * stream); make that first call outside stream capture.  After it, every
+ * launcher, the workspace reset and the CntNotify record / wait / reset /
+ * batch calls can be captured into a HIP graph (kernel nodes only).  `wgsPerCu` > 0 also
  * sizes each workgroup's LDS so that at most that many share a compute unit
  * (0 = no shaping).  `maxPoll` bounds each barrier's poll loop (0 = the
  * default CCB_SOFT_MAX_POLL); a member that exhausts it sets the error word
