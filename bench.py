@@ -16,6 +16,8 @@ The same run also measures, each on its own stream with HIP events:
   - the persistent stencil (2^26 int32, 64 iterations, 1024 workgroups):
     the HBM roofline of the data phases;
   - the batched CntNotify engine (2^20 counters x 64 ops);
+  - CntNotify record -> wait latency between streams, and the cost of a
+    record + wait pair enqueued eagerly or replayed from a HIP graph;
   - a 512 MiB streaming copy (achievable HBM ceiling);
   - the CPU oracle on the host cores (cpu_baseline).
 It prints ONE JSON line.
@@ -335,6 +337,39 @@ class Bench:
                                          "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
                                          "ops_per_s": round(CNT_COUNTERS * CNT_OPS / (bms / 1e3), 0)}
 
+    # ------------------------------------------------------------ record + wait in a graph
+    def cnt_graph(self):
+        """100 (record ADD 1, wait GE 1 with clear) pairs on one stream, enqueued
+        eagerly and replayed from a captured HIP graph: the cost of one pair
+        each way.  Every pair leaves the count at 0."""
+        ccb, torch, s = self.ccb, self.torch, self.stream
+        st, h = ccb.ccb_cnt_notify_create(0)
+        ccb.check(st, "create")
+        rec = ccb.record_info(ccb.CCB_CNT_RECORD_ADD, 1)
+        wait = ccb.wait_info(ccb.CCB_CNT_WAIT_BIGGER_OR_EQUAL, 1, 2, 1)
+
+        def pairs():
+            for _ in range(100):
+                ccb.check(ccb.ccb_cnt_notify_record(h, s, rec), "record")
+                ccb.check(ccb.ccb_cnt_notify_wait(h, s, wait), "wait")
+
+        pairs()
+        torch.cuda.synchronize()
+        eager = min(self.timer(pairs) for _ in range(5))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            pairs()
+        g.replay()
+        torch.cuda.synchronize()
+        graph = min(self.timer(g.replay) for _ in range(5))
+        st, v, last = ccb.ccb_cnt_notify_query(h, s)
+        assert (st, v, last) == (0, 0, ccb.CCB_OK), (st, v, last)
+        ccb.check(ccb.ccb_cnt_notify_destroy(h), "destroy")
+        out = {"eager_us_per_pair": round(eager * 1e3 / 100, 2),
+               "graph_us_per_pair": round(graph * 1e3 / 100, 2)}
+        self.extra["cntnotify_record_wait_pair"] = out
+        log(f"cntnotify record + wait pair: {out}")
+
     # ------------------------------------------------------------ stream-to-stream notify
     def cnt_stream_latency(self):
         """CntNotify §5's pattern on streams: the consumer stream waits GE N
@@ -455,6 +490,7 @@ def main():
         roofline = b.stencil(gbs)
         b.cnt_batch()
         b.cnt_stream_latency()
+        b.cnt_graph()
         if not args.no_cpu:
             cpu = b.cpu_baseline()
             b.cpu_context()
