@@ -11,7 +11,8 @@ round: each workgroup stores its witness, all pass the barrier, each sums all
 The same run also measures, each on its own stream with HIP events:
   - the floor: dependent agent-scope atomic round trips by one lane
     (fetch-add and load, with and without fences) and 256-way contention;
-  - barrier-only latency for every barrier variant (slope over rounds);
+  - barrier-only latency for every barrier variant (slope over rounds), and
+    HIP's cooperative-groups grid sync on the same grids for comparison;
   - the 128-member pass and the grouped A/B/mix rounds (512 workgroups);
   - the persistent stencil (2^26 int32, 64 iterations, 1024 workgroups):
     the HBM roofline of the data phases;
@@ -215,6 +216,26 @@ class Bench:
             "floor_ns": floor["fetch_add_ns"], "ratio": round(best / floor["fetch_add_ns"], 2),
             "target_ratio": 2.0}
         log(f"barrier-only ns/barrier at 256 WGs: {lat}")
+
+    # ------------------------------------------------------------ HIP's own grid barrier
+    def hip_grid_sync(self):
+        """cooperative_groups grid_group::sync() on the same grids (slope over rounds)."""
+        torch, ccb, stream = self.torch, self.ccb, self.stream
+        done = torch.zeros(1, dtype=torch.int32, device=self.dev)
+        out = {}
+        for n_wg, threads in ((256, 256), (1024, 256)):
+            res = {}
+            for r in (200, 1000):
+                def f(r=r):
+                    ccb.check(ccb.ccb_bench_hip_grid_sync(r, n_wg, threads, done, stream),
+                              "hip grid sync")
+                f()
+                res[r] = min(self.timer(f) for _ in range(3))
+                torch.cuda.synchronize()
+                assert int(done.item()) == r
+            out[f"{n_wg}x{threads}"] = round((res[1000] - res[200]) / 800 * 1e6, 1)
+        self.extra["hip_grid_sync_ns"] = out
+        log(f"HIP cooperative-groups grid sync, ns per sync: {out}")
 
     # ------------------------------------------------------------ grouped rounds
     def grouped(self):
@@ -485,6 +506,7 @@ def main():
     if not args.quick:
         floor = b.floor()
         b.latency(floor)
+        b.hip_grid_sync()
         b.grouped()
         gbs = b.copy_ceiling()
         roofline = b.stencil(gbs)

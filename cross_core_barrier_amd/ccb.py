@@ -109,6 +109,7 @@ _f = {
     "ccb_stencil_halo_bytes": _sig("ccb_stencil_halo_bytes", ctypes.c_size_t, _I64, _I32, _I32),
     "ccb_bench_atomic_chain": _sig("ccb_bench_atomic_chain", _I32, _V, _V, _I32, _I32, _I32, _V),
     "ccb_bench_atomic_contended": _sig("ccb_bench_atomic_contended", _I32, _V, _V, _I32, _I32, _V),
+    "ccb_bench_hip_grid_sync": _sig("ccb_bench_hip_grid_sync", _I32, _I32, _I32, _I32, _V, _V),
     "ccb_bench_copy": _sig("ccb_bench_copy", _I32, _V, _V, _I64, _V),
     "ccb_cnt_notify_create": _sig("ccb_cnt_notify_create", _I32, _V, _U64),
     "ccb_cnt_notify_record": _sig("ccb_cnt_notify_record", _I32, _V, _V, _V),
@@ -216,6 +217,10 @@ def ccb_bench_atomic_chain(line, ticks, iters, fenced=0, kind=0, stream=None) ->
 
 def ccb_bench_atomic_contended(line, ticks, iters, n_grid, stream=None) -> int:
     return _f["ccb_bench_atomic_contended"](_p(line), _p(ticks), iters, n_grid, _s(stream))
+
+
+def ccb_bench_hip_grid_sync(rounds, n_grid, threads, done_out, stream=None) -> int:
+    return _f["ccb_bench_hip_grid_sync"](rounds, n_grid, threads, _p(done_out), _s(stream))
 
 
 def ccb_bench_copy(dst, src, n_bytes, stream=None) -> int:

@@ -32,28 +32,45 @@ struct DeviceInfo {
 std::mutex g_dev_mu;
 DeviceInfo g_dev[kMaxDevices];
 
+// A runtime error is reported through the returned status only: the
+// thread's HIP last-error slot is cleared, so a refused launch here does not
+// surface later as the error of the caller's next, unrelated launch.
+inline ccbStatus hip_failed()
+{
+    (void)hipGetLastError();
+    return CCB_ERR_HIP;
+}
+
+inline ccbStatus from_hip(hipError_t e)
+{
+    if (e == hipSuccess) return CCB_OK;
+    (void)hipGetLastError();
+    if (e == hipErrorCooperativeLaunchTooLarge) return CCB_ERR_NOT_CORESIDENT;
+    return CCB_ERR_HIP;
+}
+
 ccbStatus current_device(int* devOut, DeviceInfo* infoOut)
 {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return CCB_ERR_HIP;
+    if (hipGetDevice(&dev) != hipSuccess) return hip_failed();
     if (dev < 0 || dev >= kMaxDevices) return CCB_ERR_UNSUPPORTED_DEVICE;
     std::lock_guard<std::mutex> lk(g_dev_mu);
     DeviceInfo& d = g_dev[dev];
     if (!d.probed) {
         hipDeviceProp_t p;
-        if (hipGetDeviceProperties(&p, dev) != hipSuccess) return CCB_ERR_HIP;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) return hip_failed();
         d.gfx950 = strncmp(p.gcnArchName, "gfx950", 6) == 0;
         d.numCUs = p.multiProcessorCount;
         int v = 0;
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
             hipSuccess)
-            return CCB_ERR_HIP;
+            return hip_failed();
         d.ldsPerCU = v;
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-            return CCB_ERR_HIP;
+            return hip_failed();
         d.ldsPerBlockMax = v;
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
-            return CCB_ERR_HIP;
+            return hip_failed();
         d.wallClockKHz = v;
         d.probed = true;
     }
@@ -65,12 +82,6 @@ ccbStatus current_device(int* devOut, DeviceInfo* infoOut)
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-inline ccbStatus from_hip(hipError_t e)
-{
-    if (e == hipSuccess) return CCB_OK;
-    if (e == hipErrorCooperativeLaunchTooLarge) return CCB_ERR_NOT_CORESIDENT;
-    return CCB_ERR_HIP;
-}
 
 inline bool valid_threads(int32_t threads)
 {
@@ -109,13 +120,13 @@ ccbStatus sgpr_waves(int dev, ccb::KernelId id, int32_t mode, int* waves)
     RegQuery& q = g_query[dev];
     if (!q.done) {
         int32_t* word = nullptr;
-        if (ccb::register_query_word(&word) != hipSuccess) return CCB_ERR_HIP;
+        if (ccb::register_query_word(&word) != hipSuccess) return hip_failed();
         for (int k = 0; k < kKernelIds; ++k)
             for (int m = 0; m < 4; ++m) {
                 int32_t alloc = 0;
                 if (ccb::launch_register_query((ccb::KernelId)k, m, word, nullptr) != hipSuccess ||
                     hipMemcpy(&alloc, word, sizeof(alloc), hipMemcpyDeviceToHost) != hipSuccess)
-                    return CCB_ERR_HIP;
+                    return hip_failed();
                 const int sgprs = ((((uint32_t)alloc >> 24) & 0xF) + 1) * 16;
                 const int w = kSgprPerSimd / (sgprs + kTrapSgprs);
                 q.waves[k][m] = (int8_t)(w < 1 ? 1 : (w > 8 ? 8 : w));
@@ -135,7 +146,7 @@ ccbStatus plan_persistent(ccb::KernelId id, int32_t mode, int32_t nGrid, int32_t
     if (st != CCB_OK) return st;
     const void* fn = ccb::kernel_ptr(id, mode);
     hipFuncAttributes attr;
-    if (hipFuncGetAttributes(&attr, fn) != hipSuccess) return CCB_ERR_HIP;
+    if (hipFuncGetAttributes(&attr, fn) != hipSuccess) return hip_failed();
     size_t lds = 0;
     if (wgsPerCu > 0) {
         long want = (long)info.ldsPerCU / wgsPerCu - (long)attr.sharedSizeBytes;
@@ -146,11 +157,11 @@ ccbStatus plan_persistent(ccb::KernelId id, int32_t mode, int32_t nGrid, int32_t
         lds = (size_t)want;
         if (lds > 0 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)lds) != hipSuccess)
-            return CCB_ERR_HIP;
+            return hip_failed();
     }
     int perCU = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&perCU, fn, threads, lds) != hipSuccess)
-        return CCB_ERR_HIP;
+        return hip_failed();
     // the SGPR limit the occupancy API misses: 4 SIMDs per CU, threads / 64
     // waves per workgroup spread over them
     int waves = 0;
@@ -217,7 +228,7 @@ ccbStatus resolve(ccbCntNotify h, uint32_t* idxOut, uint32_t** line, bool kill =
     CntSlot& s = g_cnt[idx];
     if (!s.alive || s.gen != gen) return CCB_ERR_INVALID_HANDLE;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return CCB_ERR_HIP;
+    if (hipGetDevice(&dev) != hipSuccess) return hip_failed();
     if (dev != s.device) return CCB_ERR_INVALID_HANDLE;
     if (kill) s.alive = false;
     if (idxOut) *idxOut = idx;
@@ -290,13 +301,13 @@ CCB_API ccbStatus ccb_syncall_status(const int32_t* ws, uint32_t nBarriers, int3
         return CCB_ERR_INVALID_VALUE;
     ccbStatus st = current_device(nullptr, nullptr);
     if (st != CCB_OK) return st;
-    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return CCB_ERR_HIP;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return hip_failed();
     const size_t lines = (size_t)nBarriers * CCB_STRIPES + 1;
     int32_t* buf = new int32_t[lines * kLineWords];
     hipError_t e = hipMemcpy(buf, ws, lines * CCB_LINE_BYTES, hipMemcpyDeviceToHost);
     ccbStatus rc = CCB_OK;
     if (e != hipSuccess) {
-        rc = CCB_ERR_HIP;
+        rc = hip_failed();
     } else {
         if (arrivals)
             for (uint32_t b = 0; b < nBarriers; ++b) {
@@ -437,6 +448,18 @@ CCB_API ccbStatus ccb_bench_atomic_contended(int32_t* line, uint64_t* ticksOut, 
                                                  (hipStream_t)stream));
 }
 
+CCB_API ccbStatus ccb_bench_hip_grid_sync(int32_t rounds, int32_t nGrid, int32_t threads,
+                                          int32_t* doneOut, ccbStream stream)
+{
+    if (doneOut == nullptr) return CCB_ERR_NULL_POINTER;
+    if (rounds < 1 || nGrid < 1 || !valid_threads(threads)) return CCB_ERR_INVALID_VALUE;
+    DeviceInfo info;
+    ccbStatus st = current_device(nullptr, &info);
+    if (st != CCB_OK) return st;
+    return from_hip(ccb::launch_hip_grid_sync(rounds, nGrid, threads, doneOut, info.numCUs,
+                                              (hipStream_t)stream));
+}
+
 CCB_API ccbStatus ccb_bench_copy(void* dst, const void* src, int64_t nBytes, ccbStream stream)
 {
     if (dst == nullptr || src == nullptr) return CCB_ERR_NULL_POINTER;
@@ -464,7 +487,7 @@ CCB_API ccbStatus ccb_cnt_notify_create(ccbCntNotify* out, uint64_t flag)
     if (g_cnt_pool[dev] == nullptr) {
         void* p = nullptr;
         if (hipMalloc(&p, (size_t)CCB_CNT_NOTIFY_POOL * CCB_LINE_BYTES) != hipSuccess)
-            return CCB_ERR_HIP;
+            return hip_failed();
         g_cnt_pool[dev] = static_cast<uint32_t*>(p);
     }
     uint32_t idx = CCB_CNT_NOTIFY_POOL;
@@ -478,7 +501,7 @@ CCB_API ccbStatus ccb_cnt_notify_create(ccbCntNotify* out, uint64_t flag)
     init[1] = (uint32_t)CCB_ERR_NOT_READY;
     if (hipMemcpy(g_cnt_pool[dev] + (size_t)idx * kLineWords, init, sizeof(init),
                   hipMemcpyHostToDevice) != hipSuccess)
-        return CCB_ERR_HIP;
+        return hip_failed();
     CntSlot& s = g_cnt[idx];
     s.alive = true;
     s.gen = (s.gen + 1) & 0xFFFFFu;
@@ -548,10 +571,10 @@ CCB_API ccbStatus ccb_cnt_notify_query(ccbCntNotify h, uint32_t* value, ccbStatu
     uint32_t* line = nullptr;
     ccbStatus st = resolve(h, nullptr, &line);
     if (st != CCB_OK) return st;
-    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return CCB_ERR_HIP;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return hip_failed();
     uint32_t words[2] = {0, 0};
     if (hipMemcpy(words, line, sizeof(words), hipMemcpyDeviceToHost) != hipSuccess)
-        return CCB_ERR_HIP;
+        return hip_failed();
     if (value) *value = words[0];
     if (lastWait) *lastWait = (ccbStatus)words[1];
     return CCB_OK;

@@ -11,6 +11,7 @@
 // (CANN Runtime CntNotify interfaces) §3.1-§3.3, §4.2-§4.4 for the counter
 // operations.  Each kernel cites the passage it implements.
 
+#include <hip/hip_cooperative_groups.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1109,6 +1110,17 @@ __global__ void ccb_k_atomic_contended(int32_t* line, uint64_t* ticks, int32_t i
     if (v == 0x7fffffff) ticks[2 * blockIdx.x] = 0;
 }
 
+// HIP's own grid barrier (cooperative groups' grid sync), `rounds` times in a
+// row: the platform's stock answer to the same problem, timed beside ours.
+// Workgroup 0 writes `rounds` to *done once it has passed the last one.
+__global__ void ccb_k_hip_grid_sync(int32_t rounds, int32_t* done)
+{
+    cooperative_groups::grid_group g = cooperative_groups::this_grid();
+    for (int32_t r = 0; r < rounds; ++r) g.sync();
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        __hip_atomic_store(done, rounds, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Streaming copy: every thread moves one 16-byte vector per step and the
 // whole grid advances through memory together (the access order that gets
 // the most out of HBM on this GPU), loads and stores non-temporal.
@@ -1285,6 +1297,21 @@ hipError_t launch_atomic_contended(int32_t* line, uint64_t* ticks, int32_t iters
     void* args[] = {&line, &ticks, &iters, &zero};
     return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&ccb_k_atomic_contended),
                                       dim3(nGrid), dim3(kWave), args, 0, s);
+}
+
+hipError_t launch_hip_grid_sync(int32_t rounds, int32_t nGrid, int32_t threads, int32_t* done,
+                                int numCUs, hipStream_t s)
+{
+    // grid sync waits without a bound, so the grid must be shown resident
+    // here, not only by the runtime's own check.  The kernel uses few SGPRs
+    // (21), where the occupancy API's count is exact.
+    const void* fn = reinterpret_cast<const void*>(&ccb_k_hip_grid_sync);
+    int perCU = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&perCU, fn, threads, 0);
+    if (e != hipSuccess) return e;
+    if ((int64_t)perCU * numCUs < nGrid) return hipErrorCooperativeLaunchTooLarge;
+    void* args[] = {&rounds, &done};
+    return hipLaunchCooperativeKernel(fn, dim3(nGrid), dim3(threads), args, 0, s);
 }
 
 hipError_t launch_copy(int4* dst, const int4* src, int64_t n16, int nBlocks, hipStream_t s)

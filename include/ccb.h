@@ -25,6 +25,10 @@
  *     That device must be a gfx950 GPU, else CCB_ERR_UNSUPPORTED_DEVICE.
  *   - Arguments are validated before anything is enqueued; on an error
  *     return nothing has been enqueued and no output has been written.
+ *   - A runtime error (CCB_ERR_HIP, or a cooperative launch the runtime
+ *     refuses: CCB_ERR_NOT_CORESIDENT) is reported through the returned
+ *     status alone: the calling thread's HIP last-error state is left clear,
+ *     so it does not resurface as the error of a later, unrelated launch.
  */
 #ifndef CCB_H
 #define CCB_H
@@ -292,6 +296,17 @@ CCB_API ccbStatus ccb_bench_atomic_chain(int32_t* line, uint64_t* ticksOut, int3
  * start/end ticks.  Errors: NULL_POINTER, INVALID_VALUE, NOT_CORESIDENT. */
 CCB_API ccbStatus ccb_bench_atomic_contended(int32_t* line, uint64_t* ticksOut, int32_t iters,
                                              int32_t nGrid, ccbStream stream);
+
+/* HIP's cooperative-groups grid barrier (grid_group::sync) `rounds` times in
+ * one cooperative launch of nGrid workgroups of `threads` threads (a
+ * multiple of 64, at most 1024): the platform's stock grid barrier, for
+ * timing beside the soft barrier (not on the pages).  When the launch ends,
+ * *doneOut (device int32) holds `rounds`.  The caller times it (e.g. two
+ * launches with different `rounds`).  Errors: NULL_POINTER, INVALID_VALUE,
+ * NOT_CORESIDENT (more workgroups than can be resident at once: checked
+ * before the launch, since grid sync waits without a bound). */
+CCB_API ccbStatus ccb_bench_hip_grid_sync(int32_t rounds, int32_t nGrid, int32_t threads,
+                                          int32_t* doneOut, ccbStream stream);
 
 /* Streaming copy of nBytes (multiple of 16) from src to dst (device, 16-B
  * aligned, not overlapping): the achievable HBM ceiling for the data phases.

@@ -141,6 +141,10 @@ def test_validation_before_device_work(ccb):
     assert ccb.ccb_bench_atomic_chain(None, 256, 1) == ccb.CCB_ERR_NULL_POINTER
     assert ccb.ccb_bench_atomic_chain(128, 256, 0) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_bench_copy(256, 512, 17) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_bench_hip_grid_sync(1, 8, 64, None) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_bench_hip_grid_sync(0, 8, 64, 256) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_bench_hip_grid_sync(1, 0, 64, 256) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_bench_hip_grid_sync(1, 8, 96, 256) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_cnt_notify_batch(None, None, -1, 1, None, None, 1) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_cnt_notify_batch(None, None, 0, 1, None, None, 1) == ccb.CCB_OK
     # one workgroup of 256 threads per 256 counters, fewer than 2^31 workgroups
