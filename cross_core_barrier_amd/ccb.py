@@ -170,7 +170,7 @@ def ccb_syncall_workspace_reset(ws, n_barriers: int, stream=None) -> int:
 
 def ccb_syncall_status(ws, n_barriers: int, stream=None):
     """Returns (status, [total arrivals per barrier])."""
-    buf = (_I32 * max(n_barriers, 1))()
+    buf = (_I64 * max(n_barriers, 1))()
     st = _f["ccb_syncall_status"](_p(ws), n_barriers, buf, _s(stream))
     return st, [int(buf[i]) for i in range(n_barriers)]
 

@@ -293,7 +293,7 @@ CCB_API ccbStatus ccb_syncall_workspace_reset(int32_t* ws, uint32_t nBarriers, c
     return from_hip(ccb::launch_fill_zero(ws, words, (hipStream_t)stream));
 }
 
-CCB_API ccbStatus ccb_syncall_status(const int32_t* ws, uint32_t nBarriers, int32_t* arrivals,
+CCB_API ccbStatus ccb_syncall_status(const int32_t* ws, uint32_t nBarriers, int64_t* arrivals,
                                      ccbStream stream)
 {
     if (ws == nullptr) return CCB_ERR_NULL_POINTER;
@@ -302,25 +302,29 @@ CCB_API ccbStatus ccb_syncall_status(const int32_t* ws, uint32_t nBarriers, int3
     ccbStatus st = current_device(nullptr, nullptr);
     if (st != CCB_OK) return st;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return hip_failed();
-    const size_t lines = (size_t)nBarriers * CCB_STRIPES + 1;
-    int32_t* buf = new int32_t[lines * kLineWords];
-    hipError_t e = hipMemcpy(buf, ws, lines * CCB_LINE_BYTES, hipMemcpyDeviceToHost);
-    ccbStatus rc = CCB_OK;
-    if (e != hipSuccess) {
-        rc = hip_failed();
-    } else {
-        if (arrivals)
-            for (uint32_t b = 0; b < nBarriers; ++b) {
+    int32_t errWord = 0;
+    if (hipMemcpy(&errWord, ws + (size_t)nBarriers * CCB_STRIPES * kLineWords, sizeof(errWord),
+                  hipMemcpyDeviceToHost) != hipSuccess)
+        return hip_failed();
+    if (arrivals != nullptr) {
+        // only the counter word of each stripe line is read (a strided copy),
+        // kChunk barriers at a time through a fixed host buffer
+        constexpr uint32_t kChunk = 64;
+        int32_t words[kChunk * CCB_STRIPES];
+        for (uint32_t b0 = 0; b0 < nBarriers; b0 += kChunk) {
+            const uint32_t nb = nBarriers - b0 < kChunk ? nBarriers - b0 : kChunk;
+            if (hipMemcpy2D(words, sizeof(int32_t), ws + (size_t)b0 * CCB_STRIPES * kLineWords,
+                            CCB_LINE_BYTES, sizeof(int32_t), (size_t)nb * CCB_STRIPES,
+                            hipMemcpyDeviceToHost) != hipSuccess)
+                return hip_failed();
+            for (uint32_t b = 0; b < nb; ++b) {
                 int64_t sum = 0;
-                for (uint32_t k = 0; k < CCB_STRIPES; ++k)
-                    sum += buf[((size_t)b * CCB_STRIPES + k) * kLineWords];
-                arrivals[b] = (int32_t)sum;
+                for (uint32_t k = 0; k < CCB_STRIPES; ++k) sum += words[b * CCB_STRIPES + k];
+                arrivals[b0 + b] = sum;
             }
-        const int32_t errWord = buf[(lines - 1) * kLineWords];
-        rc = errWord == CCB_OK ? CCB_OK : CCB_ERR_DEADLOCK;
+        }
     }
-    delete[] buf;
-    return rc;
+    return errWord == CCB_OK ? CCB_OK : CCB_ERR_DEADLOCK;
 }
 
 // ===========================================================================
@@ -592,7 +596,9 @@ CCB_API ccbStatus ccb_cnt_notify_batch(const uint32_t* val, const uint8_t* meta,
     if (final_ == nullptr) return CCB_ERR_NULL_POINTER;
     if (nOps > 0 && (val == nullptr || meta == nullptr)) return CCB_ERR_NULL_POINTER;
     if (nRelRows > 0 && rel == nullptr) return CCB_ERR_NULL_POINTER;
-    if (!aligned(final_, 4) || (val != nullptr && !aligned(val, 4))) return CCB_ERR_INVALID_VALUE;
+    if (!aligned(final_, 4) || (val != nullptr && !aligned(val, 4)) ||
+        (err != nullptr && !aligned(err, 4)))
+        return CCB_ERR_INVALID_VALUE;
     ccbStatus st = current_device(nullptr, nullptr);
     if (st != CCB_OK) return st;
     // C adjacent counters per thread: 4 when the count and the arrays allow

@@ -173,9 +173,12 @@ CCB_API ccbStatus ccb_syncall_workspace_reset(int32_t* ws, uint32_t nBarriers, c
 
 /* Wait for `stream`, then read the error word of a workspace of nBarriers
  * barriers and (optionally, arrivals may be NULL) store in arrivals[b] the
- * total number of arrivals on barrier b (the sum of its stripes).  Returns
- * CCB_OK or CCB_ERR_DEADLOCK (or HIP errors).  Blocks the host thread. */
-CCB_API ccbStatus ccb_syncall_status(const int32_t* ws, uint32_t nBarriers, int32_t* arrivals,
+ * total number of arrivals on barrier b (the sum of its stripes; int64, as
+ * the total of 64 int32 stripes can pass 2^31).  Reads only the counter word
+ * of each line, through a fixed-size host buffer.  Returns CCB_OK or
+ * CCB_ERR_DEADLOCK, or CCB_ERR_HIP (arrivals may then be partly written).
+ * Blocks the host thread. */
+CCB_API ccbStatus ccb_syncall_status(const int32_t* ws, uint32_t nBarriers, int64_t* arrivals,
                                      ccbStream stream);
 
 /* Barrier-only persistent grid: `rounds` consecutive soft barriers on
@@ -417,13 +420,13 @@ CCB_API ccbStatus ccb_cnt_notify_query(ccbCntNotify h, uint32_t* value, ccbStatu
  * nRelRows) leaves the count unchanged, writes rel 0 for a wait that has a
  * row, and sets *err (device int32, may be NULL) to CCB_ERR_INVALID_VALUE;
  * *err is not written otherwise, so the caller zeroes it first.
- * val, final must be 4-B aligned; nCounters * nOps may be 0.  Performance: a
+ * val, final and err must be 4-B aligned; nCounters * nOps may be 0.  Performance: a
  * count that is a multiple of 32 (128-B operand rows) with 16-B aligned val
  * and final runs 4 counters per lane at full speed; other counts run 2 or 1
  * per lane, and rows that do not start on a 128-B line cost more lines per
  * load (2^20 + 1 counters x 64 ops: about 93 us, against 55 us for 2^20).
- * Errors: NULL_POINTER, INVALID_VALUE (negative sizes, or nCounters above
- * CCB_CNT_BATCH_MAX_COUNTERS). */
+ * Errors: NULL_POINTER, INVALID_VALUE (negative sizes, a misaligned val,
+ * final or err, or nCounters above CCB_CNT_BATCH_MAX_COUNTERS). */
 #define CCB_CNT_BATCH_MAX_COUNTERS (((int64_t)1 << 31) * 256 - 256)
 CCB_API ccbStatus ccb_cnt_notify_batch(const uint32_t* val, const uint8_t* meta,
                                        int64_t nCounters, int32_t nOps, uint32_t* final_,

@@ -150,6 +150,8 @@ def test_validation_before_device_work(ccb):
     # one workgroup of 256 threads per 256 counters, fewer than 2^31 workgroups
     assert ccb.ccb_cnt_notify_batch(256, 256, 2**39, 1, 256, 256, 1) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_cnt_notify_batch(None, None, 4, 1, 256, 256, 1) == ccb.CCB_ERR_NULL_POINTER
+    # the error word takes an atomic store: it must be 4-B aligned
+    assert ccb.ccb_cnt_notify_batch(256, 256, 4, 1, 256, 256, 1, err=258) == ccb.CCB_ERR_INVALID_VALUE
 
 
 def test_device_api_test_kernels_built():

@@ -251,6 +251,30 @@ def test_reset_clears_error_word(ccb, wl):
     assert ccb.ccb_syncall_status(ws, 1, None) == (0, [0])
 
 
+def test_status_sums_stripes_of_many_barriers(ccb, wl):
+    """ccb_syncall_status reads each stripe's counter word (not the rest of its
+    line) over 130 barriers, more than one host chunk of 64, and sums the 64
+    stripes of each barrier in int64: barrier 77's stripes hold 2^30 - 1
+    each, a total past 2^31."""
+    nb = 130
+    _say(f"syncall_status over {nb} barriers")
+    ws = wl.workspace(nb)
+    lines = ws.view(-1, 32)
+    b = torch.arange(nb, device="cuda", dtype=torch.int32).repeat_interleave(ccb.CCB_STRIPES)
+    k = torch.arange(ccb.CCB_STRIPES, device="cuda", dtype=torch.int32).repeat(nb)
+    lines[: nb * ccb.CCB_STRIPES, 0] = b * 1000 + k
+    lines[: nb * ccb.CCB_STRIPES, 1:] = -7  # rest of each line: not counted
+    lines[77 * ccb.CCB_STRIPES: 78 * ccb.CCB_STRIPES, 0] = 2**30 - 1
+    st, arr = ccb.ccb_syncall_status(ws, nb, None)
+    assert st == ccb.CCB_OK
+    want = [bb * 1000 * 64 + 63 * 64 // 2 for bb in range(nb)]
+    want[77] = 64 * (2**30 - 1)
+    assert arr == want
+    lines[nb * ccb.CCB_STRIPES, 0] = ccb.CCB_ERR_DEADLOCK
+    st, arr2 = ccb.ccb_syncall_status(ws, nb, None)
+    assert st == ccb.CCB_ERR_DEADLOCK and arr2 == want
+
+
 def test_not_coresident_rejected(ccb, wl):
     _say("barrier_only oversize grid: expect NOT_CORESIDENT, nothing launched")
     ws = wl.workspace(1)
