@@ -21,20 +21,36 @@ HEADERS = [os.path.join(ROOT, "include", "ccb.h"), os.path.join(ROOT, "include",
            os.path.join(CSRC, "ccb_internal.h")]
 
 
+# flags shared by every compile of the kernels (the library and its review)
+CODE_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17",
+    # packed-FP32 instructions stay off for all device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every atomic here is issued by one lane; the wave-level atomic
+    # rewrite would only add a wait on the reply before the barrier's poll
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+]
+
+
 def hipcc_command(out: str, extra=()) -> list:
     return [
-        "hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # packed-FP32 instructions stay off for all device code
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # every atomic here is issued by one lane; the wave-level atomic
-        # rewrite would only add a wait on the reply before the barrier's poll
-        "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
-        "-fvisibility=hidden", "-Wall",
-        "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+        "hipcc", *CODE_FLAGS, "-fPIC", "-shared", "-fvisibility=hidden", "-Wall",
         *extra,
         "-o", out,
         *[os.path.join(CSRC, s) for s in SOURCES],
     ]
+
+
+def device_assembly(out: str) -> str:
+    """Write the gfx950 assembly of the kernels, compiled exactly as in the
+    library, to `out` (for reading the code the library runs)."""
+    cmd = ["hipcc", *CODE_FLAGS, "-S", "--cuda-device-only", "-o", out,
+           os.path.join(CSRC, "ccb_kernels.hip")]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc -S failed:\n" + res.stdout + res.stderr)
+    return out
 
 
 def build(verbose: bool = False) -> str:

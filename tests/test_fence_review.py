@@ -1,0 +1,162 @@
+"""Fence review of the library's own gfx950 code (CPU only, no GPU).
+
+The kernels are compiled to assembly with exactly the library's flags and
+checked against the code sequences of LLVM's AMDGPU memory model for the
+GFX942 family, which gfx950 follows:
+  - a release fence at agent scope is `buffer_wbl2 sc1` (write back L2)
+    followed by `s_waitcnt vmcnt(0)`;
+  - an acquire fence at agent scope is `buffer_inv sc1` (invalidate L2);
+  - a relaxed atomic load or store at agent scope carries `sc1`.
+
+What is checked, for every persistent kernel (barrier-only, witness rounds,
+grouped rounds, stencil; 64 stripes and one counter):
+  - full visibility: the arrival (the returning fetch-add) comes right after
+    a release sequence with no memory access in between, and an acquire
+    follows the poll;
+  - ordering-only visibility: no L2 write-back or invalidate at all (the
+    workgroup's own accesses are waited for instead), the poll loads are
+    agent-scope, and the data the kernel shares across the barrier (witness
+    slots, halo words) is stored with agent-scope stores;
+  - the first poll load goes out only after a wait for the arrival's reply
+    (a poll issued behind the wave's own arrival doubles the barrier's cost);
+and for every kernel in the file: no write through the scalar data cache and
+no packed-FP32 arithmetic.
+"""
+
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+KINDS = ("barrier_only", "slot_rounds", "grouped_rounds", "stencil")
+MEM_PREFIXES = ("global_", "buffer_", "flat_", "scratch_")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    from cross_core_barrier_amd import build
+    out = str(tmp_path_factory.mktemp("isa") / "ccb_kernels.s")
+    build.device_assembly(out)
+    with open(out) as f:
+        return f.read()
+
+
+@pytest.fixture(scope="module")
+def vis_codes():
+    """CCB_VIS_FULL / CCB_VIS_ORDER as the device header defines them."""
+    with open(os.path.join(ROOT, "include", "ccb_device.h")) as f:
+        text = f.read()
+    full = int(re.search(r"CCB_VIS_FULL\s*=\s*(\d+)", text).group(1))
+    order = int(re.search(r"CCB_VIS_ORDER\s*=\s*(\d+)", text).group(1))
+    return {full: "full", order: "order"}
+
+
+def _functions(asm_text):
+    """{mangled name: [instruction lines]} for every function in the file."""
+    parts = re.split(r"\n(_Z\w+):[^\n]*\n", asm_text)
+    out = {}
+    for i in range(1, len(parts) - 1, 2):
+        body = parts[i + 1].split(".Lfunc_end")[0]
+        out[parts[i]] = [l.strip() for l in body.split("\n")
+                         if l.startswith("\t") and l.strip() and not l.strip().startswith((".", ";"))]
+    return out
+
+
+def _persistent(asm_text, vis_codes):
+    """{(kind, stripes, visibility): instructions} of the persistent kernels."""
+    found = {}
+    for name, ins in _functions(asm_text).items():
+        m = re.match(r"_Z\d+ccb_k_(\w+?)ILi(\d+)EL\d+ccbVisibility(\d+)E", name)
+        if m and m.group(1) in KINDS:
+            found[(m.group(1), int(m.group(2)), vis_codes[int(m.group(3))])] = ins
+    return found
+
+
+def _op(line):
+    return line.split()[0]
+
+
+def _is_mem(line):
+    return _op(line).startswith(MEM_PREFIXES)
+
+
+def _arrivals(ins):
+    return [i for i, l in enumerate(ins) if _op(l) == "global_atomic_add" and " sc0" in l]
+
+
+def test_every_persistent_kernel_present(asm, vis_codes):
+    found = _persistent(asm, vis_codes)
+    want = {(k, s, v) for k in KINDS for s in (1, 64) for v in ("full", "order")}
+    assert set(found) == want
+    for key, ins in found.items():
+        assert _arrivals(ins), f"{key}: no returning fetch-add (the arrival)"
+
+
+def test_full_visibility_release_before_arrival_acquire_after_poll(asm, vis_codes):
+    for key, ins in _persistent(asm, vis_codes).items():
+        if key[2] != "full":
+            continue
+        arr = _arrivals(ins)
+        for a in arr:
+            waited = False
+            j = a - 1
+            while j >= 0 and not _is_mem(ins[j]):
+                if _op(ins[j]) == "s_waitcnt" and "vmcnt(0)" in ins[j]:
+                    waited = True
+                j -= 1
+            assert j >= 0 and ins[j] == "buffer_wbl2 sc1", \
+                f"{key}: the access before the arrival is {ins[j] if j >= 0 else None!r}"
+            assert waited, f"{key}: no s_waitcnt vmcnt(0) between the write-back and the arrival"
+        inv = [i for i, l in enumerate(ins) if l == "buffer_inv sc1"]
+        assert inv and max(inv) > min(arr), f"{key}: no agent-scope acquire after the poll"
+
+
+def test_order_visibility_has_no_cache_maintenance(asm, vis_codes):
+    for key, ins in _persistent(asm, vis_codes).items():
+        if key[2] != "order":
+            continue
+        maint = [l for l in ins if _op(l) in ("buffer_wbl2", "buffer_inv")]
+        assert maint == [], f"{key}: {maint}"
+
+
+def test_order_visibility_shares_data_through_agent_scope_accesses(asm, vis_codes):
+    for key, ins in _persistent(asm, vis_codes).items():
+        if key[2] != "order":
+            continue
+        first = min(_arrivals(ins))
+        polls = [l for l in ins[first:] if _op(l).startswith("global_load") and " sc1" in l]
+        assert polls, f"{key}: no agent-scope load after the arrival"
+        if key[0] == "barrier_only":
+            continue  # shares no data
+        # witness slots (rounds kernels), halo words (stencil)
+        stores = [l for l in ins if _op(l).startswith("global_store") and " sc1" in l]
+        assert stores, f"{key}: no agent-scope store for the data shared across the barrier"
+
+
+def test_first_poll_waits_for_the_arrivals_reply(asm, vis_codes):
+    for key, ins in _persistent(asm, vis_codes).items():
+        if key[0] != "barrier_only":
+            continue  # the rounds kernels overlap their own data loads with the arrival
+        for a in _arrivals(ins):
+            j = a + 1
+            waited = False
+            while j < len(ins) and not _is_mem(ins[j]):
+                if _op(ins[j]) == "s_waitcnt" and "vmcnt(0)" in ins[j]:
+                    waited = True
+                j += 1
+            assert j < len(ins) and _op(ins[j]).startswith("global_load") and " sc1" in ins[j], \
+                f"{key}: the access after the arrival is {ins[j] if j < len(ins) else None!r}"
+            assert waited, f"{key}: the first poll does not wait for the arrival's reply"
+
+
+def test_no_scalar_cache_writes_and_no_packed_fp32(asm):
+    banned_prefix = ("s_store", "s_buffer_store", "s_scratch_store", "s_atomic", "s_buffer_atomic",
+                     "s_dcache_wb", "s_dcache_discard")
+    banned = {"v_pk_add_f32", "v_pk_mul_f32", "v_pk_fma_f32"}
+    funcs = _functions(asm)
+    assert len(funcs) >= 20
+    for name, ins in funcs.items():
+        bad = [l for l in ins if _op(l).startswith(banned_prefix) or _op(l) in banned]
+        assert bad == [], f"{name}: {bad[:3]}"
