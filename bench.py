@@ -57,8 +57,9 @@ def parse():
     ap.add_argument("--mode", default="striped-order",
                     choices=["striped-order", "flat-order", "striped-full", "flat-full"])
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
-    ap.add_argument("--only", choices=["stencil"], default=None,
-                    help="run only the copy ceiling and the stencil (counter collection)")
+    ap.add_argument("--only", choices=["counters"], default=None,
+                    help="run only the copy ceiling, the stencil and the batched CntNotify "
+                         "engine (counter collection)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
 
@@ -72,10 +73,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def profiled_traffic():
-    """HBM bytes per stencil launch from the committed rocprofv3 PMC summary,
-    or None when absent or taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", "ccb_k_stencil_counters.md")
+def profiled_traffic(summary: str):
+    """HBM bytes per launch of one kernel from its committed rocprofv3 PMC
+    summary (profiles/<summary>), or None when absent or taken on different
+    kernel sources."""
+    path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -300,7 +302,7 @@ class Bench:
         self.extra["stencil_barriers_per_launch"] = STENCIL_ITERS - 1
         return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": profiled_traffic(), "kernel": "ccb_k_stencil",
+                "traffic": profiled_traffic("ccb_k_stencil_counters.md"), "kernel": "ccb_k_stencil",
                 "launch_ms": round(st_ms, 4), "algorithmic_bytes": alg_bytes,
                 "frac_of_copy_ceiling": round(achieved / copy_gbs, 4) if copy_gbs else None}
 
@@ -356,7 +358,9 @@ class Bench:
         gbs = cnt_bytes / (bms / 1e3) / 1e9
         self.extra["cntnotify_batch"] = {"us_per_launch": round(bms * 1e3, 2), "GBs": round(gbs, 1),
                                          "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-                                         "ops_per_s": round(CNT_COUNTERS * CNT_OPS / (bms / 1e3), 0)}
+                                         "ops_per_s": round(CNT_COUNTERS * CNT_OPS / (bms / 1e3), 0),
+                                         "algorithmic_bytes": cnt_bytes,
+                                         "traffic": profiled_traffic("ccb_k_cnt_batch_counters.md")}
 
     # ------------------------------------------------------------ record + wait in a graph
     def cnt_graph(self):
@@ -493,10 +497,12 @@ def main():
               "(the library runs each grid on a single MI355X)", file=sys.stderr)
         sys.exit(2)
     b = Bench(args)
-    if args.only == "stencil":
+    if args.only == "counters":
         gbs = b.copy_ceiling()
         roof = b.stencil(gbs)
-        print(json.dumps({"copy_512MiB_GBs": round(gbs, 1), "roofline": roof}), flush=True)
+        b.cnt_batch()
+        print(json.dumps({"copy_512MiB_GBs": round(gbs, 1), "roofline": roof,
+                          "cntnotify_batch": b.extra["cntnotify_batch"]}), flush=True)
         return
 
     ms_per_step, rounds = b.headline()

@@ -11,7 +11,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <memory>
 #include <mutex>
+#include <new>
 
 #include "ccb.h"
 #include "ccb_internal.h"
@@ -307,19 +309,21 @@ CCB_API ccbStatus ccb_syncall_status(const int32_t* ws, uint32_t nBarriers, int6
                   hipMemcpyDeviceToHost) != hipSuccess)
         return hip_failed();
     if (arrivals != nullptr) {
-        // only the counter word of each stripe line is read (a strided copy),
-        // kChunk barriers at a time through a fixed host buffer
-        constexpr uint32_t kChunk = 64;
-        int32_t words[kChunk * CCB_STRIPES];
+        // whole stripe lines, kChunk barriers (64 KiB) per plain copy
+        constexpr uint32_t kChunk = 8;
+        constexpr size_t kWords = (size_t)kChunk * CCB_STRIPES * kLineWords;
+        std::unique_ptr<int32_t[]> buf(new (std::nothrow) int32_t[kWords]);
+        if (!buf) return CCB_ERR_RESOURCE_EXHAUSTED;
         for (uint32_t b0 = 0; b0 < nBarriers; b0 += kChunk) {
             const uint32_t nb = nBarriers - b0 < kChunk ? nBarriers - b0 : kChunk;
-            if (hipMemcpy2D(words, sizeof(int32_t), ws + (size_t)b0 * CCB_STRIPES * kLineWords,
-                            CCB_LINE_BYTES, sizeof(int32_t), (size_t)nb * CCB_STRIPES,
-                            hipMemcpyDeviceToHost) != hipSuccess)
+            if (hipMemcpy(buf.get(), ws + (size_t)b0 * CCB_STRIPES * kLineWords,
+                          (size_t)nb * CCB_STRIPES * CCB_LINE_BYTES,
+                          hipMemcpyDeviceToHost) != hipSuccess)
                 return hip_failed();
             for (uint32_t b = 0; b < nb; ++b) {
                 int64_t sum = 0;
-                for (uint32_t k = 0; k < CCB_STRIPES; ++k) sum += words[b * CCB_STRIPES + k];
+                for (uint32_t k = 0; k < CCB_STRIPES; ++k)
+                    sum += buf[((size_t)b * CCB_STRIPES + k) * kLineWords];
                 arrivals[b0 + b] = sum;
             }
         }

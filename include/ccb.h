@@ -174,10 +174,11 @@ CCB_API ccbStatus ccb_syncall_workspace_reset(int32_t* ws, uint32_t nBarriers, c
 /* Wait for `stream`, then read the error word of a workspace of nBarriers
  * barriers and (optionally, arrivals may be NULL) store in arrivals[b] the
  * total number of arrivals on barrier b (the sum of its stripes; int64, as
- * the total of 64 int32 stripes can pass 2^31).  Reads only the counter word
- * of each line, through a fixed-size host buffer.  Returns CCB_OK or
- * CCB_ERR_DEADLOCK, or CCB_ERR_HIP (arrivals may then be partly written).
- * Blocks the host thread. */
+ * the total of 64 int32 stripes can pass 2^31).  Reads the stripe lines a
+ * few barriers at a time through a 64-KiB host buffer.  Returns CCB_OK or
+ * CCB_ERR_DEADLOCK; CCB_ERR_HIP, or CCB_ERR_RESOURCE_EXHAUSTED when the host
+ * buffer cannot be allocated (arrivals may then be partly written).  Blocks
+ * the host thread. */
 CCB_API ccbStatus ccb_syncall_status(const int32_t* ws, uint32_t nBarriers, int64_t* arrivals,
                                      ccbStream stream);
 
