@@ -10,7 +10,8 @@ round: each workgroup stores its witness, all pass the barrier, each sums all
 
 The same run also measures, each on its own stream with HIP events:
   - the floor: dependent agent-scope atomic round trips by one lane
-    (fetch-add and load, with and without fences) and 256-way contention;
+    (fetch-add and load, with and without fences), 256-way contention, and
+    the one-way notification latency between two CUs (ping-pong);
   - barrier-only latency for every barrier variant (slope over rounds), and
     HIP's cooperative-groups grid sync on the same grids for comparison;
   - the 128-member pass and the grouped A/B/mix rounds (512 workgroups);
@@ -191,6 +192,27 @@ class Bench:
         t = tk.cpu().numpy().reshape(-1, 2)
         floor["same_address_fetch_add_ns_at_256"] = round(
             float(t[:, 1].max() - t[:, 0].min()) * self.tick_ns / (2000 * 256), 2)
+        # one CU's update reaching another CU's poll: a ping-pong between
+        # workgroup 0 and workgroup 1 (dealt to another XCD) or 8 (the same XCD)
+        pl = torch.empty(2 * 32, dtype=torch.int32, device=self.dev)
+        pt = torch.zeros(4, dtype=torch.int64, device=self.dev)
+        perr = torch.empty(1, dtype=torch.int32, device=self.dev)
+        notify, iters = {}, 10000
+        for peer in (1, 8):
+            vals = []
+            for _ in range(3):
+                with torch.cuda.stream(stream):
+                    pl.zero_()
+                    perr.zero_()
+                ccb.check(ccb.ccb_bench_notify_pingpong(pl, pt, iters, peer, 0, perr, stream),
+                          "ping-pong")
+                stream.synchronize()
+                assert int(perr.item()) == 0
+                assert int(pl[0].item()) == int(pl[32].item()) == iters
+                t = pt.cpu().numpy()
+                vals.append(float(t[1] - t[0]) * self.tick_ns / (2 * iters))
+            notify["same_xcd" if int(t[2]) == int(t[3]) else "other_xcd"] = round(min(vals), 1)
+        floor["notify_one_way_ns"] = notify
         self.extra["floor"] = floor
         log(f"floor: {floor}")
         return floor
@@ -213,10 +235,17 @@ class Bench:
             lat[name] = round((res[5000] - res[1000]) / 4000 * 1e6, 1)
         self.extra["barrier_only_ns_at_256"] = lat
         best = lat[self.args.mode]
-        self.extra["latency_roofline"] = {
-            "bound": "atomic_round_trip", "achieved_ns_per_barrier": best,
-            "floor_ns": floor["fetch_add_ns"], "ratio": round(best / floor["fetch_add_ns"], 2),
-            "target_ratio": 2.0}
+        roof = {"bound": "atomic_round_trip", "achieved_ns_per_barrier": best,
+                "floor_ns": floor["fetch_add_ns"], "ratio": round(best / floor["fetch_add_ns"], 2),
+                "target_ratio": 2.0}
+        # a poll-based barrier pays at least the arrival's round trip and one
+        # notification (another CU's update reaching this CU's poll)
+        other = floor["notify_one_way_ns"].get("other_xcd")
+        if other is not None:
+            composed = floor["fetch_add_ns"] + other
+            roof.update({"notify_one_way_ns": other, "composed_floor_ns": round(composed, 1),
+                         "ratio_to_composed_floor": round(best / composed, 2)})
+        self.extra["latency_roofline"] = roof
         log(f"barrier-only ns/barrier at 256 WGs: {lat}")
 
     # ------------------------------------------------------------ HIP's own grid barrier

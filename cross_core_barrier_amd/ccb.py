@@ -109,6 +109,8 @@ _f = {
     "ccb_stencil_halo_bytes": _sig("ccb_stencil_halo_bytes", ctypes.c_size_t, _I64, _I32, _I32),
     "ccb_bench_atomic_chain": _sig("ccb_bench_atomic_chain", _I32, _V, _V, _I32, _I32, _I32, _V),
     "ccb_bench_atomic_contended": _sig("ccb_bench_atomic_contended", _I32, _V, _V, _I32, _I32, _V),
+    "ccb_bench_notify_pingpong": _sig("ccb_bench_notify_pingpong", _I32, _V, _V, _I32, _I32,
+                                      _U32, _V, _V),
     "ccb_bench_hip_grid_sync": _sig("ccb_bench_hip_grid_sync", _I32, _I32, _I32, _I32, _V, _V),
     "ccb_bench_copy": _sig("ccb_bench_copy", _I32, _V, _V, _I64, _V),
     "ccb_cnt_notify_create": _sig("ccb_cnt_notify_create", _I32, _V, _U64),
@@ -217,6 +219,11 @@ def ccb_bench_atomic_chain(line, ticks, iters, fenced=0, kind=0, stream=None) ->
 
 def ccb_bench_atomic_contended(line, ticks, iters, n_grid, stream=None) -> int:
     return _f["ccb_bench_atomic_contended"](_p(line), _p(ticks), iters, n_grid, _s(stream))
+
+
+def ccb_bench_notify_pingpong(lines, ticks_out, iters, peer, max_poll, err, stream=None) -> int:
+    return _f["ccb_bench_notify_pingpong"](_p(lines), _p(ticks_out), iters, peer, max_poll, _p(err),
+                                           _s(stream))
 
 
 def ccb_bench_hip_grid_sync(rounds, n_grid, threads, done_out, stream=None) -> int:

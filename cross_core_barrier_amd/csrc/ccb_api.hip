@@ -456,6 +456,20 @@ CCB_API ccbStatus ccb_bench_atomic_contended(int32_t* line, uint64_t* ticksOut, 
                                                  (hipStream_t)stream));
 }
 
+CCB_API ccbStatus ccb_bench_notify_pingpong(int32_t* lines, uint64_t* ticksOut, int32_t iters,
+                                           int32_t peer, uint32_t maxPoll, int32_t* err,
+                                           ccbStream stream)
+{
+    if (lines == nullptr || ticksOut == nullptr || err == nullptr) return CCB_ERR_NULL_POINTER;
+    if (iters < 1 || peer < 1 || peer > 255 || !aligned(lines, CCB_LINE_BYTES) ||
+        !aligned(ticksOut, 8) || !aligned(err, 4))
+        return CCB_ERR_INVALID_VALUE;
+    ccbStatus st = current_device(nullptr, nullptr);
+    if (st != CCB_OK) return st;
+    return from_hip(ccb::launch_notify_pingpong(lines, ticksOut, iters, peer, poll_bound(maxPoll),
+                                                err, (hipStream_t)stream));
+}
+
 CCB_API ccbStatus ccb_bench_hip_grid_sync(int32_t rounds, int32_t nGrid, int32_t threads,
                                           int32_t* doneOut, ccbStream stream)
 {

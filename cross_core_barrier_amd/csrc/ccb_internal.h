@@ -57,6 +57,8 @@ hipError_t launch_atomic_chain(int32_t* line, uint64_t* ticks, int32_t iters, in
                                int32_t kind, hipStream_t s);
 hipError_t launch_atomic_contended(int32_t* line, uint64_t* ticks, int32_t iters, int32_t nGrid,
                                    hipStream_t s);
+hipError_t launch_notify_pingpong(int32_t* lines, uint64_t* ticks, int32_t iters, int32_t peer,
+                                  uint32_t maxPoll, int32_t* err, hipStream_t s);
 hipError_t launch_hip_grid_sync(int32_t rounds, int32_t nGrid, int32_t threads, int32_t* done,
                                 int numCUs, hipStream_t s);
 hipError_t launch_copy(int4* dst, const int4* src, int64_t n16, int nBlocks, hipStream_t s);

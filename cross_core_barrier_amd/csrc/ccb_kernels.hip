@@ -1110,6 +1110,48 @@ __global__ void ccb_k_atomic_contended(int32_t* line, uint64_t* ticks, int32_t i
     if (v == 0x7fffffff) ticks[2 * blockIdx.x] = 0;
 }
 
+// Notification ping-pong: workgroup 0 and workgroup `peer` (one wave each)
+// take turns.  Round i: workgroup 0 adds one to line A and polls line B until
+// it holds i; the partner polls A until it holds i, then adds one to B.  The
+// update is the barrier's arrival (an agent-scope fetch-add) and the wait is
+// its poll (agent-scope loads with the same back-off), so each round trip is
+// two notifications: one CU's update reaching another CU's poll.  Every wait
+// is bounded by maxPoll (then the error word gets CCB_ERR_DEADLOCK and both
+// sides stop).  ticks: start and end on workgroup 0's clock, then the XCC id
+// of workgroup 0 and of the partner.
+__global__ void ccb_k_notify_pingpong(int32_t* lines, uint64_t* ticks, int32_t iters,
+                                      int32_t peer, uint32_t maxPoll, int32_t* err)
+{
+    const int32_t w = (int32_t)blockIdx.x;
+    if (!leader() || (w != 0 && w != peer)) return;
+    int32_t* const a = lines;
+    int32_t* const b = lines + CCB_LINE_WORDS;
+    int32_t* const watched = w == 0 ? b : a;
+    bool bad = false;
+    const uint64_t t0 = wall_clock64();
+    for (int32_t i = 1; i <= iters && !bad; ++i) {
+        if (w == 0) __hip_atomic_fetch_add(a, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t polls = 0;
+        while (__hip_atomic_load(watched, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < i) {
+            if (++polls >= maxPoll) {
+                bad = true;
+                break;
+            }
+            if (CCB_POLL_SLEEP > 0) __builtin_amdgcn_s_sleep(CCB_POLL_SLEEP);
+        }
+        if (w != 0 && !bad) __hip_atomic_fetch_add(b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const uint64_t t1 = wall_clock64();
+    if (w == 0) {
+        ticks[0] = t0;
+        ticks[1] = t1;
+    }
+    ticks[w == 0 ? 2 : 3] = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // XCC_ID
+    if (bad)
+        __hip_atomic_store(err, (int32_t)CCB_ERR_DEADLOCK, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // HIP's own grid barrier (cooperative groups' grid sync), `rounds` times in a
 // row: the platform's stock answer to the same problem, timed beside ours.
 // Workgroup 0 writes `rounds` to *done once it has passed the last one.
@@ -1297,6 +1339,16 @@ hipError_t launch_atomic_contended(int32_t* line, uint64_t* ticks, int32_t iters
     void* args[] = {&line, &ticks, &iters, &zero};
     return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&ccb_k_atomic_contended),
                                       dim3(nGrid), dim3(kWave), args, 0, s);
+}
+
+hipError_t launch_notify_pingpong(int32_t* lines, uint64_t* ticks, int32_t iters, int32_t peer,
+                                  uint32_t maxPoll, int32_t* err, hipStream_t s)
+{
+    // the two sides wait on each other: a cooperative launch guarantees that
+    // all peer + 1 one-wave workgroups are resident together
+    void* args[] = {&lines, &ticks, &iters, &peer, &maxPoll, &err};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&ccb_k_notify_pingpong),
+                                      dim3(peer + 1), dim3(kWave), args, 0, s);
 }
 
 hipError_t launch_hip_grid_sync(int32_t rounds, int32_t nGrid, int32_t threads, int32_t* done,

@@ -301,6 +301,28 @@ CCB_API ccbStatus ccb_bench_atomic_chain(int32_t* line, uint64_t* ticksOut, int3
 CCB_API ccbStatus ccb_bench_atomic_contended(int32_t* line, uint64_t* ticksOut, int32_t iters,
                                              int32_t nGrid, ccbStream stream);
 
+/* Notification ping-pong between two workgroups: the time one CU's update
+ * takes to reach another CU's poll, the step a barrier cannot avoid.
+ * Workgroups 0 and `peer` (1..255) of a cooperative launch of peer + 1
+ * one-wave workgroups take `iters` turns: workgroup 0 adds one to the int32
+ * at byte 0 of lines (line A) and polls line B (byte 128) until it holds the
+ * turn; the partner polls A, then adds one to B.  Both use the barrier's
+ * arrival (agent-scope fetch-add) and poll (agent-scope loads, same back-off).
+ *   lines     device, 2 x 128 B, 128-B aligned, zeroed by the caller; both
+ *             words equal iters afterwards
+ *   ticksOut  device, 4 uint64: start and end on workgroup 0's wall clock
+ *             (rate from ccb_device_info), then the XCC (XCD) id of workgroup
+ *             0 and of workgroup `peer`.  One-way latency = (end - start) /
+ *             (2 * iters) ticks.
+ *   maxPoll   bound on each wait (0: CCB_SOFT_MAX_POLL); past it *err (device
+ *             int32, zeroed by the caller) gets CCB_ERR_DEADLOCK and both
+ *             sides stop.
+ * Errors: NULL_POINTER, INVALID_VALUE (iters < 1, peer outside 1..255,
+ * misaligned lines, ticksOut or err), NOT_CORESIDENT. */
+CCB_API ccbStatus ccb_bench_notify_pingpong(int32_t* lines, uint64_t* ticksOut, int32_t iters,
+                                           int32_t peer, uint32_t maxPoll, int32_t* err,
+                                           ccbStream stream);
+
 /* HIP's cooperative-groups grid barrier (grid_group::sync) `rounds` times in
  * one cooperative launch of nGrid workgroups of `threads` threads (a
  * multiple of 64, at most 1024): the platform's stock grid barrier, for

@@ -141,6 +141,14 @@ def test_validation_before_device_work(ccb):
     assert ccb.ccb_bench_atomic_chain(None, 256, 1) == ccb.CCB_ERR_NULL_POINTER
     assert ccb.ccb_bench_atomic_chain(128, 256, 0) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_bench_copy(256, 512, 17) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_bench_notify_pingpong(None, 256, 1, 1, 0, 256) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_bench_notify_pingpong(256, 256, 1, 1, 0, None) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_bench_notify_pingpong(256, 256, 0, 1, 0, 256) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_bench_notify_pingpong(256, 256, 1, 0, 0, 256) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_bench_notify_pingpong(256, 256, 1, 256, 0, 256) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_bench_notify_pingpong(192, 256, 1, 1, 0, 256) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_bench_notify_pingpong(256, 260, 1, 1, 0, 256) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_bench_notify_pingpong(256, 256, 1, 1, 0, 258) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_bench_hip_grid_sync(1, 8, 64, None) == ccb.CCB_ERR_NULL_POINTER
     assert ccb.ccb_bench_hip_grid_sync(0, 8, 64, 256) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_bench_hip_grid_sync(1, 0, 64, 256) == ccb.CCB_ERR_INVALID_VALUE

@@ -50,6 +50,38 @@ def test_atomic_contended(ccb):
     assert np.all(t[:, 1] > t[:, 0])
 
 
+@pytest.mark.parametrize("peer", [1, 8, 255])
+def test_notify_pingpong(ccb, peer):
+    iters = 2000
+    _say(f"notify ping-pong workgroups 0 and {peer}, {iters} turns")
+    lines = torch.zeros(64, dtype=torch.int32, device="cuda")
+    ticks = torch.zeros(4, dtype=torch.int64, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ccb.check(ccb.ccb_bench_notify_pingpong(lines, ticks, iters, peer, 0, err), "ping-pong")
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert int(lines[0].item()) == iters and int(lines[32].item()) == iters
+    assert int(lines[1:32].abs().sum().item()) == 0 and int(lines[33:].abs().sum().item()) == 0
+    t = ticks.cpu().numpy()
+    assert t[1] > t[0] > 0
+    assert 0 <= t[2] < 8 and 0 <= t[3] < 8  # XCC ids
+
+
+def test_notify_pingpong_forced_deadlock(ccb):
+    """Line B preset to -5: after the partner's first turn it holds -4, so
+    workgroup 0 never sees turn 1 and the partner never sees turn 2.  Both
+    waits run out after maxPoll polls and report DEADLOCK; nothing hangs."""
+    _say("notify ping-pong forced deadlock, maxPoll=2000")
+    lines = torch.zeros(64, dtype=torch.int32, device="cuda")
+    lines[32] = -5
+    ticks = torch.zeros(4, dtype=torch.int64, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ccb.check(ccb.ccb_bench_notify_pingpong(lines, ticks, 10, 1, 2000, err), "ping-pong")
+    torch.cuda.synchronize()
+    assert int(err.item()) == ccb.CCB_ERR_DEADLOCK
+    assert int(lines[0].item()) == 1 and int(lines[32].item()) == -4
+
+
 @pytest.mark.parametrize("n_words", [4, 4 * 1000003, 1 << 24])
 def test_copy_bit_exact(ccb, n_words):
     _say(f"copy {n_words * 4} bytes")
