@@ -179,6 +179,12 @@ ccbStatus plan_persistent(ccb::KernelId id, int32_t mode, int32_t nGrid, int32_t
     return CCB_OK;
 }
 
+// Held from plan_persistent's setting of a kernel's dynamic-LDS limit (a
+// process-wide attribute) until that kernel is enqueued, so that concurrent
+// launches of one kernel with different wgsPerCu cannot each launch under the
+// other's limit.  Launches only enqueue, so the hold is short.
+std::mutex g_launch_mu;
+
 inline uint32_t poll_bound(uint32_t maxPoll) { return maxPoll == 0 ? CCB_SOFT_MAX_POLL : maxPoll; }
 
 // The counters are int32 (SYNCALL guide §4.1): a stripe stays valid while
@@ -344,6 +350,7 @@ CCB_API ccbStatus ccb_run_barrier_only(int32_t* ws, uint32_t* placement, int32_t
         usedCores < 0 || usedCores > nGrid || wgsPerCu < 0 || !valid_mode(mode) ||
         !counts_fit(rounds, usedCores != 0 ? usedCores : nGrid, mode))
         return CCB_ERR_INVALID_VALUE;
+    std::lock_guard<std::mutex> lk(g_launch_mu);
     ccb::LaunchShape ls;
     ccbStatus st = plan_persistent(ccb::KernelId::BarrierOnly, mode, nGrid, threads, wgsPerCu,
                                    (hipStream_t)stream, &ls);
@@ -365,6 +372,7 @@ CCB_API ccbStatus ccb_run_slot_rounds(int32_t* ws, uint32_t* slots, uint32_t* ou
         usedCores < 0 || usedCores > nGrid || wgsPerCu < 0 || !valid_mode(mode) ||
         !counts_fit(rounds, usedCores != 0 ? usedCores : nGrid, mode))
         return CCB_ERR_INVALID_VALUE;
+    std::lock_guard<std::mutex> lk(g_launch_mu);
     ccb::LaunchShape ls;
     ccbStatus st = plan_persistent(ccb::KernelId::SlotRounds, mode, nGrid, threads, wgsPerCu,
                                    (hipStream_t)stream, &ls);
@@ -385,6 +393,7 @@ CCB_API ccbStatus ccb_run_grouped_rounds(int32_t* ws, uint32_t* slots, uint32_t*
         !valid_threads(threads) || wgsPerCu < 0 || !valid_mode(mode) ||
         !counts_fit(((int64_t)rounds + 2) / 3, nGrid, mode))  // the mix counter fills first
         return CCB_ERR_INVALID_VALUE;
+    std::lock_guard<std::mutex> lk(g_launch_mu);
     ccb::LaunchShape ls;
     ccbStatus st = plan_persistent(ccb::KernelId::GroupedRounds, mode, nGrid, threads, wgsPerCu,
                                    (hipStream_t)stream, &ls);
@@ -421,6 +430,7 @@ CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32
     const uintptr_t a0 = (uintptr_t)bufA, a1 = a0 + (uintptr_t)n * 4;
     const uintptr_t b0 = (uintptr_t)bufB, b1 = b0 + (uintptr_t)n * 4;
     if (a0 < b1 && b0 < a1) return CCB_ERR_INVALID_VALUE;  // overlapping buffers
+    std::lock_guard<std::mutex> lk(g_launch_mu);
     ccb::LaunchShape ls;
     ccbStatus st = plan_persistent(ccb::KernelId::Stencil, mode, nGrid, threads, wgsPerCu,
                                    (hipStream_t)stream, &ls);

@@ -21,6 +21,9 @@
  *   - ccbStream is a hipStream_t passed as an opaque pointer; NULL is the
  *     default (null) stream ([CNTNOTIFY] §5).  Calls that take a stream only
  *     enqueue work on it and return without waiting, unless stated otherwise.
+ *   - Every call may be made from several host threads at once (the
+ *     library's own state -- device table, register query, launch planning,
+ *     CntNotify handle table -- is guarded by mutexes).
  *   - Calls act on the HIP device that is current on the calling thread.
  *     That device must be a gfx950 GPU, else CCB_ERR_UNSUPPORTED_DEVICE.
  *   - Arguments are validated before anything is enqueued; on an error

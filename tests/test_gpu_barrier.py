@@ -275,6 +275,42 @@ def test_status_sums_stripes_of_many_barriers(ccb, wl):
     assert st == ccb.CCB_ERR_DEADLOCK and arr2 == want
 
 
+def test_concurrent_launches_from_host_threads(ccb, wl):
+    """Four host threads, each with its own stream and workspace, launch
+    barrier-only grids over and over with different wgsPerCu (so each sets
+    the kernel's dynamic-LDS limit differently) and barrier variants.  Every
+    launch is accepted and every count is exact.  The grids are small enough
+    (16 workgroups) that all four fit on the device together."""
+    import threading
+    _say("barrier_only from 4 host threads x 20 launches, 16 WGs each")
+    n, rounds, reps = 16, 500, 20
+    wss = [wl.workspace(1) for _ in range(4)]
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    torch.cuda.synchronize()
+    results = [[] for _ in range(4)]
+
+    def worker(t):
+        for i in range(reps):
+            mode = MODES[(t + i) % 4]
+            st = ccb.ccb_syncall_workspace_reset(wss[t], 1, streams[t])
+            if st == 0:
+                st = ccb.ccb_run_barrier_only(wss[t], None, None, rounds, n, 64, 0, 1 + t, 0,
+                                              mode, streams[t])
+            got = ccb.ccb_syncall_status(wss[t], 1, streams[t]) if st == 0 else (st, None)
+            results[t].append((st, got))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not any(th.is_alive() for th in threads)
+    for t in range(4):
+        assert len(results[t]) == reps
+        for st, got in results[t]:
+            assert st == 0 and got == (0, [rounds * n]), (t, st, got)
+
+
 def test_not_coresident_rejected(ccb, wl):
     _say("barrier_only oversize grid: expect NOT_CORESIDENT, nothing launched")
     ws = wl.workspace(1)
