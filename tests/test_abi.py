@@ -88,9 +88,18 @@ def test_constants_match_pages(ccb):
     text = open(os.path.join(INCLUDE, "ccb.h")).read()
     m = re.search(r"#define CCB_SOFT_MAX_POLL (\d+)u", text)
     assert int(m.group(1)) == consts["soft_max_poll_iterations"] == ccb.CCB_SOFT_MAX_POLL
-    for name in ("CCB_STRIPES", "CCB_SLOT_ROWS", "CCB_SLOT_WORDS", "CCB_LINE_BYTES"):
-        m = re.search(r"#define %s (\d+)" % name, text)
-        assert m and int(m.group(1)) == getattr(ccb, name), name
+    # every numeric constant of the header that the binding mirrors
+    defines = {m.group(1): int(m.group(2))
+               for m in re.finditer(r"#define (CCB_\w+) (\d+)u?\s*$", text, re.M)}
+    enums = {**_header_enum("CCB_BARRIER_"), **_header_enum("CCB_VISIBILITY_"),
+             **_header_enum("CCB_CNT_RECORD_"), **_header_enum("CCB_CNT_WAIT_")}
+    for name in ("CCB_STRIPES", "CCB_SLOT_ROWS", "CCB_SLOT_WORDS", "CCB_LINE_BYTES",
+                 "CCB_CNT_NOTIFY_POOL", "CCB_SOFT_MAX_POLL"):
+        assert defines.get(name) == getattr(ccb, name), name
+    assert len(enums) == 13
+    for name, val in enums.items():
+        assert getattr(ccb, name) == val, name
+    assert ccb.MODES == {"striped-order": 0, "flat-order": 1, "striped-full": 2, "flat-full": 3}
     assert ccb.ccb_syncall_workspace_bytes(1) == (ccb.CCB_STRIPES + 1) * 128
     assert ccb.ccb_syncall_workspace_bytes(3) == (3 * ccb.CCB_STRIPES + 1) * 128
     # 2^26 elements in chunks of 1024, 1024 workgroups: 64 chunks each
