@@ -275,6 +275,30 @@ def test_status_sums_stripes_of_many_barriers(ccb, wl):
     assert st == ccb.CCB_ERR_DEADLOCK and arr2 == want
 
 
+@pytest.mark.parametrize("raw", [False, True], ids=["torch-stream", "raw-handle"])
+def test_helpers_on_a_side_stream(ccb, wl, raw):
+    """The torch-side helpers order their launches on a caller's stream after
+    their own fills, and the caller's current stream after the launch."""
+    _say(f"helpers on a side stream (raw handle: {raw})")
+    s = torch.cuda.Stream()
+    arg = s.cuda_stream if raw else s
+    res = wl.slot_rounds(0, 100, 8, 64, stream=arg)
+    want_out, _, want_ctr, rc = _oracle_slot(0, 100, 8, 0)
+    assert rc == 0 and res.status == 0 and res.counters == [want_ctr]
+    assert np.array_equal(_u32(res.out), want_out)
+    from cross_core_barrier_amd import inputs
+    x = inputs.stencil_input(2, 70_001)
+    st, y = wl.stencil(torch.from_numpy(x).cuda(), 5, 16, 128, stream=arg)
+    assert st == 0 and np.array_equal(y.cpu().numpy(), oracle.stencil(x, 5))
+    val, meta, rows = inputs.cnt_batch_input(3, 4100, 16, small_values=True)
+    err, final, rel = wl.cnt_batch(torch.from_numpy(val.view(np.int32)).cuda(),
+                                   torch.from_numpy(meta).cuda(), rows, stream=arg)
+    want_final, want_rel, rc = oracle.cnt_batch(val, meta, rows)
+    assert rc == 0 and int(err.item()) == 0
+    assert np.array_equal(final.cpu().numpy().view(np.uint32), want_final)
+    assert np.array_equal(rel.cpu().numpy(), want_rel)
+
+
 def test_concurrent_launches_from_host_threads(ccb, wl):
     """Four host threads, each with its own stream and workspace, launch
     barrier-only grids over and over with different wgsPerCu (so each sets
