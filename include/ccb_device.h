@@ -131,7 +131,8 @@ struct ccb_no_overlap {
  * the round from it, epoch = before / n_s + 1 with n_s the stripe's member
  * count, and polls until every stripe l in use holds at least epoch * n_l
  * arrivals (for K = 1: the counter reaches (before / n + 1) * n, the
- * pages' target); the first poll is issued before `before` is waited for,
+ * pages' target); the first poll goes out only once `before` is back (a
+ * poll issued behind the wave's own arrival doubles the barrier's cost),
  * and the arrival's own stripe also counts as complete once before + 1
  * reaches its target.  At most maxPoll polls; past that it stores
  * CCB_ERR_DEADLOCK in the error word and returns it.  Every 64th poll it
