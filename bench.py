@@ -473,7 +473,7 @@ class Bench:
         import oracle
         cfg = self.inputs.WITNESS_GRID
         reps, t_cpu = 0, 0.0
-        while t_cpu < 10.0 and reps < 30:
+        while t_cpu < 10.0 and reps < 1000:  # about 10 s of oracle work
             t1 = time.perf_counter()
             _, _, ctr, rc = oracle.slot_rounds(cfg["seed"], cfg["rounds"], cfg["n_wg"], 0)
             t_cpu += time.perf_counter() - t1
