@@ -797,28 +797,39 @@ __device__ __forceinline__ bool cnt_step(uint32_t& c, uint32_t m, uint32_t v, bo
     return false;
 }
 
-// A record op in the form the fast path below uses: with the code clamped to
-// t <= 31, the new count is (c & X) + (v & Y), X = (v & A) ^ B, where A, B
-// and Y are bit t of three tables, sign-extended to 0 or ~0:
+// A record op in the form the fast path below uses: the new count is
+// (c & X) + (v & Y), X = (v & A) ^ B, with masks A, B, Y of 0 or ~0 chosen
+// by the code:
 //   SET (0): A = 0,  B = 0,  Y = ~0  ->  v
 //   ADD (1): A = 0,  B = ~0, Y = ~0  ->  c + v
 //   OR  (2): A = ~0, B = ~0, Y = ~0  ->  (c & ~v) + v = c | v
 //   AND (4): A = ~0, B = 0,  Y = 0   ->  c & v
-// and every other code (3, 5-7, or a clear or reserved bit set, which
-// clamps to a code of 8 or more) A = 0, B = ~0, Y = 0: the count is kept.
-// seen collects 1 << t, so that a code outside {0, 1, 2, 4} is reported
-// once at the end instead of being tested on every op.
-constexpr uint32_t kRecA = 0x14u, kRecB = 0xFFFFFFEEu, kRecY = 0x07u, kRecValid = 0x17u;
+// and the codes 3, 5, 6, 7: A = 0, B = ~0, Y = 0, the count is kept (they
+// are reported once at the end instead of being tested on every op).
+//
+// For rows whose op bytes are all below 8 (a record code and no clear or
+// reserved bit), the four counters of a lane look their masks up together:
+// v_perm_b32 with the op word as selector picks byte `code` of an 8-byte
+// table (0x00 or 0xFF) for each counter, and each byte is then used sign-
+// extended (an SDWA operand) as that counter's 32-bit mask.  A fourth table
+// flags the codes that are not records (3, 5, 6, 7).  Table bytes for codes
+// 0..7, low dword first (the perm selector's order):
+//   A: 00 00 FF 00 | FF 00 00 00     B: 00 FF FF FF | 00 FF FF FF
+//   Y: FF FF FF 00 | 00 00 00 00     invalid: 00 00 00 FF | 00 FF FF FF
+constexpr uint32_t kPermA[2] = {0x00FF0000u, 0x000000FFu};
+constexpr uint32_t kPermB[2] = {0xFFFFFF00u, 0xFFFFFF00u};
+constexpr uint32_t kPermY[2] = {0x00FFFFFFu, 0x00000000u};
+constexpr uint32_t kPermBad[2] = {0xFF000000u, 0xFFFFFF00u};
 
-__device__ __forceinline__ uint32_t cnt_record_fast(uint32_t c, uint32_t b, uint32_t v,
-                                                    uint32_t& seen)
+__device__ __forceinline__ uint32_t perm_table(const uint32_t (&t)[2], uint32_t sel)
 {
-    const uint32_t t = b < 31u ? b : 31u;
-    const uint32_t a = (uint32_t)__builtin_amdgcn_sbfe((int)kRecA, t, 1u);
-    const uint32_t bb = (uint32_t)__builtin_amdgcn_sbfe((int)kRecB, t, 1u);
-    const uint32_t y = (uint32_t)__builtin_amdgcn_sbfe((int)kRecY, t, 1u);
-    seen |= 1u << t;
-    return (c & ((v & a) ^ bb)) + (v & y);
+    return __builtin_amdgcn_perm(t[1], t[0], sel);
+}
+
+// byte i of p, sign-extended: 0x00 -> 0, 0xFF -> ~0
+__device__ __forceinline__ uint32_t byte_mask(uint32_t p, int i)
+{
+    return (uint32_t)(int32_t)(int8_t)(uint8_t)(p >> (8 * i));
 }
 
 // A wait op in the form the fast path below uses.  With
@@ -880,18 +891,25 @@ __global__ __launch_bounds__(256) void ccb_k_cnt_batch(const uint32_t* __restric
 #pragma unroll
     for (int i = 0; i < C; ++i) c[i] = 0u, j[i] = 0;
     bool bad = false;
-    uint32_t seen[C], seenW[C];
+    uint32_t recBad = 0;  // invalid record codes seen by the fast path
+    uint32_t seenW[C];
 #pragma unroll
-    for (int i = 0; i < C; ++i) seen[i] = 1u, seenW[i] = 1u;
+    for (int i = 0; i < C; ++i) seenW[i] = 1u;
     constexpr uint32_t kWaitBits = C == 4 ? 0x80808080u : (C == 2 ? 0x8080u : 0x80u);
+    constexpr uint32_t kHighBits = C == 4 ? 0xF8F8F8F8u : (C == 2 ? 0xF8F8u : 0xF8u);
     auto apply = [&](uint32_t m, VT v) {
-        const uint32_t waits = m & kWaitBits;
-        if (!__any(waits != 0)) {
-            // no wait in this op anywhere in the wave: records only
+        if (!__any((m & kHighBits) != 0)) {
+            // every op of the wave is a record with a code below 8
+            const uint32_t pA = perm_table(kPermA, m), pB = perm_table(kPermB, m);
+            const uint32_t pY = perm_table(kPermY, m);
+            recBad |= perm_table(kPermBad, m);
 #pragma unroll
-            for (int i = 0; i < C; ++i) c[i] = cnt_record_fast(c[i], (m >> (8 * i)) & 0xffu, v[i], seen[i]);
+            for (int i = 0; i < C; ++i)
+                c[i] = (c[i] & ((v[i] & byte_mask(pA, i)) ^ byte_mask(pB, i))) +
+                       (v[i] & byte_mask(pY, i));
             return;
         }
+        const uint32_t waits = m & kWaitBits;
         bool oneRow = true;
 #pragma unroll
         for (int i = 1; i < C; ++i) oneRow = oneRow && j[i] == j[0];
@@ -980,10 +998,12 @@ __global__ __launch_bounds__(256) void ccb_k_cnt_batch(const uint32_t* __restric
         apply(m, v);
     }
     VT out;
+    // the perm of a C < 4 op word also reads its zero high bytes (code 0, valid)
+    bad = bad || recBad != 0;
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         out[i] = c[i];
-        bad = bad || (seen[i] & ~kRecValid) != 0 || (seenW[i] & ~kWaitValid) != 0;
+        bad = bad || (seenW[i] & ~kWaitValid) != 0;
     }
     *reinterpret_cast<VT*>(finalOut + c0) = out;
     if (bad && err != nullptr)
