@@ -12,8 +12,9 @@ The same run also measures, each on its own stream with HIP events:
   - the floor: dependent agent-scope atomic round trips by one lane
     (fetch-add and load, with and without fences), 256-way contention, and
     the one-way notification latency between two CUs (ping-pong);
-  - barrier-only latency for every barrier variant (slope over rounds), and
-    HIP's cooperative-groups grid sync on the same grids for comparison;
+  - barrier-only latency for every barrier variant (slope over rounds), the
+    chosen variant from 2 to 1024 workgroups, and HIP's cooperative-groups
+    grid sync on the same grids for comparison;
   - the 128-member pass and the grouped A/B/mix rounds (512 workgroups);
   - the persistent stencil (2^26 int32, 64 iterations, 1024 workgroups):
     the HBM roofline of the data phases;
@@ -234,6 +235,23 @@ class Bench:
             ccb.check(st, "barrier_only status")
             lat[name] = round((res[5000] - res[1000]) / 4000 * 1e6, 1)
         self.extra["barrier_only_ns_at_256"] = lat
+        # the chosen variant against the number of workgroups (256 threads each)
+        by_n = {}
+        m = ccb.MODES[self.args.mode]
+        for n in (2, 8, 64, 256, 512, 1024):
+            res = {}
+            for r in (1000, 5000):
+                def f(r=r, n=n):
+                    ccb.check(ccb.ccb_syncall_workspace_reset(ws, 1, stream), "reset")
+                    ccb.check(ccb.ccb_run_barrier_only(ws, None, None, r, n, 256, 0, 0, 0, m,
+                                                       stream), "barrier_only")
+                f()
+                res[r] = min(self.timer(f) for _ in range(3))
+            st, arr = ccb.ccb_syncall_status(ws, 1, stream)
+            ccb.check(st, "barrier_only status")
+            assert arr == [5000 * n], arr
+            by_n[str(n)] = round((res[5000] - res[1000]) / 4000 * 1e6, 1)
+        self.extra["barrier_only_ns_by_workgroups"] = by_n
         best = lat[self.args.mode]
         roof = {"bound": "atomic_round_trip", "achieved_ns_per_barrier": best,
                 "floor_ns": floor["fetch_add_ns"], "ratio": round(best / floor["fetch_add_ns"], 2),
