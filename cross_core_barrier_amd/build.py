@@ -36,6 +36,7 @@ CODE_FLAGS = [
 def hipcc_command(out: str, extra=()) -> list:
     return [
         "hipcc", *CODE_FLAGS, "-fPIC", "-shared", "-fvisibility=hidden", "-Wall",
+        "-Wl,-soname,libccb.so",
         *extra,
         "-o", out,
         *[os.path.join(CSRC, s) for s in SOURCES],
