@@ -198,8 +198,8 @@ class Bench:
         pl = torch.empty(2 * 32, dtype=torch.int32, device=self.dev)
         pt = torch.zeros(4, dtype=torch.int64, device=self.dev)
         perr = torch.empty(1, dtype=torch.int32, device=self.dev)
-        notify, iters = {}, 10000
-        for peer in (1, 8):
+        iters, same, other = 10000, [], []
+        for peer in range(1, 9):  # workgroups are dealt to the XCDs in turn
             vals = []
             for _ in range(3):
                 with torch.cuda.stream(stream):
@@ -212,7 +212,13 @@ class Bench:
                 assert int(pl[0].item()) == int(pl[32].item()) == iters
                 t = pt.cpu().numpy()
                 vals.append(float(t[1] - t[0]) * self.tick_ns / (2 * iters))
-            notify["same_xcd" if int(t[2]) == int(t[3]) else "other_xcd"] = round(min(vals), 1)
+            (same if int(t[2]) == int(t[3]) else other).append(min(vals))
+        notify = {}
+        if other:  # the median over the partner XCDs, and their range
+            notify["other_xcd"] = round(statistics.median(other), 1)
+            notify["other_xcd_range"] = [round(min(other), 1), round(max(other), 1)]
+        if same:
+            notify["same_xcd"] = round(statistics.median(same), 1)
         floor["notify_one_way_ns"] = notify
         self.extra["floor"] = floor
         log(f"floor: {floor}")
