@@ -511,7 +511,8 @@ class Bench:
 
     def cpu_context(self):
         """Context beside the GPU figures (not baselines): the epoch barrier on
-        host threads, and the oracle's stencil and batch engine on one core."""
+        host threads, and the oracle's stencil and batch engine on one core and
+        on the host threads this GPU's share allows."""
         import oracle
         nproc = os.cpu_count() or 1
         model = ""
@@ -525,21 +526,50 @@ class Bench:
         assert rc == 0
         x = self.inputs.stencil_input(self.inputs.STENCIL["seed"], STENCIL_N)
         t1 = time.perf_counter()
-        oracle.stencil(x, 1)
+        y1 = oracle.stencil(x, 1)
         st_s = time.perf_counter() - t1
         c = self.inputs.CNT_BATCH
         val, meta, rows = self.inputs.cnt_batch_input(c["seed"], CNT_COUNTERS, CNT_OPS)
         t1 = time.perf_counter()
-        _, _, rc = oracle.cnt_batch(val, meta, rows)
+        fin1, _, rc = oracle.cnt_batch(val, meta, rows)
         cb_s = time.perf_counter() - t1
         assert rc == 0
         cnt_bytes = val.nbytes + meta.nbytes + CNT_COUNTERS * 4 + rows * CNT_COUNTERS
+        # the same oracle calls on `threads` host threads (the C oracle runs
+        # without the GIL): the stencil on slices with one element of halo on
+        # each side (the slice ends are discarded, the array's own ends keep
+        # their clamp), the batch engine on column ranges of its independent
+        # counters.  The pieces must reproduce the one-thread results.
+        from concurrent.futures import ThreadPoolExecutor
+        np = self.np
+        sb = np.linspace(0, STENCIL_N, threads + 1).astype(np.int64)
+
+        def st_part(i):
+            a, b = int(sb[i]), int(sb[i + 1])
+            lo, hi = max(a - 1, 0), min(b + 1, STENCIL_N)
+            return oracle.stencil(x[lo:hi], 1)[a - lo:a - lo + (b - a)]
+        cb = np.linspace(0, CNT_COUNTERS, threads + 1).astype(np.int64)
+        vparts = [np.ascontiguousarray(val[:, cb[i]:cb[i + 1]]) for i in range(threads)]
+        mparts = [np.ascontiguousarray(meta[:, cb[i]:cb[i + 1]]) for i in range(threads)]
+        with ThreadPoolExecutor(threads) as pool:
+            t1 = time.perf_counter()
+            yp = list(pool.map(st_part, range(threads)))
+            st_par = time.perf_counter() - t1
+            t1 = time.perf_counter()
+            bp = list(pool.map(lambda i: oracle.cnt_batch(vparts[i], mparts[i], rows), range(threads)))
+            cb_par = time.perf_counter() - t1
+        assert np.array_equal(np.concatenate(yp), y1)
+        assert all(r[2] == 0 for r in bp) and np.array_equal(np.concatenate([r[0] for r in bp]), fin1)
         self.extra["cpu_context"] = {
             "host": {"nproc": nproc, "cpu_model": model},
             "host_thread_barrier": {"threads": threads, "ns_per_barrier": round(ns, 1),
                                     "rounds": 20_000},
             "oracle_stencil_one_iteration_GBs": round(STENCIL_BYTES_PER_ITER / st_s / 1e9, 3),
-            "oracle_cnt_batch_GBs": round(cnt_bytes / cb_s / 1e9, 3)}
+            "oracle_cnt_batch_GBs": round(cnt_bytes / cb_s / 1e9, 3),
+            "oracle_on_threads": {
+                "threads": threads,
+                "stencil_one_iteration_GBs": round(STENCIL_BYTES_PER_ITER / st_par / 1e9, 3),
+                "cnt_batch_GBs": round(cnt_bytes / cb_par / 1e9, 3)}}
         log(f"cpu context: {self.extra['cpu_context']}")
 
 
