@@ -150,6 +150,13 @@ def test_validation_before_device_work(ccb):
     assert ccb.ccb_bench_atomic_chain(None, 256, 1) == ccb.CCB_ERR_NULL_POINTER
     assert ccb.ccb_bench_atomic_chain(128, 256, 0) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_bench_copy(256, 512, 17) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_bench_copy(None, 512, 16) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_bench_copy(264, 512, 16) == ccb.CCB_ERR_INVALID_VALUE  # misaligned dst
+    # status: null, empty, oversized and misaligned workspaces are refused before any copy
+    assert ccb.ccb_syncall_status(None, 1)[0] == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_syncall_status(128, 0)[0] == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_syncall_status(128, (1 << 20) + 1)[0] == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_syncall_status(64, 1)[0] == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_bench_notify_pingpong(None, 256, 1, 1, 0, 256) == ccb.CCB_ERR_NULL_POINTER
     assert ccb.ccb_bench_notify_pingpong(256, 256, 1, 1, 0, None) == ccb.CCB_ERR_NULL_POINTER
     assert ccb.ccb_bench_notify_pingpong(256, 256, 0, 1, 0, 256) == ccb.CCB_ERR_INVALID_VALUE
