@@ -386,6 +386,8 @@ class Bench:
             "data_phase_GBs": round(STENCIL_BYTES_PER_ITER / float(data.mean()), 1),
             "data_phase_frac_of_peak": round(STENCIL_BYTES_PER_ITER / float(data.mean()) / HBM_PEAK_GBS, 4),
             "barrier_us_mean": round(float(barrier.mean()) / 1e3, 3),
+            "barrier_us_median": round(float(np.median(barrier)) / 1e3, 3),
+            "barrier_us_max": round(float(barrier.max()) / 1e3, 3),
             "finish_skew_us_mean": round(float(skew.mean()) / 1e3, 2),
             "in_kernel_total_ms": round(float(t[:, -1].max() - start.min()) / 1e6, 4)}
         log(f"stencil phases: {self.extra['stencil_phases']}")
