@@ -458,8 +458,8 @@ class Bench:
         record's completion to the wait's completion, from HIP events on the
         streams; rounds are separated on the host.  The records are enqueued
         before the wait, so that a wait never sits in a hardware queue in
-        front of the records it waits for (streams share the box's few
-        queues); N = 1 and 2."""
+        front of the records it waits for (streams share the process's few
+        hardware queues); N = 1 and 2."""
         ccb, torch = self.ccb, self.torch
         out = {}
         for n in (1, 2):
