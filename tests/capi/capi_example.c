@@ -4,7 +4,8 @@
  * "CANN Runtime CntNotify（计数型通知）管理接口详解" §5 (one stream records
  * ADD 1, another waits for a count of at least 1 and clears it on release),
  * then one launch of the soft barrier (8 workgroups, 100 rounds) whose
- * arrivals are read back.  It is built as a small shared object so that a
+ * arrivals are read back, one batched-engine launch and one stencil launch,
+ * each with a result fixed by construction.  It is built as a small shared object so that a
  * test can call it in-process; the one entry point returns 0 on success and
  * writes a one-line report into msg.
  */
@@ -72,6 +73,78 @@ __attribute__((visibility("default"))) int ccb_capi_example(char* msg, int msgLe
         snprintf(msg, (size_t)msgLen, "barrier: %lld arrivals, expected 800", (long long)arrivals);
         return 1;
     }
-    snprintf(msg, (size_t)msgLen, "released and cleared (id %u); 800 arrivals", id);
+
+    /* batched engine: 1024 counters, ops 0-6 record ADD 1, op 7 waits for
+     * GE 7 with clear -> every counter is released and ends at 0 */
+    enum { NC = 1024, NOPS = 8 };
+    static uint32_t hval[NOPS * NC];
+    static uint8_t hmeta[NOPS * NC];
+    for (int k = 0; k < NOPS; ++k)
+        for (int c = 0; c < NC; ++c) {
+            hval[k * NC + c] = k < 7 ? 1u : 7u;
+            hmeta[k * NC + c] = (uint8_t)(k < 7 ? CCB_CNT_RECORD_ADD
+                                                : (0x80 | 0x08 | CCB_CNT_WAIT_BIGGER_OR_EQUAL));
+        }
+    uint32_t *dval = NULL, *dfinal = NULL;
+    uint8_t *dmeta = NULL, *drel = NULL;
+    int32_t* derr = NULL;
+    HIP_TRY(hipMalloc((void**)&dval, sizeof(hval)));
+    HIP_TRY(hipMalloc((void**)&dmeta, sizeof(hmeta)));
+    HIP_TRY(hipMalloc((void**)&dfinal, NC * sizeof(uint32_t)));
+    HIP_TRY(hipMalloc((void**)&drel, NC));
+    HIP_TRY(hipMalloc((void**)&derr, sizeof(int32_t)));
+    HIP_TRY(hipMemcpy(dval, hval, sizeof(hval), hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(dmeta, hmeta, sizeof(hmeta), hipMemcpyHostToDevice));
+    HIP_TRY(hipMemset(derr, 0, sizeof(int32_t)));
+    CCB_TRY(ccb_cnt_notify_batch(dval, dmeta, NC, NOPS, dfinal, drel, 1, derr, NULL));
+    static uint32_t hfinal[NC];
+    static uint8_t hrel[NC];
+    int32_t herr = -1;
+    HIP_TRY(hipMemcpy(hfinal, dfinal, sizeof(hfinal), hipMemcpyDeviceToHost));
+    HIP_TRY(hipMemcpy(hrel, drel, sizeof(hrel), hipMemcpyDeviceToHost));
+    HIP_TRY(hipMemcpy(&herr, derr, sizeof(herr), hipMemcpyDeviceToHost));
+    for (int c = 0; c < NC; ++c)
+        if (hfinal[c] != 0u || hrel[c] != 1u || herr != 0) {
+            snprintf(msg, (size_t)msgLen, "batch: counter %d final %u released %u err %d", c,
+                     hfinal[c], (unsigned)hrel[c], (int)herr);
+            return 1;
+        }
+    HIP_TRY(hipFree(dval));
+    HIP_TRY(hipFree(dmeta));
+    HIP_TRY(hipFree(dfinal));
+    HIP_TRY(hipFree(drel));
+    HIP_TRY(hipFree(derr));
+
+    /* stencil: a constant array is a fixed point of the clamped 3-point average */
+    enum { N = 5000, ITERS = 3, GRID = 4, THREADS = 64 };
+    static int32_t hx[N];
+    for (int i = 0; i < N; ++i) hx[i] = 777;
+    int32_t *da = NULL, *db = NULL, *dws = NULL, *dhalo = NULL;
+    const size_t haloBytes = ccb_stencil_halo_bytes(N, THREADS, GRID);
+    HIP_TRY(hipMalloc((void**)&da, sizeof(hx)));
+    HIP_TRY(hipMalloc((void**)&db, sizeof(hx)));
+    HIP_TRY(hipMalloc((void**)&dws, ccb_syncall_workspace_bytes(1)));
+    HIP_TRY(hipMalloc((void**)&dhalo, haloBytes));
+    HIP_TRY(hipMemcpy(da, hx, sizeof(hx), hipMemcpyHostToDevice));
+    CCB_TRY(ccb_syncall_workspace_reset(dws, 1, NULL));
+    CCB_TRY(ccb_run_stencil(da, db, N, ITERS, dws, dhalo, haloBytes, NULL, GRID, THREADS, 0, 0,
+                            CCB_BARRIER_STRIPED | CCB_VISIBILITY_ORDER, NULL));
+    CCB_TRY(ccb_syncall_status(dws, 1, NULL, NULL));
+    static int32_t hy[N];
+    /* an odd iteration count leaves the result in the second buffer */
+    HIP_TRY(hipMemcpy(hy, db, sizeof(hy), hipMemcpyDeviceToHost));
+    for (int i = 0; i < N; ++i)
+        if (hy[i] != 777) {
+            snprintf(msg, (size_t)msgLen, "stencil: element %d is %d", i, (int)hy[i]);
+            return 1;
+        }
+    HIP_TRY(hipFree(da));
+    HIP_TRY(hipFree(db));
+    HIP_TRY(hipFree(dws));
+    HIP_TRY(hipFree(dhalo));
+
+    snprintf(msg, (size_t)msgLen,
+             "released and cleared (id %u); 800 arrivals; batch of %d released; stencil fixed point",
+             id, NC);
     return 0;
 }
