@@ -59,9 +59,10 @@ def parse():
     ap.add_argument("--mode", default="striped-order",
                     choices=["striped-order", "flat-order", "striped-full", "flat-full"])
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
-    ap.add_argument("--only", choices=["counters"], default=None,
-                    help="run only the copy ceiling, the stencil and the batched CntNotify "
-                         "engine (counter collection)")
+    ap.add_argument("--only", choices=["counters", "barrier"], default=None,
+                    help="counters: only the copy ceiling, the stencil and the batched "
+                         "CntNotify engine (counter collection); barrier: only the floor, "
+                         "the barrier-only latencies and their breakdown")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
 
@@ -271,6 +272,55 @@ class Bench:
                          "ratio_to_composed_floor": round(best / composed, 2)})
         self.extra["latency_roofline"] = roof
         log(f"barrier-only ns/barrier at 256 WGs: {lat}")
+
+    # ------------------------------------------------------------ where a barrier's time goes
+    def barrier_breakdown(self, floor, mode_name=None, n_grid=256, rounds=1024, skip=64):
+        """Per-member, per-round wall-clock stamps of barrier-only rounds at
+        n_grid workgroups x 256 threads (ccb_bench_barrier_breakdown): issue
+        of the arrival, its reply, and the poll seeing the round complete.
+        Medians over rounds (after `skip` warm-up rounds) of
+          arrival_round_trip     reply - issue, per member
+          last_arrival_to_first_observer   first release of a round - the
+                                 last issue of that round
+          first_to_last_observer last release - first release of a round
+          release_to_next_arrival  next issue - release, per member
+          round                  last release - the previous round's last
+                                 release
+        each beside the floor it is compared with."""
+        np, torch, ccb, ws, stream = self.np, self.torch, self.ccb, self.ws, self.stream
+        mode_name = mode_name or self.args.mode
+        mode = ccb.MODES[mode_name]
+        stamps = torch.zeros(rounds * n_grid * 3, dtype=torch.int64, device=self.dev)
+        ccb.check(ccb.ccb_syncall_workspace_reset(ws, 1, stream), "reset")
+        ccb.check(ccb.ccb_bench_barrier_breakdown(ws, stamps, rounds, n_grid, 256, 0, mode, stream),
+                  "breakdown")
+        st, arr = ccb.ccb_syncall_status(ws, 1, stream)
+        ccb.check(st, "breakdown status")
+        assert arr == [rounds * n_grid], arr
+        t = stamps.cpu().numpy().reshape(rounds, n_grid, 3).astype(np.float64) * self.tick_ns
+        issue, reply, rel = t[skip:, :, 0], t[skip:, :, 1], t[skip:, :, 2]
+        med = lambda a: round(float(np.median(a)), 1)
+        terms = {
+            "arrival_round_trip": med(reply - issue),
+            "last_arrival_to_first_observer": med(rel.min(axis=1) - issue.max(axis=1)),
+            "first_to_last_observer": med(rel.max(axis=1) - rel.min(axis=1)),
+            "release_to_next_arrival": med(issue[1:] - rel[:-1]),
+        }
+        last = rel.max(axis=1)
+        out = {"mode": mode_name, "workgroups": n_grid, "rounds_stamped": rounds - skip,
+               "median_ns": terms, "round_ns": med(np.diff(last)),
+               "mean_round_ns": round(float(np.diff(last).mean()), 1),
+               # who sees the release first: the member whose arrival was last
+               "first_observer_is_last_arriver": round(float(np.mean(
+                   rel.argmin(axis=1) == issue.argmax(axis=1))), 3),
+               "floors_ns": {"arrival_round_trip": floor["fetch_add_ns"],
+                             "last_arrival_to_first_observer": floor["fetch_add_ns"],
+                             "first_to_last_observer": floor["load_ns"],
+                             "notify_one_way": floor["notify_one_way_ns"].get("other_xcd")},
+               "clock_resolution_ns": round(self.tick_ns, 1)}
+        self.extra.setdefault("barrier_breakdown", {})[mode_name] = out
+        log(f"barrier breakdown ({mode_name}): {out}")
+        return out
 
     # ------------------------------------------------------------ HIP's own grid barrier
     def hip_grid_sync(self):
@@ -590,6 +640,17 @@ def main():
                           "cntnotify_batch": b.extra["cntnotify_batch"]}), flush=True)
         return
 
+    if args.only == "barrier":
+        floor = b.floor()
+        b.latency(floor)
+        b.barrier_breakdown(floor)
+        b.barrier_breakdown(floor, "striped-full")
+        print(json.dumps({k: b.extra[k] for k in ("floor", "barrier_only_ns_at_256",
+                                                   "barrier_only_ns_by_workgroups",
+                                                   "latency_roofline", "barrier_breakdown")}),
+              flush=True)
+        return
+
     ms_per_step, rounds = b.headline()
     value = rounds / (ms_per_step / 1e3)
     roofline = None
@@ -597,6 +658,8 @@ def main():
     if not args.quick:
         floor = b.floor()
         b.latency(floor)
+        b.barrier_breakdown(floor)
+        b.barrier_breakdown(floor, "striped-full")
         b.hip_grid_sync()
         b.grouped()
         gbs = b.copy_ceiling()

@@ -40,6 +40,7 @@ CCB_ERR_HIP = 9
 CCB_ERR_NOT_READY = 10
 
 CCB_SOFT_MAX_POLL = 1_000_000
+CCB_BREAKDOWN_MAX_ROUNDS = 1024
 CCB_LINE_BYTES = 128
 CCB_STRIPES = 64
 CCB_SLOT_ROWS = 6
@@ -107,6 +108,8 @@ _f = {
     "ccb_run_stencil": _sig("ccb_run_stencil", _I32, _V, _V, _I64, _I32, _V, _V, ctypes.c_size_t,
                             _V, _I32, _I32, _I32, _U32, _I32, _V),
     "ccb_stencil_halo_bytes": _sig("ccb_stencil_halo_bytes", ctypes.c_size_t, _I64, _I32, _I32),
+    "ccb_bench_barrier_breakdown": _sig("ccb_bench_barrier_breakdown", _I32, _V, _V, _I32, _I32,
+                                        _I32, _I32, _I32, _V),
     "ccb_bench_atomic_chain": _sig("ccb_bench_atomic_chain", _I32, _V, _V, _I32, _I32, _I32, _V),
     "ccb_bench_atomic_contended": _sig("ccb_bench_atomic_contended", _I32, _V, _V, _I32, _I32, _V),
     "ccb_bench_notify_pingpong": _sig("ccb_bench_notify_pingpong", _I32, _V, _V, _I32, _I32,
@@ -212,6 +215,12 @@ def ccb_run_stencil(buf_a, buf_b, n, iters, ws, halo, halo_bytes, n_grid, thread
 
 
 # --- floor microbenchmarks --------------------------------------------------------
+
+def ccb_bench_barrier_breakdown(ws, stamps, rounds, n_grid, threads, wgs_per_cu=0, mode=0,
+                                stream=None) -> int:
+    return _f["ccb_bench_barrier_breakdown"](_p(ws), _p(stamps), rounds, n_grid, threads,
+                                             wgs_per_cu, mode, _s(stream))
+
 
 def ccb_bench_atomic_chain(line, ticks, iters, fenced=0, kind=0, stream=None) -> int:
     return _f["ccb_bench_atomic_chain"](_p(line), _p(ticks), iters, fenced, kind, _s(stream))

@@ -107,7 +107,7 @@ inline bool valid_mode(int32_t mode) { return mode >= 0 && mode <= 3; }
 // streams share them); the host waits for them once.
 constexpr int kSgprPerSimd = 800;
 constexpr int kTrapSgprs = 16;
-constexpr int kKernelIds = 4;
+constexpr int kKernelIds = 5;
 
 struct RegQuery {
     bool done = false;
@@ -334,7 +334,10 @@ CCB_API ccbStatus ccb_syncall_status(const int32_t* ws, uint32_t nBarriers, int6
             }
         }
     }
-    return errWord == CCB_OK ? CCB_OK : CCB_ERR_DEADLOCK;
+    // the kernels store CCB_ERR_DEADLOCK or CCB_ERR_INVALID_VALUE (a stripe
+    // past the int32 range); anything else is reported as a deadlock
+    if (errWord == CCB_OK || errWord == CCB_ERR_INVALID_VALUE) return errWord;
+    return CCB_ERR_DEADLOCK;
 }
 
 // ===========================================================================
@@ -356,8 +359,26 @@ CCB_API ccbStatus ccb_run_barrier_only(int32_t* ws, uint32_t* placement, int32_t
                                    (hipStream_t)stream, &ls);
     if (st != CCB_OK) return st;
     const int32_t members = usedCores != 0 ? usedCores : nGrid;
-    return from_hip(ccb::launch_barrier_only(ls, ws, placement, wgStatus, rounds, members,
-                                             poll_bound(maxPoll)));
+    return from_hip(ccb::launch_barrier_only(ls, ws, placement, wgStatus, nullptr, rounds,
+                                             members, poll_bound(maxPoll)));
+}
+
+CCB_API ccbStatus ccb_bench_barrier_breakdown(int32_t* ws, uint64_t* stamps, int32_t rounds,
+                                              int32_t nGrid, int32_t threads, int32_t wgsPerCu,
+                                              int32_t mode, ccbStream stream)
+{
+    if (ws == nullptr || stamps == nullptr) return CCB_ERR_NULL_POINTER;
+    if (!aligned(ws, CCB_LINE_BYTES) || !aligned(stamps, 8) || rounds < 1 ||
+        rounds > CCB_BREAKDOWN_MAX_ROUNDS || nGrid < 1 || !valid_threads(threads) ||
+        wgsPerCu < 0 || !valid_mode(mode) || !counts_fit(rounds, nGrid, mode))
+        return CCB_ERR_INVALID_VALUE;
+    std::lock_guard<std::mutex> lk(g_launch_mu);
+    ccb::LaunchShape ls;
+    ccbStatus st = plan_persistent(ccb::KernelId::BarrierStamps, mode, nGrid, threads, wgsPerCu,
+                                   (hipStream_t)stream, &ls);
+    if (st != CCB_OK) return st;
+    return from_hip(ccb::launch_barrier_only(ls, ws, nullptr, nullptr, stamps, rounds, nGrid,
+                                             CCB_SOFT_MAX_POLL));
 }
 
 CCB_API ccbStatus ccb_run_slot_rounds(int32_t* ws, uint32_t* slots, uint32_t* out,

@@ -16,7 +16,7 @@ constexpr bool kStencilNTLoad = true;
 constexpr int kCntUnroll = 1;      // ops per register set in the batch engine's two-set pipeline
 constexpr bool kCntNTLoad = true;   // non-temporal loads of the op stream (read once)
 
-enum class KernelId { BarrierOnly, SlotRounds, GroupedRounds, Stencil };
+enum class KernelId { BarrierOnly, SlotRounds, GroupedRounds, Stencil, BarrierStamps };
 
 struct LaunchShape {
     const void* fn;  // the kernel instance
@@ -34,8 +34,8 @@ hipError_t launch_register_query(KernelId id, int32_t mode, int32_t* out, hipStr
 hipError_t register_query_word(int32_t** out);
 
 hipError_t launch_barrier_only(const LaunchShape& ls, int32_t* ws, uint32_t* placement,
-                               int32_t* wgStatus, int32_t rounds, int32_t nMembers,
-                               uint32_t maxPoll);
+                               int32_t* wgStatus, uint64_t* stamps, int32_t rounds,
+                               int32_t nMembers, uint32_t maxPoll);
 hipError_t launch_slot_rounds(const LaunchShape& ls, int32_t* ws, uint32_t* slots, uint32_t* out,
                               int32_t* wgStatus, uint64_t seed, int32_t rounds, int32_t nMembers,
                               uint32_t maxPoll);

@@ -108,13 +108,39 @@ __device__ __forceinline__ uint32_t shared_load(const uint32_t* p)
 // Barrier-only rounds: the latency benchmark of the soft barrier.
 // Members (w < nMembers) run `rounds` barriers; the rest take the partial-
 // participation exit of the SYNCALL guide §7.2 and mark themselves idle (§8).
+//
+// kStamps: lane 0 of each member also reads the wall clock when it issues
+// its arrival, when the arrival's reply is back and when its poll sees the
+// round complete.  The stamps stay in LDS during the loop (a global store
+// per round would add its acknowledgement to the next arrival's wait) and
+// go to stamps[(r * nGrid + w) * 3 + {0, 1, 2}] at the end.
 // ---------------------------------------------------------------------------
-template <int K, ccbVisibility V>
+namespace {
+
+// Wall-clock stamps of one round's reply and release (lane 0 of wave 0).
+struct StampHook {
+    uint64_t* atReply;
+    uint64_t* atRelease;
+    __device__ __forceinline__ void reply() const
+    {
+        if (__lane_id() == 0) *atReply = wall_clock64();
+    }
+    __device__ __forceinline__ void released() const
+    {
+        if (__lane_id() == 0) *atRelease = wall_clock64();
+    }
+};
+
+}  // namespace
+
+template <int K, ccbVisibility V, bool kStamps>
 __global__ __launch_bounds__(1024) void ccb_k_barrier_only(int32_t* ws, uint32_t* placement,
-                                                            int32_t* wgStatus, int32_t rounds,
-                                                            int32_t nMembers, uint32_t maxPoll)
+                                                            int32_t* wgStatus, uint64_t* stamps,
+                                                            int32_t rounds, int32_t nMembers,
+                                                            uint32_t maxPoll)
 {
     __shared__ int32_t result[2];
+    __shared__ uint64_t lds[kStamps ? 3 * CCB_BREAKDOWN_MAX_ROUNDS : 1];
     if (register_query(maxPoll, ws)) return;
     record_placement(placement);
     const int32_t w = blockIdx.x;
@@ -124,6 +150,7 @@ __global__ __launch_bounds__(1024) void ccb_k_barrier_only(int32_t* ws, uint32_t
     }
     int32_t* err = ws + CCB_STRIPES * CCB_LINE_WORDS;
     int32_t rc = CCB_OK;
+    int32_t done = 0;
     // Rounds follow each other with nothing in between, so the workgroup
     // barrier that releases round r also orders round r + 1's arrival: one
     // per round.  The result word alternates so that wave 0 can publish
@@ -131,13 +158,28 @@ __global__ __launch_bounds__(1024) void ccb_k_barrier_only(int32_t* ws, uint32_t
     for (int32_t r = 0; r < rounds; ++r) {
         if (threadIdx.x < kWave) {
             int32_t before = 0;
-            if (leader()) before = ccb_arrive<K, V>(ws, w);
-            const int32_t e = ccb_await<K, V>(ws, nMembers, w, before, maxPoll, err);
+            int32_t e;
+            if constexpr (kStamps) {
+                if (leader()) lds[3 * r] = wall_clock64();
+                if (leader()) before = ccb_arrive<K, V>(ws, w);
+                e = ccb_await<K, V>(ws, nMembers, w, before, maxPoll, err,
+                                    StampHook{&lds[3 * r + 1], &lds[3 * r + 2]});
+            } else {
+                if (leader()) before = ccb_arrive<K, V>(ws, w);
+                e = ccb_await<K, V>(ws, nMembers, w, before, maxPoll, err);
+            }
             if (leader()) result[r & 1] = e;
         }
         __syncthreads();
         rc = result[r & 1];
+        done = r + 1;
         if (rc != CCB_OK) break;
+    }
+    if constexpr (kStamps) {
+        // wave 0 wrote the stamps and writes them out
+        if (threadIdx.x < kWave)
+            for (int32_t i = threadIdx.x; i < 3 * done; i += kWave)
+                stamps[((size_t)(i / 3) * gridDim.x + w) * 3 + i % 3] = lds[i];
     }
     if (wgStatus != nullptr && leader()) wgStatus[w] = rc == CCB_OK ? 1 : 3;
 }
@@ -1208,6 +1250,15 @@ static hipError_t coop(const void* fn, int nGrid, int threads, size_t lds, hipSt
     return hipLaunchCooperativeKernel(fn, dim3(nGrid), dim3(threads), args, (unsigned)lds, s);
 }
 
+#define CCB_PICK_X(kernel, mode, x)                                                             \
+    ((mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_ORDER)                                     \
+         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_ORDER, x>)                \
+     : (mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_FULL)                                    \
+         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_FULL, x>)                 \
+     : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_ORDER)                                      \
+         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_ORDER, x>)                          \
+         : reinterpret_cast<const void*>(&kernel<1, CCB_VIS_FULL, x>))
+
 #define CCB_PICK(kernel, mode)                                                                  \
     ((mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_ORDER)                                     \
          ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_ORDER>)                   \
@@ -1220,7 +1271,8 @@ static hipError_t coop(const void* fn, int nGrid, int threads, size_t lds, hipSt
 const void* kernel_ptr(KernelId id, int32_t mode)
 {
     switch (id) {
-    case KernelId::BarrierOnly: return CCB_PICK(ccb_k_barrier_only, mode);
+    case KernelId::BarrierOnly: return CCB_PICK_X(ccb_k_barrier_only, mode, false);
+    case KernelId::BarrierStamps: return CCB_PICK_X(ccb_k_barrier_only, mode, true);
     case KernelId::SlotRounds: return CCB_PICK(ccb_k_slot_rounds, mode);
     case KernelId::GroupedRounds: return CCB_PICK(ccb_k_grouped_rounds, mode);
     case KernelId::Stencil: return CCB_PICK(ccb_k_stencil, mode);
@@ -1229,10 +1281,10 @@ const void* kernel_ptr(KernelId id, int32_t mode)
 }
 
 hipError_t launch_barrier_only(const LaunchShape& ls, int32_t* ws, uint32_t* placement,
-                               int32_t* wgStatus, int32_t rounds, int32_t nMembers,
-                               uint32_t maxPoll)
+                               int32_t* wgStatus, uint64_t* stamps, int32_t rounds,
+                               int32_t nMembers, uint32_t maxPoll)
 {
-    void* args[] = {&ws, &placement, &wgStatus, &rounds, &nMembers, &maxPoll};
+    void* args[] = {&ws, &placement, &wgStatus, &stamps, &rounds, &nMembers, &maxPoll};
     return coop(ls.fn, ls.nGrid, ls.threads, ls.lds, ls.stream, args);
 }
 
@@ -1278,8 +1330,9 @@ hipError_t launch_register_query(KernelId id, int32_t mode, int32_t* out, hipStr
     uint64_t seed = 0;
     uint32_t query = 0;  // maxPoll == 0: the register query
     switch (id) {
-    case KernelId::BarrierOnly: {
-        void* args[] = {&out, &none, &none, &zero, &zero, &query};
+    case KernelId::BarrierOnly:
+    case KernelId::BarrierStamps: {
+        void* args[] = {&out, &none, &none, &none, &zero, &zero, &query};
         return hipLaunchKernel(fn, dim3(1), dim3(kWave), args, 0, s);
     }
     case KernelId::SlotRounds: {

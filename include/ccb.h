@@ -178,10 +178,12 @@ CCB_API ccbStatus ccb_syncall_workspace_reset(int32_t* ws, uint32_t nBarriers, c
  * barriers and (optionally, arrivals may be NULL) store in arrivals[b] the
  * total number of arrivals on barrier b (the sum of its stripes; int64, as
  * the total of 64 int32 stripes can pass 2^31).  Reads the stripe lines a
- * few barriers at a time through a 64-KiB host buffer.  Returns CCB_OK or
- * CCB_ERR_DEADLOCK; CCB_ERR_HIP, or CCB_ERR_RESOURCE_EXHAUSTED when the host
- * buffer cannot be allocated (arrivals may then be partly written).  Blocks
- * the host thread. */
+ * few barriers at a time through a 64-KiB host buffer.  Returns CCB_OK,
+ * CCB_ERR_DEADLOCK (a poll hit its bound), or CCB_ERR_INVALID_VALUE (a
+ * member found its stripe past the int32 range of [SYNCALL] §4.1: the
+ * workspace was not re-zeroed in time); CCB_ERR_HIP, or
+ * CCB_ERR_RESOURCE_EXHAUSTED when the host buffer cannot be allocated
+ * (arrivals may then be partly written).  Blocks the host thread. */
 CCB_API ccbStatus ccb_syncall_status(const int32_t* ws, uint32_t nBarriers, int64_t* arrivals,
                                      ccbStream stream);
 
@@ -204,6 +206,29 @@ CCB_API ccbStatus ccb_run_barrier_only(int32_t* ws, uint32_t* placement, int32_t
                                        int32_t rounds, int32_t nGrid, int32_t threads,
                                        int32_t usedCores, int32_t wgsPerCu, uint32_t maxPoll,
                                        int32_t mode, ccbStream stream);
+
+/* Most rounds one ccb_bench_barrier_breakdown launch can stamp. */
+#define CCB_BREAKDOWN_MAX_ROUNDS 1024
+
+/* Latency breakdown of the soft barrier (instrumentation, not on the pages):
+ * ccb_run_barrier_only's rounds over all nGrid workgroups (usedCores = 0),
+ * with lane 0 of every member reading the device wall clock at three points
+ * of each round r:
+ *   stamps[(r * nGrid + w) * 3 + 0]  just before it issues its arrival
+ *   stamps[(r * nGrid + w) * 3 + 1]  when the arrival's reply is back
+ *   stamps[(r * nGrid + w) * 3 + 2]  when its poll has seen the round
+ *                                    complete (before the acquire fence)
+ * (uint64 ticks at the rate ccb_device_info reports).  The stamps are kept
+ * in LDS until the last round and written out at the end.
+ *   ws      device, workspace of 1 barrier (zeroed)
+ *   stamps  device, rounds * nGrid * 3 uint64, 8-B aligned
+ * rounds: 1 .. CCB_BREAKDOWN_MAX_ROUNDS.  wgsPerCu and mode as in
+ * ccb_run_barrier_only; the poll bound is CCB_SOFT_MAX_POLL.  Read the
+ * outcome with ccb_syncall_status.
+ * Errors: NULL_POINTER, INVALID_VALUE, NOT_CORESIDENT. */
+CCB_API ccbStatus ccb_bench_barrier_breakdown(int32_t* ws, uint64_t* stamps, int32_t rounds,
+                                              int32_t nGrid, int32_t threads, int32_t wgsPerCu,
+                                              int32_t mode, ccbStream stream);
 
 /* The witness slots of the two witness workloads: a ring of CCB_SLOT_ROWS
  * rows of nGrid slots, one slot every CCB_SLOT_WORDS uint32.  Slot p of

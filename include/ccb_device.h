@@ -115,6 +115,15 @@ struct ccb_no_overlap {
     __device__ __forceinline__ void operator()() const {}
 };
 
+/* Instrumentation points of ccb_await (all lanes of wave 0 call them):
+ * reply() once the arrival's reply is back, before the first poll load;
+ * released() once the poll has seen the round complete (or given up),
+ * before the acquire fence.  The default does nothing and costs nothing. */
+struct ccb_no_hook {
+    __device__ __forceinline__ void reply() const {}
+    __device__ __forceinline__ void released() const {}
+};
+
 /* Split-phase form of the barrier, for callers that order their own
  * workgroup around it (one workgroup barrier per round where back-to-back
  * rounds leave nothing to do between them).
@@ -138,7 +147,14 @@ struct ccb_no_overlap {
  * CCB_ERR_DEADLOCK in the error word and returns it.  Every 64th poll it
  * also reads the error word and returns its value when another member has
  * failed.  For CCB_VIS_FULL it ends with an agent-scope acquire fence.  The
- * caller then releases the rest of its workgroup (a workgroup barrier). */
+ * caller then releases the rest of its workgroup (a workgroup barrier).
+ *
+ * The counters are int32 ([SYNCALL] §4.1).  A round whose release count
+ * epoch * n_l would pass INT32_MAX on some stripe can never complete, and
+ * an old value below zero means a stripe has already wrapped: either way
+ * the member stores CCB_ERR_INVALID_VALUE in the error word and returns it
+ * without polling, and the others leave when they next read the error
+ * word.  Re-zero the workspace before a stripe gets near 2^31 arrivals. */
 template <int K, ccbVisibility kVis>
 __device__ __forceinline__ int32_t ccb_arrive(int32_t* ctr, int32_t member)
 {
@@ -150,9 +166,10 @@ __device__ __forceinline__ int32_t ccb_arrive(int32_t* ctr, int32_t member)
                                   __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int K, ccbVisibility kVis>
+template <int K, ccbVisibility kVis, class Hook = ccb_no_hook>
 __device__ __forceinline__ int32_t ccb_await(const int32_t* ctr, int32_t n, int32_t member,
-                                             int32_t before, uint32_t maxPoll, int32_t* err)
+                                             int32_t before, uint32_t maxPoll, int32_t* err,
+                                             Hook hook = Hook())
 {
     const int lane = (int)__lane_id();
     const int32_t ks = n < K ? n : K;  // stripes in use
@@ -170,8 +187,20 @@ __device__ __forceinline__ int32_t ccb_await(const int32_t* ctr, int32_t n, int3
     // that stripe complete.
     const int32_t b = __shfl(before, 0, 64);
     __builtin_amdgcn_sched_barrier(0x44F);
+    hook.reply();
     const int32_t v0 = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int32_t epoch = b / ((n - s + K - 1) / K) + 1;
+    // The release count of stripe l is epoch * n_l; stripe 0 has the most
+    // members, so the round fits in int32 exactly when
+    // (before / n_s + 1) * n_0 <= INT32_MAX, i.e. before / n_s < INT32_MAX / n_0.
+    const int32_t q = b / ((n - s + K - 1) / K);
+    const int32_t epoch = q + 1;
+    if (b < 0 || q >= INT32_MAX / ((n + K - 1) / K)) {
+        if (lane == 0)
+            __hip_atomic_store(err, (int32_t)CCB_ERR_INVALID_VALUE, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        hook.released();
+        return CCB_ERR_INVALID_VALUE;
+    }
     // stripe `lane` is complete for this round at epoch * n_lane arrivals;
     // lanes past the stripes in use re-read stripe 0 and always agree
     const int32_t need = lane < ks ? epoch * ((n - lane + K - 1) / K) : INT32_MIN;
@@ -206,6 +235,7 @@ __device__ __forceinline__ int32_t ccb_await(const int32_t* ctr, int32_t n, int3
             if (CCB_POLL_SLEEP > 0) __builtin_amdgcn_s_sleep(CCB_POLL_SLEEP);
         }
     }
+    hook.released();
     // acquire: loads after the barrier see every member's released stores
     if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     return rc;
@@ -223,8 +253,9 @@ __device__ __forceinline__ int32_t ccb_await(const int32_t* ctr, int32_t n, int3
  * kPreWait (CCB_VIS_ORDER only): every thread first waits for all of its own
  * memory operations.  A caller that has already waited for the stores it
  * shares across the barrier may turn it off.
- * Every thread of the workgroup calls it.  Returns CCB_OK or
- * CCB_ERR_DEADLOCK (the same value in every thread). */
+ * Every thread of the workgroup calls it.  Returns CCB_OK,
+ * CCB_ERR_DEADLOCK or CCB_ERR_INVALID_VALUE (the same value in every
+ * thread). */
 template <int K, ccbVisibility kVis, bool kPreWait = true, class Overlap = ccb_no_overlap>
 __device__ __forceinline__ int32_t ccb_barrier(int32_t* ctr, int32_t n, int32_t member,
                                                uint32_t maxPoll, int32_t* err,

@@ -16,7 +16,8 @@ itself; see tests/test_oracle_*.py):
                      keying is this library's convention, not the pages'.
   mix_participants   the SYNCALL guide's §4.2 formula (blocks x (1 + ratio))
                      on its 1:1 and 1:2 cases, whole launch for 0.
-  epoch_target       the SYNCALL guide's §5.2 prose (next multiple of N above
+  epoch_target,      the SYNCALL guide's §5.2 prose (next multiple of N above
+  epoch_target_checked
                      the old count), checked by brute force over small
                      (before, N) against a search for that multiple.
   slot_rounds,       brute-force enumeration of every arrival order on small
@@ -81,6 +82,8 @@ def _load():
     lib.ccbo_witness_hash.restype = u32
     lib.ccbo_epoch_target.argtypes = [i32, i32]
     lib.ccbo_epoch_target.restype = i32
+    lib.ccbo_epoch_target_checked.argtypes = [i32, i32, P]
+    lib.ccbo_epoch_target_checked.restype = ctypes.c_int
     lib.ccbo_participants.argtypes = [i32, i32]
     lib.ccbo_participants.restype = i32
     lib.ccbo_mix_participants.argtypes = [i32, i32, i32]
@@ -122,6 +125,13 @@ def witness_hash(seed: int, rnd: int, wg: int) -> int:
 
 def epoch_target(before: int, n: int) -> int:
     return int(_load().ccbo_epoch_target(before, n))
+
+
+def epoch_target_checked(before: int, n: int) -> Tuple[int, int]:
+    """(rc, target): rc INVALID_VALUE when the target leaves the int32 range."""
+    t = np.zeros(1, dtype=np.int32)
+    rc = _load().ccbo_epoch_target_checked(before, n, _ptr(t))
+    return int(rc), int(t[0])
 
 
 def participants(used_cores: int, n_launched: int) -> int:

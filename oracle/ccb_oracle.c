@@ -85,6 +85,19 @@ int32_t ccbo_epoch_target(int32_t before, int32_t n)
     return (before / n + 1) * n;
 }
 
+/* The same target with the counter's range checked.  [SYNCALL] §4.1 types  */
+/* the counter int32: a round whose target lies above INT32_MAX can never   */
+/* be reached, and an old value below zero means the counter has wrapped.   */
+/* Either is reported as ORC_INVALID_VALUE (pages silent on the limit).     */
+int ccbo_epoch_target_checked(int32_t before, int32_t n, int32_t* target)
+{
+    if (n <= 0 || before < 0) return ORC_INVALID_VALUE;
+    int64_t t = ((int64_t)before / n + 1) * (int64_t)n;
+    if (t > INT32_MAX) return ORC_INVALID_VALUE;
+    *target = (int32_t)t;
+    return ORC_OK;
+}
+
 /* Participant count.  [SYNCALL] §4.2: usedCores == 0 means every core of   */
 /* the launch; an explicit count may be smaller than the launch.  Negative  */
 /* values and counts above the launch are rejected (pages silent).          */
@@ -121,7 +134,8 @@ int32_t ccbo_mix_participants(int32_t groups, int32_t ratio, int32_t nLaunched)
 /*                                                                           */
 /* members[0..m-1]: ids of the participants of this round (ascending).       */
 /* slot: per-wg witness slot; out_row: per-wg output of this round.          */
-/* Returns ORC_OK, or ORC_DEADLOCK when some member's poll could never      */
+/* Returns ORC_OK, ORC_INVALID_VALUE when a round's target leaves the int32 */
+/* range, or ORC_DEADLOCK when some member's poll could never               */
 /* succeed (the counter sits below its target with every member arrived).   */
 /* ------------------------------------------------------------------------ */
 static int simulate_round(uint64_t seed, uint32_t round,
@@ -137,8 +151,9 @@ static int simulate_round(uint64_t seed, uint32_t round,
     /* arrive: atomic fetch-add of one, target from the old value */
     for (int32_t i = 0; i < m; ++i) {
         int32_t before = *counter;
+        if (ccbo_epoch_target_checked(before, m, &target_scratch[i]) != ORC_OK)
+            return ORC_INVALID_VALUE;
         *counter = before + 1;
-        target_scratch[i] = ccbo_epoch_target(before, m);
     }
     /* poll: released once the counter has reached the target (>=, see the
      * reading of the poll condition in the design notes) */

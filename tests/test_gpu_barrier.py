@@ -240,6 +240,80 @@ def test_forced_deadlock_is_reported(ccb, wl, mode):
     assert (w == 3).any() and set(w.tolist()) <= {1, 3}
 
 
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_counter_past_int32_is_invalid_value(ccb, wl, mode):
+    """Stripes preset one round below the int32 limit ([SYNCALL] §4.1 types
+    the counter int32): the first round still fits and completes, the second
+    round's release count would pass INT32_MAX, so every member stores
+    INVALID_VALUE in the error word and stops instead of polling for a count
+    the counter cannot hold.  Same outcome as the oracle's range-checked
+    round simulator on the single counter."""
+    n = 4
+    flat = (mode & ccb.CCB_BARRIER_FLAT) != 0
+    limit = 2**31 - 1
+    ws = wl.workspace(1)
+    if flat:
+        top = limit // n * n            # last count a round of n can reach
+        ws[0] = top - n                  # round 1 ends at top, round 2 cannot
+        want_rc1, _ = oracle.epoch_target_checked(top - n, n)
+        want_rc2, _ = oracle.epoch_target_checked(top, n)
+    else:
+        for s in range(n):              # n <= 64 stripes of one member each
+            ws[s * 32] = limit - 1
+        want_rc1, _ = oracle.epoch_target_checked(limit - 1, 1)
+        want_rc2, _ = oracle.epoch_target_checked(limit, 1)
+    assert (want_rc1, want_rc2) == (oracle.OK, oracle.INVALID_VALUE)
+    _say(f"barrier_only past int32: N={n}, 2 rounds, mode={mode}")
+    wg = torch.zeros(n, dtype=torch.int32, device="cuda")
+    assert ccb.ccb_run_barrier_only(ws, None, wg, 2, n, 64, 0, 0, 2000, mode, None) == 0
+    st, _ = ccb.ccb_syncall_status(ws, 1, None)
+    assert st == ccb.CCB_ERR_INVALID_VALUE
+    assert (wg.cpu().numpy() == 3).all()
+    # one round from the same preset is fine
+    ws = wl.workspace(1)
+    if flat:
+        ws[0] = top - n
+    else:
+        for s in range(n):
+            ws[s * 32] = limit - 1
+    assert ccb.ccb_run_barrier_only(ws, None, wg, 1, n, 64, 0, 0, 2000, mode, None) == 0
+    st, ctrs = ccb.ccb_syncall_status(ws, 1, None)
+    assert st == ccb.CCB_OK
+    assert ctrs == [top] if flat else ctrs == [n * limit]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_breakdown_stamps_are_ordered(ccb, wl, mode):
+    """ccb_bench_barrier_breakdown: every member's stamps run issue <= reply
+    <= release within a round and release <= next issue across rounds; no
+    member is released before the round's last arrival was issued; every
+    arrival is counted."""
+    n, rounds = 64, 200
+    _say(f"barrier breakdown: {n} x 256, {rounds} rounds, mode={mode}")
+    ws = wl.workspace(1)
+    stamps = torch.zeros(rounds * n * 3, dtype=torch.int64, device="cuda")
+    assert ccb.ccb_bench_barrier_breakdown(ws, stamps, rounds, n, 256, 0, mode, None) == 0
+    st, ctrs = ccb.ccb_syncall_status(ws, 1, None)
+    assert st == 0 and ctrs == [rounds * n]
+    t = stamps.cpu().numpy().reshape(rounds, n, 3)
+    assert (t > 0).all()
+    assert (t[:, :, 0] <= t[:, :, 1]).all() and (t[:, :, 1] <= t[:, :, 2]).all()
+    assert (t[1:, :, 0] >= t[:-1, :, 2]).all()
+    # the barrier: a release in round r follows every round-r arrival's issue
+    assert (t[:, :, 2].min(axis=1) >= t[:, :, 0].max(axis=1)).all()
+
+
+def test_breakdown_rejects_bad_arguments(ccb, wl):
+    ws = wl.workspace(1)
+    stamps = torch.zeros(8 * 3, dtype=torch.int64, device="cuda")
+    assert ccb.ccb_bench_barrier_breakdown(ws, None, 1, 8, 64) == ccb.CCB_ERR_NULL_POINTER
+    assert ccb.ccb_bench_barrier_breakdown(ws, stamps, 0, 8, 64) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_bench_barrier_breakdown(ws, stamps, ccb.CCB_BREAKDOWN_MAX_ROUNDS + 1, 8,
+                                           64) == ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_bench_barrier_breakdown(ws, stamps.data_ptr() + 4, 1, 8, 64) == \
+        ccb.CCB_ERR_INVALID_VALUE
+
+
 def test_reset_clears_error_word(ccb, wl):
     ws = wl.workspace(1)
     ws[0] = 5

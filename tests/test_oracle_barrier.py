@@ -77,6 +77,37 @@ def test_epoch_target_is_next_multiple():
             assert oracle.epoch_target(before, n) == t, (before, n)
 
 
+def test_epoch_target_checked_at_the_int32_limit():
+    # SYNCALL guide §4.1 types the counter int32: a target above 2^31 - 1 can
+    # never be reached, an old value below zero is a wrapped counter.  The
+    # next multiple is found by search on Python integers, then compared
+    # with the limit.
+    limit = 2**31 - 1
+    for n in (1, 2, 3, 4, 7, 64, 1000, 65_537):
+        top = limit - limit % n          # largest multiple of n in range
+        for before in (0, n - 1, top - n - 1, top - n, top - 1, top, limit):
+            t = before + 1
+            while t % n != 0:
+                t += 1
+            rc, got = oracle.epoch_target_checked(before, n)
+            if t <= limit:
+                assert (rc, got) == (oracle.OK, t), (before, n)
+            else:
+                assert rc == oracle.INVALID_VALUE, (before, n)
+    assert oracle.epoch_target_checked(-1, 4)[0] == oracle.INVALID_VALUE
+    assert oracle.epoch_target_checked(-(2**31), 1)[0] == oracle.INVALID_VALUE
+
+
+def test_round_simulator_stops_at_the_int32_limit():
+    # 8 members from one round below the limit: one more round completes and
+    # reaches the largest multiple of 8 in range; a second cannot.
+    top = (2**31 - 1) // 8 * 8
+    _, _, ctr, rc = oracle.slot_rounds(0, 1, 8, 0, counter0=top - 8)
+    assert (rc, ctr) == (oracle.OK, top)
+    _, _, _, rc = oracle.slot_rounds(0, 2, 8, 0, counter0=top - 8)
+    assert rc == oracle.INVALID_VALUE
+
+
 def test_participants_rule():
     assert oracle.participants(0, 256) == 256
     assert oracle.participants(128, 256) == 128
