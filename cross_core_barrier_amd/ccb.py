@@ -41,6 +41,7 @@ CCB_ERR_NOT_READY = 10
 
 CCB_SOFT_MAX_POLL = 1_000_000
 CCB_BREAKDOWN_MAX_ROUNDS = 1024
+CCB_NOALLOC_SCRATCH_BYTES = 4 << 20
 CCB_LINE_BYTES = 128
 CCB_STRIPES = 64
 CCB_SLOT_ROWS = 6
@@ -107,6 +108,8 @@ _f = {
                                    _I32, _I32, _U32, _I32, _V),
     "ccb_run_stencil": _sig("ccb_run_stencil", _I32, _V, _V, _I64, _I32, _V, _V, ctypes.c_size_t,
                             _V, _I32, _I32, _I32, _U32, _I32, _V),
+    "ccb_run_stencil_noalloc": _sig("ccb_run_stencil_noalloc", _I32, _V, _V, _I64, _I32, _V, _I32,
+                                    _I32, _I32, _U32, _I32, _V),
     "ccb_stencil_halo_bytes": _sig("ccb_stencil_halo_bytes", ctypes.c_size_t, _I64, _I32, _I32),
     "ccb_bench_barrier_breakdown": _sig("ccb_bench_barrier_breakdown", _I32, _V, _V, _I32, _I32,
                                         _I32, _I32, _I32, _V),
@@ -212,6 +215,12 @@ def ccb_run_stencil(buf_a, buf_b, n, iters, ws, halo, halo_bytes, n_grid, thread
     return _f["ccb_run_stencil"](_p(buf_a), _p(buf_b), n, iters, _p(ws), _p(halo), halo_bytes,
                                  _p(timeline), n_grid, threads, wgs_per_cu, max_poll, mode,
                                  _s(stream))
+
+
+def ccb_run_stencil_noalloc(buf_a, buf_b, n, iters, status_out, n_grid, threads, wgs_per_cu=0,
+                            max_poll=0, mode=0, stream=None) -> int:
+    return _f["ccb_run_stencil_noalloc"](_p(buf_a), _p(buf_b), n, iters, _p(status_out), n_grid,
+                                         threads, wgs_per_cu, max_poll, mode, _s(stream))
 
 
 # --- floor microbenchmarks --------------------------------------------------------

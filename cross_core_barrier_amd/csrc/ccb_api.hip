@@ -432,6 +432,28 @@ CCB_API size_t ccb_stencil_halo_bytes(int64_t n, int32_t threads, int32_t nGrid)
     return (size_t)2 * (size_t)nGrid * (size_t)kMax * 2 * sizeof(int32_t);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by both stencil entry points (everything but the
+// scratch arguments).  NULL buffers are checked by the callers first.
+bool stencil_args_ok(const int32_t* bufA, const int32_t* bufB, int64_t n, int32_t iters,
+                     int32_t nGrid, int32_t threads, int32_t wgsPerCu, int32_t mode)
+{
+    if (n < 1 || iters < 0 || !aligned(bufA, 16) || !aligned(bufB, 16) || nGrid < 1 ||
+        !valid_threads(threads) || wgsPerCu < 0 || !valid_mode(mode) ||
+        !counts_fit((int64_t)iters - 1, nGrid, mode))
+        return false;
+    const uintptr_t a0 = (uintptr_t)bufA, a1 = a0 + (uintptr_t)n * 4;
+    const uintptr_t b0 = (uintptr_t)bufB, b1 = b0 + (uintptr_t)n * 4;
+    return !(a0 < b1 && b0 < a1);  // the buffers must not overlap
+}
+
+}  // namespace
+
+extern "C" {
+
 CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32_t iters,
                                   int32_t* ws, int32_t* halo, size_t haloBytes,
                                   uint64_t* timeline, int32_t nGrid, int32_t threads,
@@ -441,16 +463,11 @@ CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32
     if (bufA == nullptr || bufB == nullptr || ws == nullptr) return CCB_ERR_NULL_POINTER;
     const bool needHalo = valid_mode(mode) && (mode & CCB_VISIBILITY_FULL) == 0;
     if (needHalo && halo == nullptr) return CCB_ERR_NULL_POINTER;
-    if (n < 1 || iters < 0 || !aligned(ws, CCB_LINE_BYTES) || !aligned(bufA, 16) ||
-        !aligned(bufB, 16) || nGrid < 1 || !valid_threads(threads) || wgsPerCu < 0 ||
-        !valid_mode(mode) || (halo != nullptr && !aligned(halo, 4)) ||
-        (timeline != nullptr && !aligned(timeline, 8)) ||
-        !counts_fit((int64_t)iters - 1, nGrid, mode))
+    if (!stencil_args_ok(bufA, bufB, n, iters, nGrid, threads, wgsPerCu, mode) ||
+        !aligned(ws, CCB_LINE_BYTES) || (halo != nullptr && !aligned(halo, 4)) ||
+        (timeline != nullptr && !aligned(timeline, 8)))
         return CCB_ERR_INVALID_VALUE;
     if (needHalo && haloBytes < ccb_stencil_halo_bytes(n, threads, nGrid)) return CCB_ERR_INVALID_VALUE;
-    const uintptr_t a0 = (uintptr_t)bufA, a1 = a0 + (uintptr_t)n * 4;
-    const uintptr_t b0 = (uintptr_t)bufB, b1 = b0 + (uintptr_t)n * 4;
-    if (a0 < b1 && b0 < a1) return CCB_ERR_INVALID_VALUE;  // overlapping buffers
     std::lock_guard<std::mutex> lk(g_launch_mu);
     ccb::LaunchShape ls;
     ccbStatus st = plan_persistent(ccb::KernelId::Stencil, mode, nGrid, threads, wgsPerCu,
@@ -458,6 +475,46 @@ CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32
     if (st != CCB_OK) return st;
     return from_hip(ccb::launch_stencil(ls, bufA, bufB, n, iters, ws, halo, timeline,
                                         poll_bound(maxPoll)));
+}
+
+CCB_API ccbStatus ccb_run_stencil_noalloc(int32_t* bufA, int32_t* bufB, int64_t n, int32_t iters,
+                                          int32_t* statusOut, int32_t nGrid, int32_t threads,
+                                          int32_t wgsPerCu, uint32_t maxPoll, int32_t mode,
+                                          ccbStream stream)
+{
+    if (bufA == nullptr || bufB == nullptr) return CCB_ERR_NULL_POINTER;
+    if (!stencil_args_ok(bufA, bufB, n, iters, nGrid, threads, wgsPerCu, mode) ||
+        (statusOut != nullptr && !aligned(statusOut, 4)))
+        return CCB_ERR_INVALID_VALUE;
+    // the scratch: the workspace of one barrier (padded to 256 B), then the
+    // halo buffer, which only the ordering-only barrier uses
+    const size_t wsBytes = (ccb_syncall_workspace_bytes(1) + 255) / 256 * 256;
+    const bool needHalo = (mode & CCB_VISIBILITY_FULL) == 0;
+    const size_t haloBytes = needHalo ? ccb_stencil_halo_bytes(n, threads, nGrid) : 0;
+    if (wsBytes + haloBytes > CCB_NOALLOC_SCRATCH_BYTES) return CCB_ERR_INVALID_VALUE;
+    int dev = 0;
+    ccbStatus st = current_device(&dev, nullptr);
+    if (st != CCB_OK) return st;
+    int32_t* scratch = nullptr;
+    if (ccb::noalloc_scratch(dev, &scratch) != hipSuccess) return hip_failed();
+    int32_t* ws = scratch;
+    int32_t* halo = needHalo ? scratch + wsBytes / 4 : nullptr;
+    std::lock_guard<std::mutex> lk(g_launch_mu);
+    ccb::LaunchShape ls;
+    st = plan_persistent(ccb::KernelId::Stencil, mode, nGrid, threads, wgsPerCu,
+                         (hipStream_t)stream, &ls);
+    if (st != CCB_OK) return st;
+    // the scratch keeps the previous call's contents: the stripes and the
+    // error word must start at zero (the halo is written before it is read)
+    const int64_t wsWords = (int64_t)ccb_syncall_workspace_bytes(1) / 4;
+    if ((st = from_hip(ccb::launch_fill_zero(ws, wsWords, (hipStream_t)stream))) != CCB_OK)
+        return st;
+    if ((st = from_hip(ccb::launch_stencil(ls, bufA, bufB, n, iters, ws, halo, nullptr,
+                                           poll_bound(maxPoll)))) != CCB_OK)
+        return st;
+    if (statusOut == nullptr) return CCB_OK;
+    return from_hip(ccb::launch_copy_word(ws + (size_t)CCB_STRIPES * kLineWords, statusOut,
+                                          (hipStream_t)stream));
 }
 
 // ===========================================================================

@@ -53,6 +53,10 @@ hipError_t launch_cnt_wait(uint32_t* line, int32_t mode, uint32_t value, int32_t
                            uint64_t timeoutTicks, hipStream_t s);
 hipError_t launch_cnt_reset(uint32_t* line, hipStream_t s);
 hipError_t launch_fill_zero(int32_t* p, int64_t nWords, hipStream_t s);
+hipError_t launch_copy_word(const int32_t* src, int32_t* dst, hipStream_t s);
+// Device address of the allocation-free entry point's scratch on device
+// `dev` (which must be current), looked up on the first call per device.
+hipError_t noalloc_scratch(int dev, int32_t** out);
 hipError_t launch_atomic_chain(int32_t* line, uint64_t* ticks, int32_t iters, int32_t fenced,
                                int32_t kind, hipStream_t s);
 hipError_t launch_atomic_contended(int32_t* line, uint64_t* ticks, int32_t iters, int32_t nGrid,

@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "ccb.h"
 #include "ccb_device.h"
 #include "ccb_internal.h"
@@ -1117,6 +1119,15 @@ __global__ void ccb_k_cnt_reset(uint32_t* line)
     __hip_atomic_store(line, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One word copied device-to-device with a device-coherent read (the error
+// word of a workspace into a caller's status word).
+__global__ void ccb_k_copy_word(const int32_t* src, int32_t* dst)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0)
+        *dst = __hip_atomic_load(const_cast<int32_t*>(src), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Zero fill (used instead of a memset so that captured graphs hold no
 // memset nodes).
 __global__ void ccb_k_fill_zero(int32_t* p, int64_t nWords)
@@ -1349,6 +1360,44 @@ hipError_t launch_register_query(KernelId id, int32_t mode, int32_t* out, hipStr
     }
     }
     return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free stencil entry point: the barrier workspace
+// (CCB_STRIPES stripe lines and the error line, padded to 256 bytes) and then
+// the halo exchange buffer, in one file-scope device array of
+// CCB_NOALLOC_SCRATCH_BYTES.  Every GPU the library runs on holds its own
+// copy until the process ends.  In host code the array's name is only a
+// host-side stand-in: its device address on the current device comes from
+// hipGetSymbolAddress, looked up once per device with that device current
+// and kept per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) int32_t scratch[CCB_NOALLOC_SCRATCH_BYTES / 4];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(int dev, int32_t** out)
+{
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_copy_word(const int32_t* src, int32_t* dst, hipStream_t s)
+{
+    hipLaunchKernelGGL(ccb_k_copy_word, dim3(1), dim3(kWave), 0, s, src, dst);
+    return hipGetLastError();
 }
 
 hipError_t launch_cnt_batch(const uint32_t* val, const uint8_t* meta, int64_t nCounters,

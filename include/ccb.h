@@ -309,6 +309,39 @@ CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32
  * busiest workgroup x 2 int32 (0 for invalid arguments). */
 CCB_API size_t ccb_stencil_halo_bytes(int64_t n, int32_t threads, int32_t nGrid);
 
+/* Bytes of the device scratch that ccb_run_stencil_noalloc uses on each GPU:
+ * a file-scope device array (held by every GPU the library runs on until the
+ * process ends) with the workspace of one barrier (8,448 bytes) and then the
+ * halo exchange buffer. */
+#define CCB_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/* ccb_run_stencil for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace and no halo scratch; both live in the
+ * library's own device scratch of CCB_NOALLOC_SCRATCH_BYTES, and the call
+ * allocates nothing (no hipMalloc / hipFree, no allocating library call).
+ * It enqueues on `stream`: a fill kernel that zeroes the workspace part, the
+ * stencil launch, and (statusOut != NULL) a one-lane kernel that copies the
+ * outcome word -- CCB_OK, CCB_ERR_DEADLOCK or CCB_ERR_INVALID_VALUE, as
+ * ccb_syncall_status reports it -- to *statusOut (device int32, 4-B
+ * aligned).  Arguments and results are those of ccb_run_stencil otherwise.
+ * Limit: with CCB_VISIBILITY_ORDER, 8,448 + ccb_stencil_halo_bytes(n,
+ * threads, nGrid) must fit in CCB_NOALLOC_SCRATCH_BYTES (n up to about
+ * 2.6e8 elements at 256 threads per workgroup); CCB_VISIBILITY_FULL needs
+ * only the workspace part.  Larger launches return CCB_ERR_INVALID_VALUE.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in
+ * time on one GPU (on different streams, or from different host threads
+ * without ordering) race on it and give wrong results; order them on one
+ * stream.  The first persistent launch of the process on a device also runs
+ * the launchers' one-time register query (see above): make one call outside
+ * stream capture first.
+ * Errors: as ccb_run_stencil (NULL_POINTER for bufA / bufB; INVALID_VALUE
+ * also for a launch beyond the scratch or a misaligned statusOut). */
+CCB_API ccbStatus ccb_run_stencil_noalloc(int32_t* bufA, int32_t* bufB, int64_t n, int32_t iters,
+                                          int32_t* statusOut, int32_t nGrid, int32_t threads,
+                                          int32_t wgsPerCu, uint32_t maxPoll, int32_t mode,
+                                          ccbStream stream);
+
 /* ========================================================================
  * Floor microbenchmarks (the barrier's latency and bandwidth roofline)
  * ======================================================================== */
