@@ -59,10 +59,11 @@ def parse():
     ap.add_argument("--mode", default="striped-order",
                     choices=["striped-order", "flat-order", "striped-full", "flat-full"])
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
-    ap.add_argument("--only", choices=["counters", "barrier"], default=None,
+    ap.add_argument("--only", choices=["counters", "barrier", "cnt"], default=None,
                     help="counters: only the copy ceiling, the stencil and the batched "
                          "CntNotify engine (counter collection); barrier: only the floor, "
-                         "the barrier-only latencies and their breakdown")
+                         "the barrier-only latencies and their breakdown; cnt: only the "
+                         "CntNotify stream legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     return ap.parse_args()
 
@@ -501,28 +502,39 @@ class Bench:
         log(f"cntnotify record + wait pair: {out}")
 
     # ------------------------------------------------------------ stream-to-stream notify
-    def cnt_stream_latency(self):
-        """CntNotify §5's pattern on streams: the consumer stream waits GE N
-        (isClear) while N producer streams each record ADD 1 after a short
-        spin (so the wait is usually polling already).  Latency = the last
-        record's completion to the wait's completion, from HIP events on the
-        streams; rounds are separated on the host.  The records are enqueued
-        before the wait, so that a wait never sits in a hardware queue in
-        front of the records it waits for (streams share the process's few
-        hardware queues); N = 1 and 2."""
+    def cnt_stream_latency(self, producers=(1, 2, 4, 8, 16), rounds=110, skip=10):
+        """CntNotify §5's pattern on streams at scale: N producer streams each
+        record ADD 1 after a short spin (so the wait is usually polling
+        already), the consumer stream waits GE N with isClear.  Latency = the
+        last record's completion to the wait's completion, from HIP events on
+        the streams; rounds are separated on the host.  The records are
+        enqueued before the wait, so that a wait never sits in a hardware
+        queue in front of the records it waits for (the process has 4
+        hardware queues).  Beside it, on the same streams, HIP's own
+        cross-stream dependency: each producer runs an empty one-lane kernel
+        and records an event, the consumer waits for all N events and runs an
+        empty one-lane kernel; latency = the last producer event to the
+        consumer's event.  And the floor of any stream-ordered wait: an empty
+        one-lane kernel between two events on one stream."""
         ccb, torch = self.ccb, self.torch
         out = {}
-        for n in (1, 2):
+
+        def stats(xs):
+            xs = sorted(xs)
+            return {"median_us": round(xs[len(xs) // 2], 2),
+                    "p90_us": round(xs[int(len(xs) * 0.9)], 2)}
+
+        for n in producers:
             prods = [torch.cuda.Stream() for _ in range(n)]
             cons = torch.cuda.Stream()
             st, h = ccb.ccb_cnt_notify_create(0)
             ccb.check(st, "create")
-            lat = []
-            for r in range(100):
+            lat, base = [], []
+            for r in range(rounds):
                 evs = []
                 for s in prods:  # producers first: see the docstring
                     with torch.cuda.stream(s):
-                        torch.cuda._sleep(50000)
+                        torch.cuda._sleep(20000)
                     ccb.check(ccb.ccb_cnt_notify_record(
                         h, s, ccb.record_info(ccb.CCB_CNT_RECORD_ADD, 1)), "record")
                     e = torch.cuda.Event(enable_timing=True)
@@ -534,13 +546,46 @@ class Bench:
                 ev_c.record(cons)
                 torch.cuda.synchronize()
                 st, v, last = ccb.ccb_cnt_notify_query(h, cons)
-                assert (st, v, last) == (0, 0, ccb.CCB_OK), (r, st, v, last)
-                if r >= 10:
+                assert (st, v, last) == (0, 0, ccb.CCB_OK), (n, r, st, v, last)
+                # the floor: the same dependency through HIP events
+                evs2 = []
+                for s in prods:
+                    with torch.cuda.stream(s):
+                        torch.cuda._sleep(20000)
+                        torch.cuda._sleep(1)  # empty one-lane kernel
+                    e = torch.cuda.Event(enable_timing=True)
+                    e.record(s)
+                    evs2.append(e)
+                for e in evs2:
+                    cons.wait_event(e)
+                with torch.cuda.stream(cons):
+                    torch.cuda._sleep(1)
+                ev_f = torch.cuda.Event(enable_timing=True)
+                ev_f.record(cons)
+                torch.cuda.synchronize()
+                if r >= skip:
                     lat.append(min(e.elapsed_time(ev_c) for e in evs) * 1e3)
+                    base.append(min(e.elapsed_time(ev_f) for e in evs2) * 1e3)
             ccb.check(ccb.ccb_cnt_notify_destroy(h), "destroy")
-            lat.sort()
-            out[f"producers_{n}"] = {"median_us": round(lat[len(lat) // 2], 2),
-                                     "p90_us": round(lat[int(len(lat) * 0.9)], 2)}
+            out[f"producers_{n}"] = {**stats(lat), "hip_event_dependency": stats(base)}
+        # the part no stream-ordered wait can avoid: a kernel's completion
+        # reaching an event on its stream (an empty one-lane kernel between
+        # two events on one stream), and two events back to back
+        s = torch.cuda.Stream()
+        kern, ev = [], []
+        for r in range(rounds):
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record(s)
+            e1.record(s)
+            with torch.cuda.stream(s):
+                torch.cuda._sleep(1)
+            e2.record(s)
+            e2.synchronize()
+            if r >= skip:
+                ev.append(e0.elapsed_time(e1) * 1e3)
+                kern.append(e1.elapsed_time(e2) * 1e3)
+        out["floor_empty_kernel_on_one_stream"] = stats(kern)
+        out["floor_event_to_event"] = stats(ev)
         self.extra["cntnotify_stream_notify_latency"] = out
         log(f"cntnotify stream notify latency: {out}")
 
@@ -649,6 +694,13 @@ def main():
                                                    "barrier_only_ns_by_workgroups",
                                                    "latency_roofline", "barrier_breakdown")}),
               flush=True)
+        return
+
+    if args.only == "cnt":
+        b.cnt_stream_latency()
+        b.cnt_graph()
+        print(json.dumps({k: b.extra[k] for k in ("cntnotify_stream_notify_latency",
+                                                   "cntnotify_record_wait_pair")}), flush=True)
         return
 
     ms_per_step, rounds = b.headline()

@@ -38,6 +38,7 @@ CCB_ERR_NOT_CORESIDENT = 7
 CCB_ERR_UNSUPPORTED_DEVICE = 8
 CCB_ERR_HIP = 9
 CCB_ERR_NOT_READY = 10
+CCB_ERR_CANCELLED = 11
 
 CCB_SOFT_MAX_POLL = 1_000_000
 CCB_BREAKDOWN_MAX_ROUNDS = 1024
@@ -125,6 +126,7 @@ _f = {
     "ccb_cnt_notify_reset": _sig("ccb_cnt_notify_reset", _I32, _V, _V),
     "ccb_cnt_notify_get_id": _sig("ccb_cnt_notify_get_id", _I32, _V, _V),
     "ccb_cnt_notify_destroy": _sig("ccb_cnt_notify_destroy", _I32, _V),
+    "ccb_cnt_notify_abort": _sig("ccb_cnt_notify_abort", _I32, _V),
     "ccb_cnt_notify_query": _sig("ccb_cnt_notify_query", _I32, _V, _V, _V, _V),
     "ccb_cnt_notify_batch": _sig("ccb_cnt_notify_batch", _I32, _V, _V, _I64, _I32, _V, _V, _I32, _V,
                                  _V),
@@ -281,6 +283,10 @@ def ccb_cnt_notify_get_id(h, null_out: bool = False):
 
 def ccb_cnt_notify_destroy(h) -> int:
     return _f["ccb_cnt_notify_destroy"](h)
+
+
+def ccb_cnt_notify_abort(h) -> int:
+    return _f["ccb_cnt_notify_abort"](h)
 
 
 def ccb_cnt_notify_query(h, stream=None):

@@ -203,16 +203,56 @@ inline bool counts_fit(int64_t barriers, int64_t members, int32_t mode)
 // CntNotify handle table (CntNotify interfaces §4.1, §4.5, §4.6, §6.1).
 // A handle value encodes (generation << 20) | (index + 1); it is never
 // dereferenced, so a stale or made-up handle is detected, not followed.
+//
+// Each handle owns one 128-B line of the device pool.  Within the line,
+// generation g uses the word pair (count, outcome) at words 2 (g mod 16) and
+// 2 (g mod 16) + 1, so kernels still queued for a destroyed handle act on
+// their own generation's pair, never on the count of the line's next owner.
+// Freed lines go to the back of a FIFO and are reused least recently freed
+// first, so a line comes back to a pair it used before only after 16
+// generations of reuse.
+//
+// Cancel tokens: one uint32 per line in coherent pinned host memory.  A wait
+// kernel carries the token its line had when it was enqueued and ends with
+// CCB_ERR_CANCELLED once the token changes; abort and destroy change it.
 // ---------------------------------------------------------------------------
+constexpr uint32_t kGenPairs = CCB_LINE_BYTES / 8;
+
 struct CntSlot {
     bool alive = false;
     uint32_t gen = 0;
     int device = -1;
 };
 
+struct CntFreeList {
+    uint32_t q[CCB_CNT_NOTIFY_POOL];
+    uint32_t head = 0, size = 0;
+    CntFreeList()
+    {
+        for (uint32_t i = 0; i < CCB_CNT_NOTIFY_POOL; ++i) q[i] = i;
+        size = CCB_CNT_NOTIFY_POOL;
+    }
+    bool pop(uint32_t* idx)
+    {
+        if (size == 0) return false;
+        *idx = q[head];
+        head = (head + 1) % CCB_CNT_NOTIFY_POOL;
+        --size;
+        return true;
+    }
+    void push(uint32_t idx)
+    {
+        q[(head + size) % CCB_CNT_NOTIFY_POOL] = idx;
+        ++size;
+    }
+};
+
 std::mutex g_cnt_mu;
 CntSlot g_cnt[CCB_CNT_NOTIFY_POOL];
+CntFreeList g_cnt_free;
 uint32_t* g_cnt_pool[kMaxDevices] = {nullptr};
+uint32_t* g_cnt_cancel[kMaxDevices] = {nullptr};     // host view of the tokens
+uint32_t* g_cnt_cancel_dev[kMaxDevices] = {nullptr}; // the same words, device view
 constexpr uint32_t kLineWords = CCB_LINE_BYTES / 4;
 
 ccbCntNotify encode_handle(uint32_t idx, uint32_t gen)
@@ -221,10 +261,18 @@ ccbCntNotify encode_handle(uint32_t idx, uint32_t gen)
     return reinterpret_cast<ccbCntNotify>(v);
 }
 
-// Looks a handle up; on success *line is its device line.  `kill` also marks
-// the slot free, under the same lock as the check, so that of two concurrent
-// destroys of one handle only one succeeds.
-ccbStatus resolve(ccbCntNotify h, uint32_t* idxOut, uint32_t** line, bool kill = false)
+// What a call on a live handle needs.
+struct CntRef {
+    uint32_t idx;
+    uint32_t* pair;         // device: count, then outcome
+    uint32_t* cancelHost;   // host view of the line's cancel token
+    const uint32_t* cancelDev;
+};
+
+// Looks a handle up.  `kill` also marks the slot free, under the same lock
+// as the check, so that of two concurrent destroys of one handle only one
+// succeeds.
+ccbStatus resolve(ccbCntNotify h, CntRef* ref, bool kill = false)
 {
     const uintptr_t v = reinterpret_cast<uintptr_t>(h);
     if (v == 0) return CCB_ERR_INVALID_HANDLE;
@@ -238,11 +286,21 @@ ccbStatus resolve(ccbCntNotify h, uint32_t* idxOut, uint32_t** line, bool kill =
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hip_failed();
     if (dev != s.device) return CCB_ERR_INVALID_HANDLE;
-    if (kill) s.alive = false;
-    if (idxOut) *idxOut = idx;
-    if (line) *line = g_cnt_pool[s.device] + (size_t)idx * kLineWords;
+    if (kill) {
+        s.alive = false;
+        g_cnt_free.push(idx);
+    }
+    if (ref != nullptr) {
+        ref->idx = idx;
+        ref->pair = g_cnt_pool[s.device] + (size_t)idx * kLineWords + 2 * (s.gen % kGenPairs);
+        ref->cancelHost = g_cnt_cancel[s.device] + idx;
+        ref->cancelDev = g_cnt_cancel_dev[s.device] + idx;
+    }
     return CCB_OK;
 }
+
+// Ends the waits enqueued so far on a line: they see a new token.
+void cancel_waits(const CntRef& ref) { __atomic_fetch_add(ref.cancelHost, 1u, __ATOMIC_RELEASE); }
 
 }  // namespace
 
@@ -265,6 +323,7 @@ CCB_API const char* ccb_status_string(ccbStatus s)
     case CCB_ERR_UNSUPPORTED_DEVICE: return "CCB_ERR_UNSUPPORTED_DEVICE";
     case CCB_ERR_HIP: return "CCB_ERR_HIP";
     case CCB_ERR_NOT_READY: return "CCB_ERR_NOT_READY";
+    case CCB_ERR_CANCELLED: return "CCB_ERR_CANCELLED";
     default: return "CCB_ERR_UNKNOWN";
     }
 }
@@ -600,45 +659,58 @@ CCB_API ccbStatus ccb_cnt_notify_create(ccbCntNotify* out, uint64_t flag)
             return hip_failed();
         g_cnt_pool[dev] = static_cast<uint32_t*>(p);
     }
-    uint32_t idx = CCB_CNT_NOTIFY_POOL;
-    for (uint32_t i = 0; i < CCB_CNT_NOTIFY_POOL; ++i) {
-        if (!g_cnt[i].alive) { idx = i; break; }
+    if (g_cnt_cancel[dev] == nullptr) {
+        // coherent: the device's system-scope reads see the host's stores
+        void* hp = nullptr;
+        void* dp = nullptr;
+        if (hipHostMalloc(&hp, (size_t)CCB_CNT_NOTIFY_POOL * sizeof(uint32_t),
+                          hipHostMallocCoherent | hipHostMallocMapped) != hipSuccess)
+            return hip_failed();
+        memset(hp, 0, (size_t)CCB_CNT_NOTIFY_POOL * sizeof(uint32_t));
+        if (hipHostGetDevicePointer(&dp, hp, 0) != hipSuccess) {
+            (void)hipHostFree(hp);
+            return hip_failed();
+        }
+        g_cnt_cancel[dev] = static_cast<uint32_t*>(hp);
+        g_cnt_cancel_dev[dev] = static_cast<uint32_t*>(dp);
     }
-    if (idx == CCB_CNT_NOTIFY_POOL) return CCB_ERR_RESOURCE_EXHAUSTED;
-    // count 0, no wait completed yet
-    uint32_t init[kLineWords];
-    memset(init, 0, sizeof(init));
-    init[1] = (uint32_t)CCB_ERR_NOT_READY;
-    if (hipMemcpy(g_cnt_pool[dev] + (size_t)idx * kLineWords, init, sizeof(init),
-                  hipMemcpyHostToDevice) != hipSuccess)
-        return hip_failed();
+    uint32_t idx = 0;
+    if (!g_cnt_free.pop(&idx)) return CCB_ERR_RESOURCE_EXHAUSTED;
     CntSlot& s = g_cnt[idx];
+    uint32_t gen = (s.gen + 1) & 0xFFFFFu;
+    if (gen == 0) gen = 1;
+    // count 0, no wait completed yet, in this generation's pair
+    const uint32_t init[2] = {0u, (uint32_t)CCB_ERR_NOT_READY};
+    if (hipMemcpy(g_cnt_pool[dev] + (size_t)idx * kLineWords + 2 * (gen % kGenPairs), init,
+                  sizeof(init), hipMemcpyHostToDevice) != hipSuccess) {
+        g_cnt_free.push(idx);
+        return hip_failed();
+    }
     s.alive = true;
-    s.gen = (s.gen + 1) & 0xFFFFFu;
-    if (s.gen == 0) s.gen = 1;
+    s.gen = gen;
     s.device = dev;
-    *out = encode_handle(idx, s.gen);
+    *out = encode_handle(idx, gen);
     return CCB_OK;
 }
 
 CCB_API ccbStatus ccb_cnt_notify_record(ccbCntNotify h, ccbStream stream,
                                         const ccbCntRecordInfo* info)
 {
-    uint32_t* line = nullptr;
-    ccbStatus st = resolve(h, nullptr, &line);
+    CntRef ref;
+    ccbStatus st = resolve(h, &ref);
     if (st != CCB_OK) return st;
     if (info == nullptr) return CCB_ERR_NULL_POINTER;
     const int32_t m = info->mode;
     if (!(m == CCB_CNT_RECORD_SET_VALUE || m == CCB_CNT_RECORD_ADD || m == CCB_CNT_RECORD_BIT_OR ||
           m == CCB_CNT_RECORD_BIT_AND))
         return CCB_ERR_INVALID_VALUE;
-    return from_hip(ccb::launch_cnt_record(line, m, info->value, (hipStream_t)stream));
+    return from_hip(ccb::launch_cnt_record(ref.pair, m, info->value, (hipStream_t)stream));
 }
 
 CCB_API ccbStatus ccb_cnt_notify_wait(ccbCntNotify h, ccbStream stream, const ccbCntWaitInfo* info)
 {
-    uint32_t* line = nullptr;
-    ccbStatus st = resolve(h, nullptr, &line);
+    CntRef ref;
+    ccbStatus st = resolve(h, &ref);
     if (st != CCB_OK) return st;
     if (info == nullptr) return CCB_ERR_NULL_POINTER;
     if (info->mode < CCB_CNT_WAIT_LESS || info->mode > CCB_CNT_WAIT_EQUAL_WITH_BITMASK ||
@@ -648,42 +720,56 @@ CCB_API ccbStatus ccb_cnt_notify_wait(ccbCntNotify h, ccbStream stream, const cc
     st = current_device(nullptr, &dinfo);
     if (st != CCB_OK) return st;
     const uint64_t ticks = (uint64_t)info->timeout * (uint64_t)dinfo.wallClockKHz * 1000ull;
-    return from_hip(ccb::launch_cnt_wait(line, info->mode, info->value, info->isClear, ticks,
-                                         (hipStream_t)stream));
+    const uint32_t token = __atomic_load_n(ref.cancelHost, __ATOMIC_ACQUIRE);
+    return from_hip(ccb::launch_cnt_wait(ref.pair, info->mode, info->value, info->isClear, ticks,
+                                         ref.cancelDev, token, (hipStream_t)stream));
 }
 
 CCB_API ccbStatus ccb_cnt_notify_reset(ccbCntNotify h, ccbStream stream)
 {
-    uint32_t* line = nullptr;
-    ccbStatus st = resolve(h, nullptr, &line);
+    CntRef ref;
+    ccbStatus st = resolve(h, &ref);
     if (st != CCB_OK) return st;
-    return from_hip(ccb::launch_cnt_reset(line, (hipStream_t)stream));
+    return from_hip(ccb::launch_cnt_reset(ref.pair, (hipStream_t)stream));
 }
 
 CCB_API ccbStatus ccb_cnt_notify_get_id(ccbCntNotify h, uint32_t* id)
 {
-    uint32_t idx = 0;
-    ccbStatus st = resolve(h, &idx, nullptr);
+    CntRef ref;
+    ccbStatus st = resolve(h, &ref);
     if (st != CCB_OK) return st;
     if (id == nullptr) return CCB_ERR_NULL_POINTER;
-    *id = idx;
+    *id = ref.idx;
+    return CCB_OK;
+}
+
+CCB_API ccbStatus ccb_cnt_notify_abort(ccbCntNotify h)
+{
+    CntRef ref;
+    ccbStatus st = resolve(h, &ref);
+    if (st != CCB_OK) return st;
+    cancel_waits(ref);
     return CCB_OK;
 }
 
 CCB_API ccbStatus ccb_cnt_notify_destroy(ccbCntNotify h)
 {
-    return resolve(h, nullptr, nullptr, true);
+    CntRef ref;
+    ccbStatus st = resolve(h, &ref, true);
+    if (st != CCB_OK) return st;
+    cancel_waits(ref);  // a wait still queued for the handle ends instead of spinning
+    return CCB_OK;
 }
 
 CCB_API ccbStatus ccb_cnt_notify_query(ccbCntNotify h, uint32_t* value, ccbStatus* lastWait,
                                        ccbStream stream)
 {
-    uint32_t* line = nullptr;
-    ccbStatus st = resolve(h, nullptr, &line);
+    CntRef ref;
+    ccbStatus st = resolve(h, &ref);
     if (st != CCB_OK) return st;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return hip_failed();
     uint32_t words[2] = {0, 0};
-    if (hipMemcpy(words, line, sizeof(words), hipMemcpyDeviceToHost) != hipSuccess)
+    if (hipMemcpy(words, ref.pair, sizeof(words), hipMemcpyDeviceToHost) != hipSuccess)
         return hip_failed();
     if (value) *value = words[0];
     if (lastWait) *lastWait = (ccbStatus)words[1];

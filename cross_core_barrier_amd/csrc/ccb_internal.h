@@ -50,7 +50,8 @@ hipError_t launch_cnt_batch(const uint32_t* val, const uint8_t* meta, int64_t nC
                             int32_t* err, int perThread, hipStream_t s);
 hipError_t launch_cnt_record(uint32_t* line, int32_t mode, uint32_t value, hipStream_t s);
 hipError_t launch_cnt_wait(uint32_t* line, int32_t mode, uint32_t value, int32_t isClear,
-                           uint64_t timeoutTicks, hipStream_t s);
+                           uint64_t timeoutTicks, const uint32_t* cancel, uint32_t token,
+                           hipStream_t s);
 hipError_t launch_cnt_reset(uint32_t* line, hipStream_t s);
 hipError_t launch_fill_zero(int32_t* p, int64_t nWords, hipStream_t s);
 hipError_t launch_copy_word(const int32_t* src, int32_t* dst, hipStream_t s);

@@ -1084,15 +1084,21 @@ __global__ void ccb_k_cnt_record(uint32_t* line, int32_t mode, uint32_t value)
 // predicate holds or the timeout passes.  A release with isClear swaps the
 // count it saw for 0 in one compare-and-swap, so a record landing between
 // the check and the clear makes the swap fail and the wait looks again.
-// The outcome goes to word 1 of the handle's line.
+// The outcome goes to the word after the count.
+//
+// cancel: a word in host memory (coherent, pinned) that the host changes to
+// call off the waits enqueued before it; every 64 polls the wait reads it
+// at system scope and, if it no longer holds `token`, ends with
+// CCB_ERR_CANCELLED (no clear).  This is how a wait without a time limit
+// can still be ended.
 __global__ void ccb_k_cnt_wait(uint32_t* line, int32_t mode, uint32_t value, int32_t isClear,
-                               uint64_t timeoutTicks)
+                               uint64_t timeoutTicks, const uint32_t* cancel, uint32_t token)
 {
     if (!leader()) return;
     int32_t* outcome = reinterpret_cast<int32_t*>(line + 1);
     const uint64_t t0 = wall_clock64();
     int32_t result = CCB_ERR_TIMEOUT;
-    for (;;) {
+    for (uint32_t polls = 1;; ++polls) {
         uint32_t c = __hip_atomic_load(line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         bool bad;
         if (cnt_holds(c, (uint32_t)mode, value, bad)) {
@@ -1105,6 +1111,12 @@ __global__ void ccb_k_cnt_wait(uint32_t* line, int32_t mode, uint32_t value, int
             continue;  // the count moved under us: evaluate the new value
         }
         if (timeoutTicks != 0 && wall_clock64() - t0 >= timeoutTicks) break;
+        if ((polls % 64) == 0 &&
+            __hip_atomic_load(const_cast<uint32_t*>(cancel), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_SYSTEM) != token) {
+            result = CCB_ERR_CANCELLED;
+            break;
+        }
         __builtin_amdgcn_s_sleep(2);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -1426,10 +1438,11 @@ hipError_t launch_cnt_record(uint32_t* line, int32_t mode, uint32_t value, hipSt
 }
 
 hipError_t launch_cnt_wait(uint32_t* line, int32_t mode, uint32_t value, int32_t isClear,
-                           uint64_t timeoutTicks, hipStream_t s)
+                           uint64_t timeoutTicks, const uint32_t* cancel, uint32_t token,
+                           hipStream_t s)
 {
     hipLaunchKernelGGL(ccb_k_cnt_wait, dim3(1), dim3(kWave), 0, s, line, mode, value, isClear,
-                       timeoutTicks);
+                       timeoutTicks, cancel, token);
     return hipGetLastError();
 }
 

@@ -59,7 +59,8 @@ enum {
     CCB_ERR_NOT_CORESIDENT = 7,     /* the grid cannot be resident at once ([SYNCALL] §6.3) */
     CCB_ERR_UNSUPPORTED_DEVICE = 8, /* current device is not gfx950 */
     CCB_ERR_HIP = 9,                /* the HIP runtime reported an error */
-    CCB_ERR_NOT_READY = 10          /* no CntNotify wait has completed yet */
+    CCB_ERR_NOT_READY = 10,         /* no CntNotify wait has completed yet */
+    CCB_ERR_CANCELLED = 11          /* a CntNotify wait ended by abort or destroy */
 };
 
 /* Default poll bound of the soft barrier: [SYNCALL] §5.2 bounds the poll at
@@ -452,12 +453,14 @@ CCB_API ccbStatus ccb_cnt_notify_record(ccbCntNotify h, ccbStream stream,
  * count, or until info->timeout seconds have passed (0 = no limit).  When it
  * is released and isClear is 1 the count is set to 0 atomically with the
  * check that released it (a concurrent record is never lost).  The outcome
- * (CCB_OK or CCB_ERR_TIMEOUT) is stored with the handle; read it with
- * ccb_cnt_notify_query.  A timed-out wait does not clear.  The wait is a
- * one-lane polling kernel: streams share a few hardware queues, and a queue
- * runs its kernels in order, so enqueue the records a wait depends on before
- * the wait (or give the wait a timeout); a record queued behind a wait with
- * no limit on the same hardware queue can never run.
+ * (CCB_OK, CCB_ERR_TIMEOUT or CCB_ERR_CANCELLED) is stored with the
+ * handle; read it with ccb_cnt_notify_query.  A timed-out or cancelled wait
+ * does not clear.  The wait is a one-lane polling kernel: streams share a
+ * few hardware queues, and a queue runs its kernels in order, so enqueue the
+ * records a wait depends on before the wait (or give the wait a timeout); a
+ * record queued behind a wait with no limit on the same hardware queue can
+ * never run.  Such a wait can still be ended from the host with
+ * ccb_cnt_notify_abort or ccb_cnt_notify_destroy.
  * Errors: INVALID_HANDLE, NULL_POINTER (info), INVALID_VALUE (mode,
  * isClear > 1, rev not zero). */
 CCB_API ccbStatus ccb_cnt_notify_wait(ccbCntNotify h, ccbStream stream,
@@ -473,15 +476,32 @@ CCB_API ccbStatus ccb_cnt_notify_reset(ccbCntNotify h, ccbStream stream);
 CCB_API ccbStatus ccb_cnt_notify_get_id(ccbCntNotify h, uint32_t* id);
 
 /* [CNTNOTIFY] §4.6.  Return the handle's line to the pool; the handle is
- * invalid afterwards (later calls on it return CCB_ERR_INVALID_HANDLE).  The
- * caller must not destroy a handle that queued work still uses.
+ * invalid afterwards (later calls on it return CCB_ERR_INVALID_HANDLE).
+ * Waits on the handle that are still queued or polling end as by
+ * ccb_cnt_notify_abort, so no stream stays blocked on a destroyed handle.
+ * Records and resets still queued for it act on the line's word pair of
+ * this handle's generation only: each of the 16 generations of a line uses
+ * its own (count, outcome) pair, and freed lines are reused least recently
+ * freed first, so they never reach the count of the line's next owner
+ * unless that line has since been reused 16 times.
  * Errors: INVALID_HANDLE. */
 CCB_API ccbStatus ccb_cnt_notify_destroy(ccbCntNotify h);
 
+/* Calls off every wait on h enqueued before this call (not on the pages,
+ * whose waits end only by release or time-out; for a stream whose wait can
+ * no longer be satisfied, such as a wait with no time limit).  Each such
+ * wait that has not been released ends with CCB_ERR_CANCELLED, does not
+ * clear, and unblocks its stream; waits enqueued after the call are not
+ * affected.  The host stores a new token for the handle in pinned host
+ * memory and returns at once; a polling wait reads the token every 64 polls
+ * (tens of microseconds).
+ * Errors: INVALID_HANDLE. */
+CCB_API ccbStatus ccb_cnt_notify_abort(ccbCntNotify h);
+
 /* Test and diagnostics hook (not on the pages): wait for `stream`, then copy
  * the current count to *value and the outcome of the last completed wait to
- * *lastWait (CCB_OK, CCB_ERR_TIMEOUT, or CCB_ERR_NOT_READY if none has
- * completed since create).  Either pointer may be NULL.  Blocks the host.
+ * *lastWait (CCB_OK, CCB_ERR_TIMEOUT, CCB_ERR_CANCELLED, or
+ * CCB_ERR_NOT_READY if none has completed since create).  Either pointer may be NULL.  Blocks the host.
  * Errors: INVALID_HANDLE, HIP. */
 CCB_API ccbStatus ccb_cnt_notify_query(ccbCntNotify h, uint32_t* value, ccbStatus* lastWait,
                                        ccbStream stream);

@@ -24,9 +24,14 @@ block forever (timeout 0).  This matches a polling GPU wait exactly when the
 outcome does not depend on which intermediate counts the poll observes, which
 is the only kind of sequence the tests give it.
 
+Beyond the pages: abort(h) calls off the waits pending on h -- each ends
+with CANCELLED and does not clear -- and leaves later waits alone (the
+library's ccb_cnt_notify_abort; destroy does the same to the waits of the
+handle it ends).
+
 Status codes restated here (the oracle includes nothing from the library):
 OK 0, INVALID_VALUE 1, NULL_POINTER 2, INVALID_HANDLE 3, RESOURCE_EXHAUSTED 4,
-TIMEOUT 5.
+TIMEOUT 5, CANCELLED 11.
 """
 
 from __future__ import annotations
@@ -35,6 +40,7 @@ from dataclasses import dataclass
 from typing import Dict, List, Optional, Tuple
 
 OK, INVALID_VALUE, NULL_POINTER, INVALID_HANDLE, RESOURCE_EXHAUSTED, TIMEOUT = 0, 1, 2, 3, 4, 5
+CANCELLED = 11
 
 M32 = 0xFFFFFFFF
 
@@ -139,6 +145,15 @@ class CntNotifyModel:
         if not want_out:
             return NULL_POINTER, None
         return OK, h
+
+    def abort(self, h) -> int:
+        """Every wait pending on h ends with CANCELLED, without its clear."""
+        if not self._valid(h):
+            return INVALID_HANDLE
+        if self.pending[h]:
+            self.pending[h].clear()
+            self.last_wait[h] = CANCELLED
+        return OK
 
     def destroy(self, h) -> int:
         if not self._valid(h):

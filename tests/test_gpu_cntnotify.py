@@ -178,6 +178,112 @@ def test_n_producers(ccb):
     assert ccb.ccb_cnt_notify_destroy(h) == 0
 
 
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16])
+def test_n_producers_at_scale(ccb, n):
+    """CntNotify §5 and §7 at scale: N producer streams (more streams than the
+    process's hardware queues from N = 4 on) each record ADD 1 per round, the
+    consumer stream waits GE N with isClear, over 100 rounds; every round is
+    checked against the handle model.  The records are enqueued before the
+    wait, so that no wait sits in a hardware queue in front of a record it
+    needs (each producer first spins a little, so the wait usually starts
+    polling before the records land)."""
+    rounds = 100
+    _say(f"cntnotify at scale: {n} producers ADD 1, consumer GE {n} with clear, {rounds} rounds")
+    prods = [torch.cuda.Stream() for _ in range(n)]
+    cons = torch.cuda.Stream()
+    h = _mk(ccb)
+    m = handles.CntNotifyModel(capacity=1)
+    _, mh = m.create(0)
+    for r in range(rounds):
+        for s in prods:
+            with torch.cuda.stream(s):
+                torch.cuda._sleep(20000)
+            assert ccb.ccb_cnt_notify_record(h, s, ccb.record_info(ccb.CCB_CNT_RECORD_ADD, 1)) == 0
+            assert m.record(mh, (ccb.CCB_CNT_RECORD_ADD, 1)) == handles.OK
+        assert ccb.ccb_cnt_notify_wait(
+            h, cons, ccb.wait_info(ccb.CCB_CNT_WAIT_BIGGER_OR_EQUAL, n, 2, 1)) == 0
+        assert m.wait(mh, (ccb.CCB_CNT_WAIT_BIGGER_OR_EQUAL, n, 2, 1)) == handles.OK
+        torch.cuda.synchronize()
+        st, v, last = ccb.ccb_cnt_notify_query(h, cons)
+        assert (st, v, last) == (0, m.count[mh], m.last_wait[mh]) == (0, 0, ccb.CCB_OK), r
+    assert ccb.ccb_cnt_notify_destroy(h) == 0
+
+
+def test_abort_ends_a_pending_wait(ccb):
+    """ccb_cnt_notify_abort from the host while a wait (GE 1, nothing will
+    record) polls: the wait ends with CANCELLED well before its 5 s limit,
+    does not clear, and the handle keeps working; as in the handle model."""
+    import time
+    _say("cntnotify abort of a polling wait (5 s limit, no record)")
+    s = torch.cuda.Stream()
+    h = _mk(ccb)
+    m = handles.CntNotifyModel(capacity=1)
+    _, mh = m.create(0)
+    assert ccb.ccb_cnt_notify_record(h, s, ccb.record_info(ccb.CCB_CNT_RECORD_SET_VALUE, 0)) == 0
+    m.record(mh, (ccb.CCB_CNT_RECORD_SET_VALUE, 0))
+    t0 = time.perf_counter()
+    assert ccb.ccb_cnt_notify_wait(h, s, ccb.wait_info(ccb.CCB_CNT_WAIT_BIGGER_OR_EQUAL, 1, 5, 1)) == 0
+    m.wait(mh, (ccb.CCB_CNT_WAIT_BIGGER_OR_EQUAL, 1, 5, 1))
+    time.sleep(0.05)  # the wait is polling by now
+    assert ccb.ccb_cnt_notify_abort(h) == 0
+    m.abort(mh)
+    s.synchronize()
+    assert time.perf_counter() - t0 < 2.0
+    st, v, last = ccb.ccb_cnt_notify_query(h, s)
+    assert (st, v, last) == (0, m.count[mh], m.last_wait[mh]) == (0, 0, ccb.CCB_ERR_CANCELLED)
+    # later waits are not affected
+    assert ccb.ccb_cnt_notify_record(h, s, ccb.record_info(ccb.CCB_CNT_RECORD_ADD, 4)) == 0
+    assert ccb.ccb_cnt_notify_wait(h, s, ccb.wait_info(ccb.CCB_CNT_WAIT_EQUAL, 4, 5, 1)) == 0
+    assert ccb.ccb_cnt_notify_query(h, s) == (0, 0, ccb.CCB_OK)
+    assert ccb.ccb_cnt_notify_destroy(h) == 0
+    assert ccb.ccb_cnt_notify_abort(h) == ccb.CCB_ERR_INVALID_HANDLE
+
+
+def test_destroy_ends_a_pending_wait(ccb):
+    """A wait still polling when its handle is destroyed ends (CANCELLED), so
+    its stream does not stay blocked until the 5 s limit."""
+    import time
+    _say("cntnotify destroy while a wait polls (5 s limit, no record)")
+    s = torch.cuda.Stream()
+    h = _mk(ccb)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t0 = time.perf_counter()
+    assert ccb.ccb_cnt_notify_wait(h, s, ccb.wait_info(ccb.CCB_CNT_WAIT_BIGGER_OR_EQUAL, 1, 5, 0)) == 0
+    with torch.cuda.stream(s):
+        flag.fill_(1)  # ordered after the wait
+    time.sleep(0.05)
+    assert ccb.ccb_cnt_notify_destroy(h) == 0
+    s.synchronize()
+    assert time.perf_counter() - t0 < 2.0
+    assert int(flag.item()) == 1
+
+
+def test_stale_record_does_not_reach_the_next_owner(ccb):
+    """A record enqueued for a handle, but run only after that handle was
+    destroyed and its line given to a new handle, changes the old
+    generation's count, not the new owner's."""
+    _say("cntnotify stale record after the line changed owner")
+    hs = []
+    for _ in range(ccb.CCB_CNT_NOTIFY_POOL):
+        st, x = ccb.ccb_cnt_notify_create(0)
+        assert st == 0
+        hs.append(x)
+    old = hs.pop(7)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(20_000_000)  # the record below runs after the re-create
+    assert ccb.ccb_cnt_notify_record(old, s, ccb.record_info(ccb.CCB_CNT_RECORD_ADD, 5)) == 0
+    line = ccb.ccb_cnt_notify_get_id(old)[1]
+    assert ccb.ccb_cnt_notify_destroy(old) == 0
+    st, new = ccb.ccb_cnt_notify_create(0)  # the only free line: the same one
+    assert st == 0 and ccb.ccb_cnt_notify_get_id(new)[1] == line
+    hs.append(new)
+    s.synchronize()
+    assert ccb.ccb_cnt_notify_query(new, None) == (0, 0, ccb.CCB_ERR_NOT_READY)
+    for x in hs:
+        assert ccb.ccb_cnt_notify_destroy(x) == 0
+
+
 def test_rounds_reuse_with_clear(ccb):
     """CntNotify §5/§7: the same counter reused round after round -- N producer
     streams ADD 1, the consumer waits GE N with isClear -- each round released

@@ -238,6 +238,27 @@ def test_model_error_codes():
     assert m.create(0)[0] == handles.OK                        # the resource came back
 
 
+def test_model_abort():
+    # abort is the library's extension: pending waits end CANCELLED with no
+    # clear; a wait that is already released, or one enqueued afterwards, is
+    # untouched
+    m = handles.CntNotifyModel(capacity=1)
+    _, h = m.create(0)
+    assert m.record(h, (0, 3)) == handles.OK
+    assert m.wait(h, (3, 5, 0, 1)) == handles.OK               # GE 5: pending
+    assert m.last_wait[h] is None
+    assert m.abort(h) == handles.OK
+    assert (m.count[h], m.last_wait[h]) == (3, handles.CANCELLED)
+    assert m.record(h, (1, 2)) == handles.OK                   # 5 now: nothing left to release
+    assert m.last_wait[h] == handles.CANCELLED
+    assert m.wait(h, (1, 5, 0, 1)) == handles.OK               # EQUAL 5, clear
+    assert (m.count[h], m.last_wait[h]) == (0, handles.OK)
+    assert m.abort(h) == handles.OK                            # nothing pending
+    assert m.last_wait[h] == handles.OK
+    assert m.destroy(h) == handles.OK
+    assert m.abort(h) == handles.INVALID_HANDLE
+
+
 # --- batch interpreter vs the sequential model --------------------------------------
 
 def _model_batch(val, meta, n_rel_rows):
