@@ -57,7 +57,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--mode", default="striped-order",
-                    choices=["striped-order", "flat-order", "striped-full", "flat-full"])
+                    choices=["striped-order", "flat-order", "striped-full", "flat-full",
+                             "tree-order", "tree-full"])
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
     ap.add_argument("--only", choices=["counters", "barrier", "cnt"], default=None,
                     help="counters: only the copy ceiling, the stencil and the batched "
@@ -243,23 +244,28 @@ class Bench:
             ccb.check(st, "barrier_only status")
             lat[name] = round((res[5000] - res[1000]) / 4000 * 1e6, 1)
         self.extra["barrier_only_ns_at_256"] = lat
-        # the chosen variant against the number of workgroups (256 threads each)
-        by_n = {}
-        m = ccb.MODES[self.args.mode]
-        for n in (2, 8, 64, 256, 512, 1024):
-            res = {}
-            for r in (1000, 5000):
-                def f(r=r, n=n):
-                    ccb.check(ccb.ccb_syncall_workspace_reset(ws, 1, stream), "reset")
-                    ccb.check(ccb.ccb_run_barrier_only(ws, None, None, r, n, 256, 0, 0, 0, m,
-                                                       stream), "barrier_only")
-                f()
-                res[r] = min(self.timer(f) for _ in range(3))
-            st, arr = ccb.ccb_syncall_status(ws, 1, stream)
-            ccb.check(st, "barrier_only status")
-            assert arr == [5000 * n], arr
-            by_n[str(n)] = round((res[5000] - res[1000]) / 4000 * 1e6, 1)
-        self.extra["barrier_only_ns_by_workgroups"] = by_n
+        # the chosen variant against the number of workgroups (256 threads
+        # each), and beside it the two-level tree (the striped counter's
+        # alternative for cutting same-address serialisation)
+        def by_workgroups(m):
+            by_n = {}
+            for n in (2, 8, 64, 256, 512, 1024):
+                res = {}
+                for r in (1000, 5000):
+                    def f(r=r, n=n):
+                        ccb.check(ccb.ccb_syncall_workspace_reset(ws, 1, stream), "reset")
+                        ccb.check(ccb.ccb_run_barrier_only(ws, None, None, r, n, 256, 0, 0, 0, m,
+                                                           stream), "barrier_only")
+                    f()
+                    res[r] = min(self.timer(f) for _ in range(3))
+                st, arr = ccb.ccb_syncall_status(ws, 1, stream)
+                ccb.check(st, "barrier_only status")
+                assert arr == [5000 * n], arr
+                by_n[str(n)] = round((res[5000] - res[1000]) / 4000 * 1e6, 1)
+            return by_n
+        self.extra["barrier_only_ns_by_workgroups"] = by_workgroups(ccb.MODES[self.args.mode])
+        if self.args.mode != "tree-order":
+            self.extra["tree_order_ns_by_workgroups"] = by_workgroups(ccb.MODES["tree-order"])
         best = lat[self.args.mode]
         roof = {"bound": "atomic_round_trip", "achieved_ns_per_barrier": best,
                 "floor_ns": floor["fetch_add_ns"], "ratio": round(best / floor["fetch_add_ns"], 2),
@@ -692,6 +698,7 @@ def main():
         b.barrier_breakdown(floor, "striped-full")
         print(json.dumps({k: b.extra[k] for k in ("floor", "barrier_only_ns_at_256",
                                                    "barrier_only_ns_by_workgroups",
+                                                   "tree_order_ns_by_workgroups",
                                                    "latency_roofline", "barrier_breakdown")}),
               flush=True)
         return

@@ -92,7 +92,15 @@ inline bool valid_threads(int32_t threads)
 
 // Dynamic LDS that keeps at most wgsPerCu workgroups on one CU, and the check
 // that nGrid workgroups fit on the device at once (SYNCALL guide §6.3).
-inline bool valid_mode(int32_t mode) { return mode >= 0 && mode <= 3; }
+inline bool valid_mode(int32_t mode)
+{
+    return (mode >= 0 && mode <= 3) || mode == (CCB_BARRIER_TREE | CCB_VISIBILITY_ORDER) ||
+           mode == (CCB_BARRIER_TREE | CCB_VISIBILITY_FULL);
+}
+
+// Every valid mode, for the register query.
+constexpr int32_t kModes[] = {0, 1, 2, 3, CCB_BARRIER_TREE, CCB_BARRIER_TREE | CCB_VISIBILITY_FULL};
+constexpr int kModeSlots = 8;  // mode values 0..7 index the query table
 
 // Waves per SIMD that a persistent kernel's SGPR allocation allows.  The
 // occupancy API counts only the kernel's own SGPRs.  On MI355X each wave also
@@ -111,7 +119,7 @@ constexpr int kKernelIds = 5;
 
 struct RegQuery {
     bool done = false;
-    int8_t waves[kKernelIds][4] = {};
+    int8_t waves[kKernelIds][kModeSlots] = {};
 };
 std::mutex g_query_mu;
 RegQuery g_query[kMaxDevices];
@@ -124,7 +132,7 @@ ccbStatus sgpr_waves(int dev, ccb::KernelId id, int32_t mode, int* waves)
         int32_t* word = nullptr;
         if (ccb::register_query_word(&word) != hipSuccess) return hip_failed();
         for (int k = 0; k < kKernelIds; ++k)
-            for (int m = 0; m < 4; ++m) {
+            for (int32_t m : kModes) {
                 int32_t alloc = 0;
                 if (ccb::launch_register_query((ccb::KernelId)k, m, word, nullptr) != hipSuccess ||
                     hipMemcpy(&alloc, word, sizeof(alloc), hipMemcpyDeviceToHost) != hipSuccess)
@@ -190,12 +198,19 @@ inline uint32_t poll_bound(uint32_t maxPoll) { return maxPoll == 0 ? CCB_SOFT_MA
 // The counters are int32 (SYNCALL guide §4.1): a stripe stays valid while
 // its arrivals since the reset plus its participant count stay below 2^31.
 // Member m arrives on stripe m mod CCB_STRIPES, so the fullest stripe takes
-// ceil(N / 64) arrivals per barrier; the single-counter variant takes N.
+// ceil(N / 64) arrivals per barrier; the single-counter variant takes N; the
+// tree takes ceil(N / 8) on its fullest group counter and min(N, 8) on top.
 // Checked for a launch that starts from a zeroed workspace.
 inline bool counts_fit(int64_t barriers, int64_t members, int32_t mode)
 {
-    const int64_t perStripe =
-        (mode & CCB_BARRIER_FLAT) ? members : (members + CCB_STRIPES - 1) / CCB_STRIPES;
+    int64_t perStripe = (members + CCB_STRIPES - 1) / CCB_STRIPES;
+    if (mode & CCB_BARRIER_FLAT) perStripe = members;
+    if (mode & CCB_BARRIER_TREE) {
+        // the fullest group counter, and the top counter (one per group)
+        const int64_t group = (members + CCB_TREE_GROUPS - 1) / CCB_TREE_GROUPS;
+        const int64_t top = members < CCB_TREE_GROUPS ? members : CCB_TREE_GROUPS;
+        perStripe = group > top ? group : top;
+    }
     return barriers <= 0 || perStripe <= INT32_MAX / (barriers + 1);
 }
 

@@ -1273,23 +1273,31 @@ static hipError_t coop(const void* fn, int nGrid, int threads, size_t lds, hipSt
     return hipLaunchCooperativeKernel(fn, dim3(nGrid), dim3(threads), args, (unsigned)lds, s);
 }
 
-#define CCB_PICK_X(kernel, mode, x)                                                             \
+#define CCB_PICK_X(kernel, mode, x)                                                                  \
     ((mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_ORDER)                                     \
-         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_ORDER, x>)                \
+         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_ORDER, x>)                 \
      : (mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_FULL)                                    \
-         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_FULL, x>)                 \
+         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_FULL, x>)                  \
      : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_ORDER)                                      \
-         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_ORDER, x>)                          \
-         : reinterpret_cast<const void*>(&kernel<1, CCB_VIS_FULL, x>))
+         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_ORDER, x>)                           \
+     : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_FULL)                                       \
+         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_FULL, x>)                            \
+     : (mode) == (CCB_BARRIER_TREE | CCB_VISIBILITY_ORDER)                                      \
+         ? reinterpret_cast<const void*>(&kernel<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_ORDER, x>)   \
+         : reinterpret_cast<const void*>(&kernel<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_FULL, x>))
 
 #define CCB_PICK(kernel, mode)                                                                  \
     ((mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_ORDER)                                     \
-         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_ORDER>)                   \
+         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_ORDER>)                 \
      : (mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_FULL)                                    \
-         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_FULL>)                    \
+         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_FULL>)                  \
      : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_ORDER)                                      \
-         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_ORDER>)                             \
-         : reinterpret_cast<const void*>(&kernel<1, CCB_VIS_FULL>))
+         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_ORDER>)                           \
+     : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_FULL)                                       \
+         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_FULL>)                            \
+     : (mode) == (CCB_BARRIER_TREE | CCB_VISIBILITY_ORDER)                                      \
+         ? reinterpret_cast<const void*>(&kernel<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_ORDER>)   \
+         : reinterpret_cast<const void*>(&kernel<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_FULL>))
 
 const void* kernel_ptr(KernelId id, int32_t mode)
 {

@@ -80,6 +80,11 @@ enum {
  *                         arrives on stripe m mod CCB_STRIPES and one wave
  *                         polls every stripe with a single gather load
  *   CCB_BARRIER_FLAT      the pages' single counter ([SYNCALL] §5.2)
+ *   CCB_BARRIER_TREE      a two-level arrival tree: CCB_TREE_GROUPS group
+ *                         counters (member m arrives on group m mod 8) under
+ *                         one top counter that each group's completing
+ *                         arrival adds to; every member polls the top
+ *                         counter (see ccb_device.h)
  *   CCB_VISIBILITY_ORDER  arrival plus ordering of each thread's memory
  *                         operations, no cache maintenance ([SYNCALL] §6.1);
  *                         the workloads then share data through
@@ -90,9 +95,15 @@ enum {
 enum {
     CCB_BARRIER_STRIPED = 0,
     CCB_BARRIER_FLAT = 1,
+    CCB_BARRIER_TREE = 4,
     CCB_VISIBILITY_ORDER = 0,
     CCB_VISIBILITY_FULL = 2
 };
+
+/* Group counters of CCB_BARRIER_TREE: the MI355X's XCD count, so that with
+ * the usual round-robin dispatch of workgroups over the XCDs each group's
+ * members share one XCD. */
+#define CCB_TREE_GROUPS 8
 
 /* CntNotify mode codes, as enumerated in [CNTNOTIFY] §3.1 and §3.2. */
 enum {
@@ -142,7 +153,10 @@ CCB_API ccbStatus ccb_device_info(int32_t* numCUs, int32_t* ldsPerCU, int32_t* w
  * the last reset plus the participant count stays below 2^31; the launchers
  * below return CCB_ERR_INVALID_VALUE for a launch that would break this when
  * started from a zeroed workspace (striped: ceil(N / CCB_STRIPES) arrivals
- * per stripe and barrier; FLAT: N).
+ * per stripe and barrier; FLAT: N; TREE: ceil(N / CCB_TREE_GROUPS) per group
+ * counter and min(N, CCB_TREE_GROUPS) on the top counter).  A TREE barrier
+ * uses stripe lines 0 .. CCB_TREE_GROUPS - 1 for its group counters and the
+ * int32 at byte 64 of line CCB_STRIPES - 1 for its top counter.
  *
  * Every workload launcher below runs one persistent grid in which each
  * workgroup is resident for the whole launch ([SYNCALL] §6.3: the
@@ -162,7 +176,8 @@ CCB_API ccbStatus ccb_device_info(int32_t* numCUs, int32_t* ldsPerCU, int32_t* w
  * default CCB_SOFT_MAX_POLL); a member that exhausts it sets the error word
  * and leaves its round loop, and so does every member that then sees the
  * error word -- no launch traps or hangs.  `mode` picks the barrier variant
- * (CCB_BARRIER_* | CCB_VISIBILITY_*); any other value is INVALID_VALUE.  Read
+ * (CCB_BARRIER_* | CCB_VISIBILITY_*: 0, 1, 2, 3, 4 or 6); any other value is
+ * INVALID_VALUE.  Read
  * the outcome with ccb_syncall_status after the stream has run the launch.
  * ======================================================================== */
 

@@ -155,15 +155,95 @@ struct ccb_no_hook {
  * the member stores CCB_ERR_INVALID_VALUE in the error word and returns it
  * without polling, and the others leave when they next read the error
  * word.  Re-zero the workspace before a stripe gets near 2^31 arrivals. */
+/* Counter layouts, the template argument K of the functions below:
+ *   K = 1 .. 64      K stripes (K = 1: the pages' single counter);
+ *   K = ccb_tree(G)  a two-level arrival tree of G group counters (G = 1 .. 32)
+ *                    under one top counter: member m arrives on group
+ *                    m mod G with the pages' epoch rule for the group's
+ *                    n_g = ceil((N - g) / G) members; the arrival whose reply
+ *                    completes its group's round adds one to the top counter,
+ *                    whose participants are the min(N, G) groups, and every
+ *                    member polls the top counter for epoch * min(N, G).
+ *                    Group g sits at byte 0 of line g, the top counter at
+ *                    byte 64 of line CCB_STRIPES - 1 (so the sum of the lines'
+ *                    first words is still the number of member arrivals).
+ *                    The same shape as a core -> cluster barrier bus, with
+ *                    counters in memory instead of wires. */
+__host__ __device__ constexpr int ccb_tree(int groups) { return -groups; }
+
+#define CCB_TREE_TOP_WORD ((CCB_STRIPES - 1) * CCB_LINE_WORDS + CCB_LINE_WORDS / 2)
+
 template <int K, ccbVisibility kVis>
 __device__ __forceinline__ int32_t ccb_arrive(int32_t* ctr, int32_t member)
 {
-    static_assert(K >= 1 && K <= 64, "stripes are polled by one wave");
+    static_assert((K >= 1 && K <= 64) || (K <= -1 && K >= -32),
+                  "stripes are polled by one wave; tree groups sit below the top line");
+    constexpr int kLines = K > 0 ? K : -K;
     // release: the workgroup's earlier global stores become visible at agent
     // scope before the arrival can be observed
     if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    return __hip_atomic_fetch_add(ctr + (member % K) * CCB_LINE_WORDS, 1, __ATOMIC_RELAXED,
+    return __hip_atomic_fetch_add(ctr + (member % kLines) * CCB_LINE_WORDS, 1, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
+}
+
+/* The poll of a two-level tree (K = ccb_tree(G)); see ccb_await. */
+template <int G, ccbVisibility kVis, class Hook>
+__device__ __forceinline__ int32_t ccb_await_tree(const int32_t* ctr, int32_t n, int32_t member,
+                                                  int32_t before, uint32_t maxPoll, int32_t* err,
+                                                  Hook hook)
+{
+    const int lane = (int)__lane_id();
+    int32_t* const top = const_cast<int32_t*>(ctr) + CCB_TREE_TOP_WORD;
+    const int32_t b = __shfl(before, 0, 64);
+    __builtin_amdgcn_sched_barrier(0x44F);
+    hook.reply();
+    const int32_t g = member % G;
+    const int32_t ng = (n - g + G - 1) / G;  // members of this group
+    const int32_t gu = n < G ? n : G;        // groups in use: the top counter's members
+    const int32_t q = b / ng;
+    // group 0 is the largest; both its count and the top's must stay in int32
+    if (b < 0 || q >= INT32_MAX / ((n + G - 1) / G) || q >= INT32_MAX / gu) {
+        if (lane == 0)
+            __hip_atomic_store(err, (int32_t)CCB_ERR_INVALID_VALUE, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        hook.released();
+        return CCB_ERR_INVALID_VALUE;
+    }
+    const int32_t epoch = q + 1;
+    if (b + 1 == epoch * ng) {
+        // this arrival completed its group's round: the group arrives on top.
+        // With full visibility the group's released stores must reach the
+        // pollers of the top counter through this member: acquire from the
+        // group counter, release to the top.
+        if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+        if (lane == 0)
+            __hip_atomic_fetch_add(top, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const int32_t need = epoch * gu;
+    int32_t rc = CCB_OK;
+    uint32_t polls = 0;
+    for (;;) {
+        const int32_t v = __hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v >= need) break;
+        if (++polls >= maxPoll) {
+            if (lane == 0)
+                __hip_atomic_store(err, (int32_t)CCB_ERR_DEADLOCK, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            rc = CCB_ERR_DEADLOCK;
+            break;
+        }
+        if ((polls % CCB_ERR_CHECK_EVERY) == 0) {
+            const int32_t e = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (e != CCB_OK) {
+                rc = e;
+                break;
+            }
+        }
+        if (CCB_POLL_SLEEP > 0) __builtin_amdgcn_s_sleep(CCB_POLL_SLEEP);
+    }
+    hook.released();
+    if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return rc;
 }
 
 template <int K, ccbVisibility kVis, class Hook = ccb_no_hook>
@@ -171,74 +251,78 @@ __device__ __forceinline__ int32_t ccb_await(const int32_t* ctr, int32_t n, int3
                                              int32_t before, uint32_t maxPoll, int32_t* err,
                                              Hook hook = Hook())
 {
-    const int lane = (int)__lane_id();
-    const int32_t ks = n < K ? n : K;  // stripes in use
-    const int32_t s = member % K;
-    int32_t* mine = const_cast<int32_t*>(ctr) + (lane < ks ? lane : 0) * CCB_LINE_WORDS;
-    // The first poll goes out only after the arrival's reply is back: a poll
-    // load issued while the wave's own arrival is still in flight makes the
-    // barrier about twice as slow on gfx950, whichever stripe it reads
-    // (measured at 256 workgroups: 1.75-1.85 us against 0.94 us).  The shuffle
-    // waits for the reply; the scheduling barrier keeps vector memory reads
-    // and the shuffle on their sides of it (mask 0x44F: ALU work and vector
-    // memory writes may still move across).
-    // The reply itself says whether this arrival completed its own stripe,
-    // and counters only grow, so any value read that meets the target proves
-    // that stripe complete.
-    const int32_t b = __shfl(before, 0, 64);
-    __builtin_amdgcn_sched_barrier(0x44F);
-    hook.reply();
-    const int32_t v0 = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // The release count of stripe l is epoch * n_l; stripe 0 has the most
-    // members, so the round fits in int32 exactly when
-    // (before / n_s + 1) * n_0 <= INT32_MAX, i.e. before / n_s < INT32_MAX / n_0.
-    const int32_t q = b / ((n - s + K - 1) / K);
-    const int32_t epoch = q + 1;
-    if (b < 0 || q >= INT32_MAX / ((n + K - 1) / K)) {
-        if (lane == 0)
-            __hip_atomic_store(err, (int32_t)CCB_ERR_INVALID_VALUE, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        hook.released();
-        return CCB_ERR_INVALID_VALUE;
-    }
-    // stripe `lane` is complete for this round at epoch * n_lane arrivals;
-    // lanes past the stripes in use re-read stripe 0 and always agree
-    const int32_t need = lane < ks ? epoch * ((n - lane + K - 1) / K) : INT32_MIN;
-    int32_t rc = CCB_OK;
-    uint32_t polls = 0;
-    // A stripe seen complete stays complete, so later polls read only the
-    // unfinished ones: lanes that are done re-read the first unfinished
-    // stripe, which adds no line to the gather.
-    int32_t* const base = const_cast<int32_t*>(ctr);
-    bool done = v0 >= need || (lane == s && b + 1 >= need);
-    if (!__all(done)) {
-        for (;;) {
-            const uint64_t pending = __ballot(!done);
-            int32_t* const addr = done ? base + __builtin_ctzll(pending) * CCB_LINE_WORDS : mine;
-            const int32_t v = __hip_atomic_load(addr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            done = done || v >= need;
-            if (__all(done)) break;
-            if (++polls >= maxPoll) {
-                if (lane == 0)
-                    __hip_atomic_store(err, (int32_t)CCB_ERR_DEADLOCK, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                rc = CCB_ERR_DEADLOCK;
-                break;
-            }
-            if ((polls % CCB_ERR_CHECK_EVERY) == 0) {
-                const int32_t e = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (e != CCB_OK) {
-                    rc = e;
+    if constexpr (K < 0) {
+        return ccb_await_tree<-K, kVis>(ctr, n, member, before, maxPoll, err, hook);
+    } else {
+        const int lane = (int)__lane_id();
+        const int32_t ks = n < K ? n : K;  // stripes in use
+        const int32_t s = member % K;
+        int32_t* mine = const_cast<int32_t*>(ctr) + (lane < ks ? lane : 0) * CCB_LINE_WORDS;
+        // The first poll goes out only after the arrival's reply is back: a poll
+        // load issued while the wave's own arrival is still in flight makes the
+        // barrier about twice as slow on gfx950, whichever stripe it reads
+        // (measured at 256 workgroups: 1.75-1.85 us against 0.94 us).  The shuffle
+        // waits for the reply; the scheduling barrier keeps vector memory reads
+        // and the shuffle on their sides of it (mask 0x44F: ALU work and vector
+        // memory writes may still move across).
+        // The reply itself says whether this arrival completed its own stripe,
+        // and counters only grow, so any value read that meets the target proves
+        // that stripe complete.
+        const int32_t b = __shfl(before, 0, 64);
+        __builtin_amdgcn_sched_barrier(0x44F);
+        hook.reply();
+        const int32_t v0 = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // The release count of stripe l is epoch * n_l; stripe 0 has the most
+        // members, so the round fits in int32 exactly when
+        // (before / n_s + 1) * n_0 <= INT32_MAX, i.e. before / n_s < INT32_MAX / n_0.
+        const int32_t q = b / ((n - s + K - 1) / K);
+        const int32_t epoch = q + 1;
+        if (b < 0 || q >= INT32_MAX / ((n + K - 1) / K)) {
+            if (lane == 0)
+                __hip_atomic_store(err, (int32_t)CCB_ERR_INVALID_VALUE, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            hook.released();
+            return CCB_ERR_INVALID_VALUE;
+        }
+        // stripe `lane` is complete for this round at epoch * n_lane arrivals;
+        // lanes past the stripes in use re-read stripe 0 and always agree
+        const int32_t need = lane < ks ? epoch * ((n - lane + K - 1) / K) : INT32_MIN;
+        int32_t rc = CCB_OK;
+        uint32_t polls = 0;
+        // A stripe seen complete stays complete, so later polls read only the
+        // unfinished ones: lanes that are done re-read the first unfinished
+        // stripe, which adds no line to the gather.
+        int32_t* const base = const_cast<int32_t*>(ctr);
+        bool done = v0 >= need || (lane == s && b + 1 >= need);
+        if (!__all(done)) {
+            for (;;) {
+                const uint64_t pending = __ballot(!done);
+                int32_t* const addr = done ? base + __builtin_ctzll(pending) * CCB_LINE_WORDS : mine;
+                const int32_t v = __hip_atomic_load(addr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                done = done || v >= need;
+                if (__all(done)) break;
+                if (++polls >= maxPoll) {
+                    if (lane == 0)
+                        __hip_atomic_store(err, (int32_t)CCB_ERR_DEADLOCK, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    rc = CCB_ERR_DEADLOCK;
                     break;
                 }
+                if ((polls % CCB_ERR_CHECK_EVERY) == 0) {
+                    const int32_t e = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (e != CCB_OK) {
+                        rc = e;
+                        break;
+                    }
+                }
+                if (CCB_POLL_SLEEP > 0) __builtin_amdgcn_s_sleep(CCB_POLL_SLEEP);
             }
-            if (CCB_POLL_SLEEP > 0) __builtin_amdgcn_s_sleep(CCB_POLL_SLEEP);
         }
+        hook.released();
+        // acquire: loads after the barrier see every member's released stores
+        if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        return rc;
     }
-    hook.released();
-    // acquire: loads after the barrier see every member's released stores
-    if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    return rc;
 }
 
 /* The barrier proper (both phases with the workgroup barriers around them).

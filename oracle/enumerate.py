@@ -75,51 +75,23 @@ class Result:
 
 
 def _programs(rounds: Sequence[RoundSpec], n_participants: int,
-              skip: Sequence[Tuple[int, int]] = (),
-              early_write: bool = False, write_lead: int = 0,
-              read_lag: int = 0) -> List[List[Tuple[int, int]]]:
-    """Per participant: the flat list of (step kind, round) it executes.
-
-    In the plain schedule every member round is WRITE, ARRIVE, POLL, READ.
-    A pipelined schedule (write_lead = a >= 1) counts in the participant's
-    own member rounds m_0, m_1, ...: the witnesses of m_0 .. m_{a-1} are
-    written before the first barrier, the witness of m_{i+a} right after
-    passing the barrier of m_i, and the read of m_i may still be in flight
-    until the participant arrives at m_{i+b} (b = read_lag >= 1).  The READ
-    step sits at that latest point: a slot that still holds round m_i there
-    held it since the barrier of m_i (a slot is only ever overwritten by a
-    later round), so this placement covers every earlier one.  early_write
-    is a = b = 1.  A skipped barrier drops that round's ARRIVE and POLL."""
-    if early_write:
-        write_lead, read_lag = max(write_lead, 1), max(read_lag, 1)
+              skip: Sequence[Tuple[int, int]] = ()) -> List[List[Tuple[int, int]]]:
+    """Per participant: the flat list of (step kind, round) it executes --
+    WRITE, ARRIVE, POLL, READ for every round it belongs to.  A skipped
+    barrier drops that round's ARRIVE and POLL (the participant still writes
+    and reads)."""
     skipped = set(skip)
-    member_rounds: List[List[int]] = [[] for _ in range(n_participants)]
-    for r, spec in enumerate(rounds):
-        for p in spec.members:
-            member_rounds[p].append(r)
     progs: List[List[Tuple[int, int]]] = []
     for p in range(n_participants):
-        mine = member_rounds[p]
         steps: List[Tuple[int, int]] = []
-        if write_lead <= 0:
-            for r in mine:
-                steps.append((WRITE, r))
-                if (p, r) not in skipped:
-                    steps.append((ARRIVE, r))
-                    steps.append((POLL, r))
-                steps.append((READ, r))
-        else:
-            a, b = write_lead, max(read_lag, 1)
-            steps.extend((WRITE, mine[j]) for j in range(min(a, len(mine))))
-            for i, r in enumerate(mine):
-                if i - b >= 0:
-                    steps.append((READ, mine[i - b]))
-                if (p, r) not in skipped:
-                    steps.append((ARRIVE, r))
-                    steps.append((POLL, r))
-                if i + a < len(mine):
-                    steps.append((WRITE, mine[i + a]))
-            steps.extend((READ, mine[j]) for j in range(max(0, len(mine) - b), len(mine)))
+        for r, spec in enumerate(rounds):
+            if p not in spec.members:
+                continue
+            steps.append((WRITE, r))
+            if (p, r) not in skipped:
+                steps.append((ARRIVE, r))
+                steps.append((POLL, r))
+            steps.append((READ, r))
         progs.append(steps)
     return progs
 
@@ -128,8 +100,6 @@ def enumerate_schedules(rounds: Sequence[RoundSpec], n_participants: int, *,
                         ring_depth: int = 4, poll_cmp: str = "ge",
                         counter_init: Optional[Sequence[int]] = None,
                         skip: Sequence[Tuple[int, int]] = (),
-                        early_write: bool = False, stripes: int = 1,
-                        write_lead: int = 0, read_lag: int = 0,
                         max_states: int = 5_000_000) -> Result:
     """Explore every interleaving of the participants' steps.
 
@@ -139,30 +109,15 @@ def enumerate_schedules(rounds: Sequence[RoundSpec], n_participants: int, *,
     counter_init  starting value of each counter (default all zero)
     skip          (participant, round) pairs whose barrier is left out
                   (the participant still writes and reads)
-    early_write   the pipelined step order with a = b = 1 (see _programs)
-    write_lead    a, read_lag b: a pipelined step order (see _programs)
-    stripes       K: each counter is split into K stripes; the member with
-                  index m in its round's member list arrives on stripe m mod K,
-                  whose member count is n_s = ceil((N - s) / K), derives its
-                  round e = before // n_s + 1 from that stripe, and is released
-                  once every stripe l < min(N, K) holds at least e * n_l.  K = 1
-                  is the single counter of the SYNCALL guide.
     """
     n_counters = 1 + max(spec.counter for spec in rounds)
-    K = stripes
-    ctr0 = (tuple(c for c in counter_init for _ in range(1)) if counter_init is not None
-            else (0,) * n_counters)
-    if counter_init is not None:
-        # an initial value applies to stripe 0 of each counter
-        ctr0 = tuple(v if s == 0 else 0 for v in counter_init for s in range(K))
-    else:
-        ctr0 = (0,) * (n_counters * K)
-    progs = _programs(rounds, n_participants, skip, early_write, write_lead, read_lag)
+    ctr0 = tuple(counter_init) if counter_init is not None else (0,) * n_counters
+    progs = _programs(rounds, n_participants, skip)
     res = Result()
 
     # state = (pcs, counters, targets, slots)
     #   pcs[p]     = index of participant p's next step
-    #   targets[p] = the round (epoch) derived at its last ARRIVE (or -1)
+    #   targets[p] = the target derived at its last ARRIVE (or -1)
     #   slots      = tuple over (ring row, participant) of the last round written
     start = ((0,) * n_participants, ctr0, (-1,) * n_participants,
              (-1,) * (ring_depth * n_participants))
@@ -194,21 +149,12 @@ def enumerate_schedules(rounds: Sequence[RoundSpec], n_participants: int, *,
                 successors.append((nxt, ctrs, tgts, tuple(new_slots)))
             elif kind == ARRIVE:
                 n = spec.n
-                st = spec.members.index(p) % K
-                ns = (n - st + K - 1) // K
-                before = ctrs[g * K + st]
-                epoch = before // ns + 1       # target = epoch * ns, the pages' rule per stripe
-                successors.append((nxt, _set(ctrs, g * K + st, before + 1), _set(tgts, p, epoch),
-                                   slots))
+                before = ctrs[g]
+                target = (before // n + 1) * n     # the pages' rule
+                successors.append((nxt, _set(ctrs, g, before + 1), _set(tgts, p, target), slots))
             elif kind == POLL:
-                n = spec.n
-                epoch = tgts[p]
-                ok = True
-                for lane in range(min(n, K)):
-                    nl = (n - lane + K - 1) // K
-                    c = ctrs[g * K + lane]
-                    ok = ok and (c >= epoch * nl if poll_cmp == "ge" else c == epoch * nl)
-                if ok:
+                c = ctrs[g]
+                if (c >= tgts[p]) if poll_cmp == "ge" else (c == tgts[p]):
                     successors.append((nxt, ctrs, tgts, slots))
             else:  # READ
                 for q in spec.members:
@@ -217,7 +163,7 @@ def enumerate_schedules(rounds: Sequence[RoundSpec], n_participants: int, *,
                         res.violations.append((r, p, q, got))
                 successors.append((nxt, ctrs, tgts, slots))
         if all_done:
-            res.final_counters.add(tuple(sum(ctrs[g * K:(g + 1) * K]) for g in range(n_counters)))
+            res.final_counters.add(tuple(ctrs))
             res.complete_schedules_seen = True
             continue
         if not successors:

@@ -94,12 +94,14 @@ def test_constants_match_pages(ccb):
     enums = {**_header_enum("CCB_BARRIER_"), **_header_enum("CCB_VISIBILITY_"),
              **_header_enum("CCB_CNT_RECORD_"), **_header_enum("CCB_CNT_WAIT_")}
     for name in ("CCB_STRIPES", "CCB_SLOT_ROWS", "CCB_SLOT_WORDS", "CCB_LINE_BYTES",
-                 "CCB_CNT_NOTIFY_POOL", "CCB_SOFT_MAX_POLL"):
+                 "CCB_CNT_NOTIFY_POOL", "CCB_SOFT_MAX_POLL", "CCB_TREE_GROUPS",
+                 "CCB_BREAKDOWN_MAX_ROUNDS"):
         assert defines.get(name) == getattr(ccb, name), name
-    assert len(enums) == 13
+    assert len(enums) == 14
     for name, val in enums.items():
         assert getattr(ccb, name) == val, name
-    assert ccb.MODES == {"striped-order": 0, "flat-order": 1, "striped-full": 2, "flat-full": 3}
+    assert ccb.MODES == {"striped-order": 0, "flat-order": 1, "striped-full": 2, "flat-full": 3,
+                         "tree-order": 4, "tree-full": 6}
     assert ccb.ccb_syncall_workspace_bytes(1) == (ccb.CCB_STRIPES + 1) * 128
     assert ccb.ccb_syncall_workspace_bytes(3) == (3 * ccb.CCB_STRIPES + 1) * 128
     # 2^26 elements in chunks of 1024, 1024 workgroups: 64 chunks each

@@ -9,7 +9,8 @@ GFX942 family, which gfx950 follows:
   - a relaxed atomic load or store at agent scope carries `sc1`.
 
 What is checked, for every persistent kernel (barrier-only, witness rounds,
-grouped rounds, stencil; 64 stripes and one counter):
+grouped rounds, stencil; 64 stripes, one counter, and the two-level tree of
+8 group counters):
   - full visibility: the arrival (the returning fetch-add) comes right after
     a release sequence with no memory access in between, and an acquire
     follows the poll;
@@ -19,6 +20,10 @@ grouped rounds, stencil; 64 stripes and one counter):
     slots, halo words) is stored with agent-scope stores;
   - the first poll load goes out only after a wait for the arrival's reply
     (a poll issued behind the wave's own arrival doubles the barrier's cost);
+  - tree, full visibility: the group completer's arrival on the top counter
+    (a non-returning atomic) comes right after an acquire-release sequence
+    (`buffer_wbl2 sc1` then `buffer_inv sc1`), so the group's released
+    stores reach the top counter's pollers through it;
 and for every kernel in the file: no write through the scalar data cache and
 no packed-FP32 arithmetic.
 """
@@ -65,12 +70,15 @@ def _functions(asm_text):
 
 
 def _persistent(asm_text, vis_codes):
-    """{(kind, stripes, visibility): instructions} of the persistent kernels."""
+    """{(kind, counter layout K, visibility): instructions} of the persistent
+    kernels; K < 0 is the tree of -K groups (mangled as Lin8E)."""
     found = {}
     for name, ins in _functions(asm_text).items():
-        m = re.match(r"_Z\d+ccb_k_(\w+?)ILi(\d+)EL\d+ccbVisibility(\d+)E", name)
+        m = re.match(r"_Z\d+ccb_k_(\w+?)ILi(n?\d+)EL\d+ccbVisibility(\d+)E", name)
         if m and m.group(1) in KINDS:
-            found[(m.group(1), int(m.group(2)), vis_codes[int(m.group(3))])] = ins
+            k = m.group(2)
+            k = -int(k[1:]) if k.startswith("n") else int(k)
+            found[(m.group(1), k, vis_codes[int(m.group(3))])] = ins
     return found
 
 
@@ -86,31 +94,122 @@ def _arrivals(ins):
     return [i for i, l in enumerate(ins) if _op(l) == "global_atomic_add" and " sc0" in l]
 
 
+def _top_arrivals(ins):
+    """The tree's arrivals on the top counter: fetch-adds whose reply is unused."""
+    return [i for i, l in enumerate(ins) if _op(l) == "global_atomic_add" and " sc0" not in l]
+
+
 def test_every_persistent_kernel_present(asm, vis_codes):
     found = _persistent(asm, vis_codes)
-    want = {(k, s, v) for k in KINDS for s in (1, 64) for v in ("full", "order")}
+    want = {(k, s, v) for k in KINDS for s in (1, 64, -8) for v in ("full", "order")}
     assert set(found) == want
     for key, ins in found.items():
         assert _arrivals(ins), f"{key}: no returning fetch-add (the arrival)"
 
 
-def test_full_visibility_release_before_arrival_acquire_after_poll(asm, vis_codes):
-    for key, ins in _persistent(asm, vis_codes).items():
+# --- the checks: each returns the problems it finds (empty = passes) ------------
+
+def _check_release(found):
+    bad = []
+    for key, ins in found.items():
         if key[2] != "full":
             continue
-        arr = _arrivals(ins)
-        for a in arr:
+        for a in _arrivals(ins):
             waited = False
             j = a - 1
             while j >= 0 and not _is_mem(ins[j]):
                 if _op(ins[j]) == "s_waitcnt" and "vmcnt(0)" in ins[j]:
                     waited = True
                 j -= 1
-            assert j >= 0 and ins[j] == "buffer_wbl2 sc1", \
-                f"{key}: the access before the arrival is {ins[j] if j >= 0 else None!r}"
-            assert waited, f"{key}: no s_waitcnt vmcnt(0) between the write-back and the arrival"
+            if not (j >= 0 and ins[j] == "buffer_wbl2 sc1"):
+                bad.append(f"{key}: the access before the arrival is {ins[j] if j >= 0 else None!r}")
+            elif not waited:
+                bad.append(f"{key}: no s_waitcnt vmcnt(0) between the write-back and the arrival")
+    return bad
+
+
+def _check_acquire(found):
+    """Full visibility: an acquire (buffer_inv sc1) after the last agent-scope
+    load, i.e. after the poll loop."""
+    bad = []
+    for key, ins in found.items():
+        if key[2] != "full":
+            continue
+        polls = [i for i, l in enumerate(ins) if _op(l).startswith("global_load") and " sc1" in l]
         inv = [i for i, l in enumerate(ins) if l == "buffer_inv sc1"]
-        assert inv and max(inv) > min(arr), f"{key}: no agent-scope acquire after the poll"
+        if not polls or not inv or max(inv) < max(polls):
+            bad.append(f"{key}: no agent-scope acquire after the poll")
+    return bad
+
+
+def _check_tree_top(found):
+    bad = []
+    for key, ins in found.items():
+        if key[1] >= 0:
+            continue
+        tops = _top_arrivals(ins)
+        if not tops:
+            bad.append(f"{key}: no arrival on the top counter")
+        if key[2] != "full":
+            continue
+        for t in tops:
+            j = t - 1
+            while j >= 0 and not _is_mem(ins[j]):
+                j -= 1
+            if not (j >= 1 and ins[j] == "buffer_inv sc1"):
+                bad.append(f"{key}: the access before the top arrival is "
+                           f"{ins[j] if j >= 0 else None!r}")
+                continue
+            j -= 1
+            while j >= 0 and not _is_mem(ins[j]):
+                j -= 1
+            if not (j >= 0 and ins[j] == "buffer_wbl2 sc1"):
+                bad.append(f"{key}: no write-back ahead of the top arrival's acquire")
+    return bad
+
+
+def _check_first_poll(found):
+    bad = []
+    for key, ins in found.items():
+        if key[0] != "barrier_only":
+            continue  # the rounds kernels overlap their own data loads with the arrival
+        for a in _arrivals(ins):
+            j = a + 1
+            waited = False
+            while j < len(ins) and not _is_mem(ins[j]):
+                if _op(ins[j]) == "s_waitcnt" and "vmcnt(0)" in ins[j]:
+                    waited = True
+                j += 1
+            if key[1] < 0:
+                # full visibility: the completer's acquire-release comes
+                # first (its own check)
+                while j < len(ins) and (_op(ins[j]) in ("buffer_wbl2", "buffer_inv")
+                                        or not _is_mem(ins[j])):
+                    j += 1
+            if key[1] < 0 and j < len(ins) and j in _top_arrivals(ins):
+                # a tree: a group's completer first arrives on the top counter
+                # (whose reply nothing waits for), then polls
+                if not waited:
+                    bad.append(f"{key}: the top arrival does not wait for the group's reply")
+                j += 1
+                while j < len(ins) and not _is_mem(ins[j]):
+                    j += 1
+            if not (j < len(ins) and _op(ins[j]).startswith("global_load") and " sc1" in ins[j]):
+                bad.append(f"{key}: the access after the arrival is "
+                           f"{ins[j] if j < len(ins) else None!r}")
+            elif not waited:
+                bad.append(f"{key}: the first poll does not wait for the arrival's reply")
+    return bad
+
+
+def test_full_visibility_release_before_arrival_acquire_after_poll(asm, vis_codes):
+    found = _persistent(asm, vis_codes)
+    assert _check_release(found) == []
+    assert _check_acquire(found) == []
+
+
+def test_tree_full_top_arrival_after_acquire_release(asm, vis_codes):
+    assert _check_tree_top(_persistent(asm, vis_codes)) == []
 
 
 def test_order_visibility_has_no_cache_maintenance(asm, vis_codes):
@@ -136,19 +235,63 @@ def test_order_visibility_shares_data_through_agent_scope_accesses(asm, vis_code
 
 
 def test_first_poll_waits_for_the_arrivals_reply(asm, vis_codes):
-    for key, ins in _persistent(asm, vis_codes).items():
-        if key[0] != "barrier_only":
-            continue  # the rounds kernels overlap their own data loads with the arrival
-        for a in _arrivals(ins):
-            j = a + 1
-            waited = False
-            while j < len(ins) and not _is_mem(ins[j]):
-                if _op(ins[j]) == "s_waitcnt" and "vmcnt(0)" in ins[j]:
-                    waited = True
-                j += 1
-            assert j < len(ins) and _op(ins[j]).startswith("global_load") and " sc1" in ins[j], \
-                f"{key}: the access after the arrival is {ins[j] if j < len(ins) else None!r}"
-            assert waited, f"{key}: the first poll does not wait for the arrival's reply"
+    assert _check_first_poll(_persistent(asm, vis_codes)) == []
+
+
+# --- negative controls: a copy of the device header with one fence taken out
+# (or the first poll moved ahead of the reply), compiled the same way; the
+# check that guards that step must find it.
+
+NEGATIVE = {
+    "no_release": (
+        [('if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");', "")],
+        _check_release),
+    "no_acquire": (
+        [('if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");', "")],
+        _check_acquire),
+    "no_tree_acquire_release": (
+        [('if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");', "")],
+        _check_tree_top),
+    "poll_before_reply": (
+        [("const int32_t b = __shfl(before, 0, 64);\n"
+          "        __builtin_amdgcn_sched_barrier(0x44F);\n"
+          "        hook.reply();\n"
+          "        const int32_t v0 = __hip_atomic_load(mine, __ATOMIC_RELAXED, "
+          "__HIP_MEMORY_SCOPE_AGENT);",
+          "const int32_t v0 = __hip_atomic_load(mine, __ATOMIC_RELAXED, "
+          "__HIP_MEMORY_SCOPE_AGENT);\n"
+          "        __builtin_amdgcn_sched_barrier(0);\n"
+          "        const int32_t b = __shfl(before, 0, 64);\n"
+          "        hook.reply();")],
+        _check_first_poll),
+}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(NEGATIVE))
+def test_negative_control_is_caught(name, tmp_path, vis_codes):
+    import shutil
+    import subprocess
+    from cross_core_barrier_amd import build
+    inc = tmp_path / "include"
+    shutil.copytree(os.path.join(ROOT, "include"), inc)
+    hdr = inc / "ccb_device.h"
+    text = hdr.read_text()
+    edits, check = NEGATIVE[name]
+    for old, new in edits:
+        assert text.count(old) >= 1, f"{name}: the header no longer has {old!r}"
+        text = text.replace(old, new)
+    hdr.write_text(text)
+    flags = list(build.CODE_FLAGS)
+    flags[flags.index(os.path.join(ROOT, "include"))] = str(inc)
+    out = str(tmp_path / "k.s")
+    cmd = ["hipcc", *flags, "-S", "--cuda-device-only", "-o", out,
+           os.path.join(build.CSRC, "ccb_kernels.hip")]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    with open(out) as f:
+        found = _persistent(f.read(), vis_codes)
+    assert check(found) != [], f"{name}: {check.__name__} does not notice"
 
 
 def test_no_scalar_cache_writes_and_no_packed_fp32(asm):

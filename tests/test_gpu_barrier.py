@@ -36,8 +36,8 @@ def _u32(t):
     return t.cpu().numpy().view(np.uint32)
 
 
-MODES = [0, 1, 2, 3]  # striped/flat x ordering-only/full fences
-MODE_IDS = ["striped-order", "flat-order", "striped-full", "flat-full"]
+MODES = [0, 1, 2, 3, 4, 6]  # striped / flat / tree x ordering-only / full fences
+MODE_IDS = ["striped-order", "flat-order", "striped-full", "flat-full", "tree-order", "tree-full"]
 _oracle_cache = {}
 
 
@@ -250,19 +250,31 @@ def test_counter_past_int32_is_invalid_value(ccb, wl, mode):
     round simulator on the single counter."""
     n = 4
     flat = (mode & ccb.CCB_BARRIER_FLAT) != 0
+    tree = (mode & ccb.CCB_BARRIER_TREE) != 0
     limit = 2**31 - 1
-    ws = wl.workspace(1)
-    if flat:
-        top = limit // n * n            # last count a round of n can reach
-        ws[0] = top - n                  # round 1 ends at top, round 2 cannot
+    top = limit // n * n                # last count a round of n can reach
+
+    def preset(ws):
+        if flat:
+            ws[0] = top - n              # round 1 ends at top, round 2 cannot
+        elif tree:
+            # 4 groups of one member: the top counter (4 members) fills first
+            for g in range(n):
+                ws[g * 32] = top // n - 1
+            ws[ccb.CCB_TREE_TOP_WORD] = top - n
+        else:
+            for s in range(n):           # n <= 64 stripes of one member each
+                ws[s * 32] = limit - 1
+
+    if flat or tree:
         want_rc1, _ = oracle.epoch_target_checked(top - n, n)
         want_rc2, _ = oracle.epoch_target_checked(top, n)
     else:
-        for s in range(n):              # n <= 64 stripes of one member each
-            ws[s * 32] = limit - 1
         want_rc1, _ = oracle.epoch_target_checked(limit - 1, 1)
         want_rc2, _ = oracle.epoch_target_checked(limit, 1)
     assert (want_rc1, want_rc2) == (oracle.OK, oracle.INVALID_VALUE)
+    ws = wl.workspace(1)
+    preset(ws)
     _say(f"barrier_only past int32: N={n}, 2 rounds, mode={mode}")
     wg = torch.zeros(n, dtype=torch.int32, device="cuda")
     assert ccb.ccb_run_barrier_only(ws, None, wg, 2, n, 64, 0, 0, 2000, mode, None) == 0
@@ -271,15 +283,16 @@ def test_counter_past_int32_is_invalid_value(ccb, wl, mode):
     assert (wg.cpu().numpy() == 3).all()
     # one round from the same preset is fine
     ws = wl.workspace(1)
-    if flat:
-        ws[0] = top - n
-    else:
-        for s in range(n):
-            ws[s * 32] = limit - 1
+    preset(ws)
     assert ccb.ccb_run_barrier_only(ws, None, wg, 1, n, 64, 0, 0, 2000, mode, None) == 0
     st, ctrs = ccb.ccb_syncall_status(ws, 1, None)
     assert st == ccb.CCB_OK
-    assert ctrs == [top] if flat else ctrs == [n * limit]
+    if flat:
+        assert ctrs == [top]
+    elif tree:
+        assert ctrs == [top] and int(ws[ccb.CCB_TREE_TOP_WORD]) == top
+    else:
+        assert ctrs == [n * limit]
 
 
 @pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
@@ -389,7 +402,7 @@ def test_concurrent_launches_from_host_threads(ccb, wl):
 
     def worker(t):
         for i in range(reps):
-            mode = MODES[(t + i) % 4]
+            mode = MODES[(t + i) % len(MODES)]
             st = ccb.ccb_syncall_workspace_reset(wss[t], 1, streams[t])
             if st == 0:
                 st = ccb.ccb_run_barrier_only(wss[t], None, None, rounds, n, 64, 0, 1 + t, 0,
@@ -422,6 +435,8 @@ def test_invalid_arguments(ccb, wl):
     assert ccb.ccb_run_barrier_only(ws, None, None, 1, 8, 65) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_run_barrier_only(ws, None, None, 1, 8, 64, 9) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_run_barrier_only(ws, None, None, 1, 8, 64, -1) == ccb.CCB_ERR_INVALID_VALUE
-    assert ccb.ccb_run_barrier_only(ws, None, None, 1, 8, 64, mode=4) == ccb.CCB_ERR_INVALID_VALUE
+    for bad in (5, 7, 8, -1):
+        assert ccb.ccb_run_barrier_only(ws, None, None, 1, 8, 64, mode=bad) == \
+            ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_run_barrier_only(ws.data_ptr() + 4, None, None, 1, 8, 64) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_run_grouped_rounds(ws, ws, ws, None, 0, 1, 7, 64) == ccb.CCB_ERR_INVALID_VALUE

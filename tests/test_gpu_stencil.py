@@ -22,8 +22,8 @@ def wl():
     return workloads
 
 
-MODES = [0, 1, 2, 3]
-MODE_IDS = ["striped-order", "flat-order", "striped-full", "flat-full"]
+MODES = [0, 1, 2, 3, 4, 6]  # striped / flat / tree x ordering-only / full fences
+MODE_IDS = ["striped-order", "flat-order", "striped-full", "flat-full", "tree-order", "tree-full"]
 
 
 @pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)

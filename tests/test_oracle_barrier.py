@@ -299,94 +299,6 @@ def test_grouped_full_counters_formula():
             int((kinds == 2).sum()) * 512) == (8_533_504, 8_533_248, 17_066_496)
 
 
-# --- striped counters and the pipelined (early-write) schedule ----------------
-# The GPU kernels split each counter into stripes and, with ordering-only
-# visibility, write the next round's witness right after passing a barrier.
-# The same brute force pins both.
-
-@pytest.mark.parametrize("p,r,k", [(2, 3, 2), (3, 3, 2), (3, 2, 3), (3, 3, 4)])
-def test_enumerator_striped_whole_grid(p, r, k):
-    res = en.enumerate_schedules(en.whole_grid(p, r), p, stripes=k)
-    assert not res.deadlock and res.violations == []
-    assert res.final_counters == {(r * p,)}
-
-
-def test_enumerator_striped_partial_and_oversized_n():
-    res = en.enumerate_schedules(en.whole_grid(3, 3, used_cores=2, n_members=2), 3, stripes=2)
-    assert not res.deadlock and res.violations == [] and res.final_counters == {(6,)}
-    res = en.enumerate_schedules(en.whole_grid(2, 1, used_cores=3, n_members=2), 2, stripes=2)
-    assert res.deadlock
-
-
-def test_enumerator_striped_negative_controls():
-    assert en.enumerate_schedules(en.whole_grid(2, 2), 2, stripes=2, poll_cmp="eq").deadlock
-    assert en.enumerate_schedules(en.whole_grid(3, 2), 3, stripes=2, skip=[(1, 0)]).deadlock
-    res = en.enumerate_schedules(en.whole_grid(3, 3), 3, stripes=2, counter_init=[1])
-    assert res.violations != [] or res.deadlock
-
-
-@pytest.mark.parametrize("k", [1, 2])
-def test_enumerator_early_write_ring_depths(k):
-    # whole grid: a writer can lead a reader by one round -> 2 rows suffice
-    assert en.enumerate_schedules(en.whole_grid(3, 3), 3, stripes=k, early_write=True,
-                                  ring_depth=2).violations == []
-    assert en.enumerate_schedules(en.whole_grid(3, 3), 3, stripes=k, early_write=True,
-                                  ring_depth=1).violations != []
-    # grouped A/B/mix: 4 rows are needed and suffice
-    g = en.grouped(4, 6)
-    res4 = en.enumerate_schedules(g, 4, stripes=k, early_write=True, ring_depth=4)
-    assert not res4.deadlock and res4.violations == [] and res4.final_counters == {(4, 4, 8)}
-    assert en.enumerate_schedules(g, 4, stripes=k, early_write=True, ring_depth=3).violations != []
-
-
-def test_enumerator_early_write_grouped_longer():
-    res = en.enumerate_schedules(en.grouped(4, 9), 4, stripes=2, early_write=True, ring_depth=4)
-    assert not res.deadlock and res.violations == [] and res.final_counters == {(6, 6, 12)}
-
-
-# The two-deep pipeline of the ordered witness kernels: a member writes the
-# witness of its own round i + 2 right after passing round i's barrier, and
-# may still be reading round i's row until it arrives at round i + 2.  A ring
-# of D rows is safe exactly when the writer cannot reach a row again while a
-# reader is still on it; the brute force fixes the smallest D for each
-# pattern (the kernels use six rows for both).
-
-@pytest.mark.parametrize("k", [1, 2])
-def test_enumerator_two_deep_pipeline_whole_grid(k):
-    for p, r in ((3, 4), (4, 6)):
-        res = en.enumerate_schedules(en.whole_grid(p, r), p, stripes=k, write_lead=2, read_lag=2,
-                                     ring_depth=4)
-        assert not res.deadlock and res.violations == [] and res.final_counters == {(p * r,)}
-        assert en.enumerate_schedules(en.whole_grid(p, r), p, stripes=k, write_lead=2,
-                                      read_lag=2, ring_depth=3).violations != []
-    res = en.enumerate_schedules(en.whole_grid(3, 4, used_cores=2, n_members=2), 3, stripes=k,
-                                 write_lead=2, read_lag=2, ring_depth=4)
-    assert not res.deadlock and res.violations == [] and res.final_counters == {(8,)}
-
-
-@pytest.mark.parametrize("k", [1, 2])
-def test_enumerator_two_deep_pipeline_grouped(k):
-    for p, r in ((4, 9), (4, 12), (5, 9)):
-        g = en.grouped(p, r)
-        res = en.enumerate_schedules(g, p, stripes=k, write_lead=2, read_lag=2, ring_depth=6)
-        assert not res.deadlock and res.violations == []
-        assert res.final_counters == {en.expected_final_counters(g)}
-    g = en.grouped(4, 12)
-    assert en.enumerate_schedules(g, 4, stripes=k, write_lead=2, read_lag=2,
-                                  ring_depth=5).violations != []
-
-
-def test_enumerator_lead_plus_lag_bound():
-    # whole grid: safe exactly when write lead + read lag <= D
-    for a in (1, 2, 3):
-        for b in (1, 2, 3):
-            for d in (a + b - 1, a + b):
-                # enough rounds for the writer to come back to the same row
-                res = en.enumerate_schedules(en.whole_grid(3, d + 2), 3, write_lead=a,
-                                             read_lag=b, ring_depth=d)
-                assert (res.violations == []) == (d >= a + b), (a, b, d)
-
-
 # The method on real host threads: T threads write, pass the epoch barrier
 # (acq_rel add, acquire poll) and sum every slot; the sums must equal the
 # sequential simulator's for every round.

@@ -15,8 +15,8 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-MODES = [0, 1, 2, 3]
-MODE_IDS = ["striped-order", "flat-order", "striped-full", "flat-full"]
+MODES = [0, 1, 2, 3, 4, 6]  # striped / flat / tree x ordering-only / full fences
+MODE_IDS = ["striped-order", "flat-order", "striped-full", "flat-full", "tree-order", "tree-full"]
 
 
 def _say(msg):
