@@ -51,6 +51,10 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def sha256_of(a) -> str:
+    return hashlib.sha256(memoryview(a).cast("B")).hexdigest()
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +133,7 @@ class Bench:
         self.dev = torch.device("cuda")
         self.ws = workloads.workspace(3)
         self.extra = {}
+        self.gpu_sha = {}  # SHA-256 of each configuration's GPU outputs
 
     # ------------------------------------------------------------ headline
     def headline(self):
@@ -157,6 +162,7 @@ class Bench:
         assert arrivals == [rounds * n_grid], arrivals
         ms_per_step = max(ms_events, wall * 1e3 / args.steps)
         self.extra["ns_per_round_with_witness"] = round(ms_per_step * 1e6 / rounds, 1)
+        self.gpu_sha["cfg1"] = sha256_of(out.cpu().numpy())
 
         def pass2():
             ccb.check(ccb.ccb_syncall_workspace_reset(ws, 1, stream), "reset")
@@ -366,6 +372,40 @@ class Bench:
         st, _ = ccb.ccb_syncall_status(ws, 3, stream)
         ccb.check(st, "grouped status")
         self.extra["grouped_ns_per_round"] = round(ms * 1e6 / g["rounds"], 1)
+        out_sha = sha256_of(gout.cpu().numpy())
+        self.grouped_kinds(gslots, gout, out_sha)
+        return out_sha
+
+    def grouped_kinds(self, gslots, gout, out_sha, skip=64):
+        """Time per round kind from a timeline launch (ccb_bench_grouped_timeline):
+        each member's wall clock at every barrier it passes, for its first
+        1024 own rounds.  An even member's own rounds alternate A, mix; an odd
+        member's B, mix; a round's time is the member's stamp minus its
+        previous one.  The timeline launch must compute the same outputs."""
+        np, torch, ccb, ws, stream = self.np, self.torch, self.ccb, self.ws, self.stream
+        g = self.inputs.GROUPED
+        n_wg, cap = g["n_wg"], ccb.CCB_BREAKDOWN_MAX_ROUNDS
+        stamps = torch.zeros(cap * n_wg, dtype=torch.int64, device=self.dev)
+        ccb.check(ccb.ccb_syncall_workspace_reset(ws, 3, stream), "reset")
+        ccb.check(ccb.ccb_bench_grouped_timeline(ws, gslots, gout, stamps, g["seed"], g["rounds"],
+                                                 n_wg, g["threads"], 2, self.mode, stream),
+                  "grouped timeline")
+        st, _ = ccb.ccb_syncall_status(ws, 3, stream)
+        ccb.check(st, "grouped timeline status")
+        assert sha256_of(gout.cpu().numpy()) == out_sha
+        t = stamps.cpu().numpy().reshape(cap, n_wg).astype(np.float64) * self.tick_ns
+        d = np.diff(t, axis=0)[skip:]   # row i - 1 - skip: own round i
+        first = skip + 1                # own round index of d's first row
+        own = np.arange(first, first + d.shape[0])
+        even, odd = d[:, 0::2], d[:, 1::2]
+        med = lambda a: round(float(np.median(a)), 1)
+        self.extra["grouped_ns_per_round_kind"] = {
+            "A": med(even[own % 2 == 0]), "B": med(odd[own % 2 == 0]),
+            "mix": med(np.concatenate([even[own % 2 == 1], odd[own % 2 == 1]])),
+            "own_rounds_stamped": int(d.shape[0]),
+            "note": "per member: wall clock at passing a barrier minus at passing its previous "
+                    "one; A and B rounds run at the same time on disjoint halves"}
+        log(f"grouped per kind: {self.extra['grouped_ns_per_round_kind']}")
 
     # ------------------------------------------------------------ streaming copy ceiling
     def copy_ceiling(self):
@@ -406,6 +446,7 @@ class Bench:
         ccb.check(st, "stencil status")
         assert arr == [(STENCIL_ITERS - 1) * s["n_wg"]], arr
         st_ms = statistics.median(times)
+        self.gpu_sha["cfg2"] = sha256_of(a.cpu().numpy())  # 64 iterations end in bufA
         self.stencil_phases(run_args=(a, b, x0, halo, s))
         alg_bytes = STENCIL_BYTES_PER_ITER * STENCIL_ITERS
         achieved = alg_bytes / (st_ms / 1e3) / 1e9
@@ -466,6 +507,7 @@ class Bench:
         batch()
         bms = min(self.timer(batch, reps=20) for _ in range(3))
         assert int(err.item()) == 0
+        self.gpu_sha["cfg3"] = (sha256_of(fin.cpu().numpy()), sha256_of(rel.cpu().numpy()))
         cnt_bytes = val.nbytes + meta.nbytes + CNT_COUNTERS * 4 + rows * CNT_COUNTERS
         gbs = cnt_bytes / (bms / 1e3) / 1e9
         self.extra["cntnotify_batch"] = {"us_per_launch": round(bms * 1e3, 2), "GBs": round(gbs, 1),
@@ -508,20 +550,22 @@ class Bench:
         log(f"cntnotify record + wait pair: {out}")
 
     # ------------------------------------------------------------ stream-to-stream notify
-    def cnt_stream_latency(self, producers=(1, 2, 4, 8, 16), rounds=110, skip=10):
+    def cnt_stream_latency(self, producers=(1, 2, 4, 8, 16), rounds=210, skip=10):
         """CntNotify §5's pattern on streams at scale: N producer streams each
-        record ADD 1 after a short spin (so the wait is usually polling
-        already), the consumer stream waits GE N with isClear.  Latency = the
-        last record's completion to the wait's completion, from HIP events on
-        the streams; rounds are separated on the host.  The records are
-        enqueued before the wait, so that a wait never sits in a hardware
-        queue in front of the records it waits for (the process has 4
-        hardware queues).  Beside it, on the same streams, HIP's own
-        cross-stream dependency: each producer runs an empty one-lane kernel
-        and records an event, the consumer waits for all N events and runs an
-        empty one-lane kernel; latency = the last producer event to the
-        consumer's event.  And the floor of any stream-ordered wait: an empty
-        one-lane kernel between two events on one stream."""
+        spin briefly (so the wait is usually polling already), record an
+        event, then record ADD 1; the consumer stream waits GE N with isClear
+        and records an event.  Latency = the consumer's event minus the
+        latest producer event, so it covers the record kernel's own launch,
+        the wait's detection and the wait kernel's completion.  (An event
+        recorded after a record kernel is not a usable start: with more
+        streams than the process's 4 hardware queues its timestamp can trail
+        the consumer's.)  The records are enqueued before the wait, so that a
+        wait never sits in a hardware queue in front of a record it needs.
+        Beside it, the same shape through HIP's own cross-stream dependency
+        (producers run an empty one-lane kernel, the consumer waits for
+        their events and runs one), and an empty one-lane kernel between two
+        events on one stream: the launch-and-complete cost any kernel on the
+        path pays."""
         ccb, torch = self.ccb, self.torch
         out = {}
 
@@ -530,70 +574,127 @@ class Bench:
             return {"median_us": round(xs[len(xs) // 2], 2),
                     "p90_us": round(xs[int(len(xs) * 0.9)], 2)}
 
+        def ev(stream):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            return e
+
         for n in producers:
             prods = [torch.cuda.Stream() for _ in range(n)]
             cons = torch.cuda.Stream()
             st, h = ccb.ccb_cnt_notify_create(0)
             ccb.check(st, "create")
-            lat, base = [], []
+            lat, dep = [], []
             for r in range(rounds):
-                evs = []
+                pre = []
                 for s in prods:  # producers first: see the docstring
                     with torch.cuda.stream(s):
                         torch.cuda._sleep(20000)
+                    pre.append(ev(s))
                     ccb.check(ccb.ccb_cnt_notify_record(
                         h, s, ccb.record_info(ccb.CCB_CNT_RECORD_ADD, 1)), "record")
-                    e = torch.cuda.Event(enable_timing=True)
-                    e.record(s)
-                    evs.append(e)
                 ccb.check(ccb.ccb_cnt_notify_wait(
                     h, cons, ccb.wait_info(ccb.CCB_CNT_WAIT_BIGGER_OR_EQUAL, n, 2, 1)), "wait")
-                ev_c = torch.cuda.Event(enable_timing=True)
-                ev_c.record(cons)
+                ev_c = ev(cons)
                 torch.cuda.synchronize()
                 st, v, last = ccb.ccb_cnt_notify_query(h, cons)
                 assert (st, v, last) == (0, 0, ccb.CCB_OK), (n, r, st, v, last)
-                # the floor: the same dependency through HIP events
-                evs2 = []
+                # the same dependency through HIP events
+                pre2, post2 = [], []
                 for s in prods:
                     with torch.cuda.stream(s):
                         torch.cuda._sleep(20000)
+                    pre2.append(ev(s))
+                    with torch.cuda.stream(s):
                         torch.cuda._sleep(1)  # empty one-lane kernel
-                    e = torch.cuda.Event(enable_timing=True)
-                    e.record(s)
-                    evs2.append(e)
-                for e in evs2:
+                    post2.append(ev(s))
+                for e in post2:
                     cons.wait_event(e)
                 with torch.cuda.stream(cons):
                     torch.cuda._sleep(1)
-                ev_f = torch.cuda.Event(enable_timing=True)
-                ev_f.record(cons)
+                ev_f = ev(cons)
                 torch.cuda.synchronize()
                 if r >= skip:
-                    lat.append(min(e.elapsed_time(ev_c) for e in evs) * 1e3)
-                    base.append(min(e.elapsed_time(ev_f) for e in evs2) * 1e3)
+                    lat.append(min(e.elapsed_time(ev_c) for e in pre) * 1e3)
+                    dep.append(min(e.elapsed_time(ev_f) for e in pre2) * 1e3)
             ccb.check(ccb.ccb_cnt_notify_destroy(h), "destroy")
-            out[f"producers_{n}"] = {**stats(lat), "hip_event_dependency": stats(base)}
-        # the part no stream-ordered wait can avoid: a kernel's completion
-        # reaching an event on its stream (an empty one-lane kernel between
-        # two events on one stream), and two events back to back
+            out[f"producers_{n}"] = {**stats(lat), "hip_event_dependency": stats(dep)}
         s = torch.cuda.Stream()
-        kern, ev = [], []
+        kern = []
         for r in range(rounds):
-            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-            e0.record(s)
-            e1.record(s)
+            # the spin keeps the stream busy while the host enqueues, so that
+            # e1 -> e2 is the kernel's launch and completion, not host time
+            with torch.cuda.stream(s):
+                torch.cuda._sleep(20000)
+            e1 = ev(s)
             with torch.cuda.stream(s):
                 torch.cuda._sleep(1)
-            e2.record(s)
+            e2 = ev(s)
             e2.synchronize()
             if r >= skip:
-                ev.append(e0.elapsed_time(e1) * 1e3)
                 kern.append(e1.elapsed_time(e2) * 1e3)
-        out["floor_empty_kernel_on_one_stream"] = stats(kern)
-        out["floor_event_to_event"] = stats(ev)
+        out["empty_kernel_between_events"] = stats(kern)
         self.extra["cntnotify_stream_notify_latency"] = out
         log(f"cntnotify stream notify latency: {out}")
+
+    # ------------------------------------------------------------ parity record
+    def parity_record(self):
+        """Every configuration at full size: SHA-256 of its input arrays, of
+        the GPU's outputs and of the oracle's (one host thread, timed).  The
+        witness configurations have no input arrays: their values come from
+        the seed inside the kernels."""
+        import oracle
+        np = self.np
+        rec = {}
+
+        def timed(fn):
+            t1 = time.perf_counter()
+            r = fn()
+            return r, time.perf_counter() - t1
+
+        # cfg 0: 8 workgroups x 64 threads, 100 rounds, seed 0 (run here)
+        res = self.wl.slot_rounds(0, 100, 8, 64)
+        (o0, _, c0, rc), t0 = timed(lambda: oracle.slot_rounds(0, 100, 8, 0))
+        assert rc == 0 and res.counters == [c0] == [800]
+        rec["cfg0"] = {"inputs": "seed 0 (no input arrays)",
+                       "gpu_out_sha256": sha256_of(res.out.cpu().numpy()),
+                       "oracle_out_sha256": sha256_of(o0), "oracle_one_thread_s": round(t0, 4)}
+        w = self.inputs.WITNESS_GRID
+        (o1, _, c1, rc), t1 = timed(lambda: oracle.slot_rounds(w["seed"], w["rounds"], w["n_wg"], 0))
+        assert rc == 0
+        rec["cfg1"] = {"inputs": "seed 1 (no input arrays)", "gpu_out_sha256": self.gpu_sha["cfg1"],
+                       "oracle_out_sha256": sha256_of(o1), "oracle_one_thread_s": round(t1, 3)}
+        st = self.inputs.STENCIL
+        x = self.inputs.stencil_input(st["seed"], STENCIL_N)
+        y, t2 = timed(lambda: oracle.stencil(x, STENCIL_ITERS))
+        rec["cfg2"] = {"x_sha256": sha256_of(x), "gpu_out_sha256": self.gpu_sha["cfg2"],
+                       "oracle_out_sha256": sha256_of(y), "oracle_one_thread_s": round(t2, 2)}
+        c = self.inputs.CNT_BATCH
+        val, meta, rows = self.inputs.cnt_batch_input(c["seed"], CNT_COUNTERS, CNT_OPS)
+        (fin, rel, rc), t3 = timed(lambda: oracle.cnt_batch(val, meta, rows))
+        assert rc == 0
+        rec["cfg3"] = {"val_sha256": sha256_of(val), "meta_sha256": sha256_of(meta),
+                       "gpu_final_sha256": self.gpu_sha["cfg3"][0],
+                       "gpu_rel_sha256": self.gpu_sha["cfg3"][1],
+                       "oracle_final_sha256": sha256_of(fin), "oracle_rel_sha256": sha256_of(rel),
+                       "oracle_one_thread_s": round(t3, 3)}
+        g = self.inputs.GROUPED
+        (o4, _, c4, rc), t4 = timed(lambda: oracle.grouped_rounds(g["seed"], g["rounds"], g["n_wg"]))
+        assert rc == 0
+        rec["cfg4"] = {"inputs": "seed 4 (no input arrays)", "gpu_out_sha256": self.gpu_sha["cfg4"],
+                       "oracle_out_sha256": sha256_of(o4), "oracle_one_thread_s": round(t4, 2)}
+        for k, r in rec.items():
+            gpu = [v for n, v in r.items() if n.startswith("gpu_")]
+            ora = [v for n, v in r.items() if n.startswith("oracle_") and n.endswith("sha256")]
+            r["match"] = gpu == ora
+        self.extra["parity_record"] = rec
+        self.oracle_times = {"cfg0_ns_per_barrier": round(t0 / 100 * 1e9, 1),
+                             "cfg4_ns_per_round": round(t4 / g["rounds"] * 1e9, 1),
+                             "stencil_64_iterations_s": round(t2, 2),
+                             "stencil_64_iterations_GBs": round(
+                                 STENCIL_BYTES_PER_ITER * STENCIL_ITERS / t2 / 1e9, 3)}
+        log(f"parity record: { {k: r['match'] for k, r in rec.items()} }")
+        assert all(r["match"] for r in rec.values()), rec
 
     # ------------------------------------------------------------ CPU baseline
     def cpu_baseline(self):
@@ -665,6 +766,7 @@ class Bench:
         assert all(r[2] == 0 for r in bp) and np.array_equal(np.concatenate([r[0] for r in bp]), fin1)
         self.extra["cpu_context"] = {
             "host": {"nproc": nproc, "cpu_model": model},
+            "oracle_one_thread": getattr(self, "oracle_times", None),
             "host_thread_barrier": {"threads": threads, "ns_per_barrier": round(ns, 1),
                                     "rounds": 20_000},
             "oracle_stencil_one_iteration_GBs": round(STENCIL_BYTES_PER_ITER / st_s / 1e9, 3),
@@ -720,7 +822,7 @@ def main():
         b.barrier_breakdown(floor)
         b.barrier_breakdown(floor, "striped-full")
         b.hip_grid_sync()
-        b.grouped()
+        b.gpu_sha["cfg4"] = b.grouped()
         gbs = b.copy_ceiling()
         roofline = b.stencil(gbs)
         b.cnt_batch()
@@ -728,6 +830,7 @@ def main():
         b.cnt_graph()
         if not args.no_cpu:
             cpu = b.cpu_baseline()
+            b.parity_record()
             b.cpu_context()
 
     line = {

@@ -112,6 +112,8 @@ _f = {
                                 _I32, _I32, _U32, _I32, _V),
     "ccb_run_grouped_rounds": _sig("ccb_run_grouped_rounds", _I32, _V, _V, _V, _V, _U64, _I32, _I32,
                                    _I32, _I32, _U32, _I32, _V),
+    "ccb_bench_grouped_timeline": _sig("ccb_bench_grouped_timeline", _I32, _V, _V, _V, _V, _U64,
+                                       _I32, _I32, _I32, _I32, _I32, _V),
     "ccb_run_stencil": _sig("ccb_run_stencil", _I32, _V, _V, _I64, _I32, _V, _V, ctypes.c_size_t,
                             _V, _I32, _I32, _I32, _U32, _I32, _V),
     "ccb_run_stencil_noalloc": _sig("ccb_run_stencil_noalloc", _I32, _V, _V, _I64, _I32, _V, _I32,
@@ -207,6 +209,12 @@ def ccb_run_grouped_rounds(ws, slots, out, wg_status, seed, rounds, n_grid, thre
                            wgs_per_cu=0, max_poll=0, mode=0, stream=None) -> int:
     return _f["ccb_run_grouped_rounds"](_p(ws), _p(slots), _p(out), _p(wg_status), seed, rounds,
                                         n_grid, threads, wgs_per_cu, max_poll, mode, _s(stream))
+
+
+def ccb_bench_grouped_timeline(ws, slots, out, stamps, seed, rounds, n_grid, threads,
+                               wgs_per_cu=0, mode=0, stream=None) -> int:
+    return _f["ccb_bench_grouped_timeline"](_p(ws), _p(slots), _p(out), _p(stamps), seed, rounds,
+                                            n_grid, threads, wgs_per_cu, mode, _s(stream))
 
 
 def ccb_stencil_halo_bytes(n: int, threads: int, n_grid: int) -> int:

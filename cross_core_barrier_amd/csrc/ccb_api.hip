@@ -115,7 +115,7 @@ constexpr int kModeSlots = 8;  // mode values 0..7 index the query table
 // streams share them); the host waits for them once.
 constexpr int kSgprPerSimd = 800;
 constexpr int kTrapSgprs = 16;
-constexpr int kKernelIds = 5;
+constexpr int kKernelIds = 6;
 
 struct RegQuery {
     bool done = false;
@@ -493,8 +493,28 @@ CCB_API ccbStatus ccb_run_grouped_rounds(int32_t* ws, uint32_t* slots, uint32_t*
     ccbStatus st = plan_persistent(ccb::KernelId::GroupedRounds, mode, nGrid, threads, wgsPerCu,
                                    (hipStream_t)stream, &ls);
     if (st != CCB_OK) return st;
-    return from_hip(ccb::launch_grouped_rounds(ls, ws, slots, out, wgStatus, seed, rounds,
+    return from_hip(ccb::launch_grouped_rounds(ls, ws, slots, out, wgStatus, nullptr, seed, rounds,
                                                poll_bound(maxPoll)));
+}
+
+CCB_API ccbStatus ccb_bench_grouped_timeline(int32_t* ws, uint32_t* slots, uint32_t* out,
+                                             uint64_t* stamps, uint64_t seed, int32_t rounds,
+                                             int32_t nGrid, int32_t threads, int32_t wgsPerCu,
+                                             int32_t mode, ccbStream stream)
+{
+    if (ws == nullptr || stamps == nullptr || (rounds > 0 && (slots == nullptr || out == nullptr)))
+        return CCB_ERR_NULL_POINTER;
+    if (!aligned(ws, CCB_LINE_BYTES) || !aligned(stamps, 8) || rounds < 0 || nGrid < 2 ||
+        (nGrid % 2) != 0 || !valid_threads(threads) || wgsPerCu < 0 || !valid_mode(mode) ||
+        !counts_fit(((int64_t)rounds + 2) / 3, nGrid, mode))
+        return CCB_ERR_INVALID_VALUE;
+    std::lock_guard<std::mutex> lk(g_launch_mu);
+    ccb::LaunchShape ls;
+    ccbStatus st = plan_persistent(ccb::KernelId::GroupedStamps, mode, nGrid, threads, wgsPerCu,
+                                   (hipStream_t)stream, &ls);
+    if (st != CCB_OK) return st;
+    return from_hip(ccb::launch_grouped_rounds(ls, ws, slots, out, nullptr, stamps, seed, rounds,
+                                               CCB_SOFT_MAX_POLL));
 }
 
 CCB_API size_t ccb_stencil_halo_bytes(int64_t n, int32_t threads, int32_t nGrid)

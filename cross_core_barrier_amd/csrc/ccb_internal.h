@@ -16,7 +16,7 @@ constexpr bool kStencilNTLoad = true;
 constexpr int kCntUnroll = 1;      // ops per register set in the batch engine's two-set pipeline
 constexpr bool kCntNTLoad = true;   // non-temporal loads of the op stream (read once)
 
-enum class KernelId { BarrierOnly, SlotRounds, GroupedRounds, Stencil, BarrierStamps };
+enum class KernelId { BarrierOnly, SlotRounds, GroupedRounds, Stencil, BarrierStamps, GroupedStamps };
 
 struct LaunchShape {
     const void* fn;  // the kernel instance
@@ -40,8 +40,8 @@ hipError_t launch_slot_rounds(const LaunchShape& ls, int32_t* ws, uint32_t* slot
                               int32_t* wgStatus, uint64_t seed, int32_t rounds, int32_t nMembers,
                               uint32_t maxPoll);
 hipError_t launch_grouped_rounds(const LaunchShape& ls, int32_t* ws, uint32_t* slots,
-                                 uint32_t* out, int32_t* wgStatus, uint64_t seed, int32_t rounds,
-                                 uint32_t maxPoll);
+                                 uint32_t* out, int32_t* wgStatus, uint64_t* stamps, uint64_t seed,
+                                 int32_t rounds, uint32_t maxPoll);
 hipError_t launch_stencil(const LaunchShape& ls, int32_t* bufA, int32_t* bufB, int64_t n,
                           int32_t iters, int32_t* ws, int32_t* halo, uint64_t* timeline,
                           uint32_t maxPoll);

@@ -290,10 +290,27 @@ struct FinishRound {
 //   counter(q), n(q), member(q)   barrier of round q
 //   row(q), len(q)          the slots summed in round q
 //   slot(q)                 this member's slot in round q
-template <int K, ccbVisibility V, class Sched>
+// No round stamps.
+struct NoStamps {
+    __device__ __forceinline__ void operator()(int32_t) const {}
+};
+
+// The wall clock at which the member passed the barrier of its own round i,
+// for the first `cap` rounds, into LDS (written out by the caller).
+struct RoundStamps {
+    uint64_t* lds;
+    int32_t cap;
+    __device__ __forceinline__ void operator()(int32_t i) const
+    {
+        if (i < cap) lds[i] = wall_clock64();
+    }
+};
+
+template <int K, ccbVisibility V, class Sched, class Stamp = NoStamps>
 __device__ __forceinline__ int32_t witness_pipeline(const Sched& sc, int32_t rounds,
                                                     uint32_t* out, int32_t nGrid, int32_t w,
-                                                    uint64_t seed, uint32_t maxPoll, int32_t* err)
+                                                    uint64_t seed, uint32_t maxPoll, int32_t* err,
+                                                    Stamp stamp = Stamp())
 {
     __shared__ uint32_t partials[2][1024 / kWave];
     __shared__ int32_t result[2];
@@ -329,7 +346,10 @@ __device__ __forceinline__ int32_t witness_pipeline(const Sched& sc, int32_t rou
         work(i, into, from);
         if (threadIdx.x < kWave) {
             const int32_t e = ccb_await<K, V>(sc.counter(q), sc.n(q), sc.member(q), before, maxPoll, err);
-            if (leader()) result[i & 1] = e;
+            if (leader()) {
+                result[i & 1] = e;
+                stamp(i);
+            }
         }
         ccb_wait_memory();  // this round's loads and stores, before the next arrival
         __syncthreads();
@@ -419,14 +439,23 @@ __global__ __launch_bounds__(1024) void ccb_k_slot_rounds(int32_t* ws, uint32_t*
 // its round m_i a member reads row m_i, stores the witness of m_{i+2} and
 // sums row m_{i-1} before arriving at m_{i+1}.
 // ---------------------------------------------------------------------------
-template <int K, ccbVisibility V>
+// kStamps: member w also records, for each of its own first
+// CCB_BREAKDOWN_MAX_ROUNDS rounds i, the wall clock when it passed that
+// round's barrier; they stay in LDS and go to stamps[i * nGrid + w] at the
+// end (0 past the member's last round).
+template <int K, ccbVisibility V, bool kStamps>
 __global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32_t* slots,
                                                               uint32_t* out, int32_t* wgStatus,
-                                                              uint64_t seed, int32_t rounds,
-                                                              uint32_t maxPoll)
+                                                              uint64_t* stamps, uint64_t seed,
+                                                              int32_t rounds, uint32_t maxPoll)
 {
     __shared__ uint32_t partial[1024 / kWave];
+    __shared__ uint64_t stampLds[kStamps ? CCB_BREAKDOWN_MAX_ROUNDS : 1];
     if (register_query(maxPoll, ws)) return;
+    if constexpr (kStamps) {
+        for (int32_t i = threadIdx.x; i < CCB_BREAKDOWN_MAX_ROUNDS; i += blockDim.x) stampLds[i] = 0;
+        __syncthreads();
+    }
     const int32_t w = blockIdx.x;
     const int32_t nGrid = gridDim.x;
     const int32_t half = nGrid / 2;
@@ -436,6 +465,7 @@ __global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32
     int32_t rc = CCB_OK;
     auto member_of = [&](int32_t r) { return (r % 3) == 2 || (r % 3) == parity; };
     if constexpr (V == CCB_VIS_FULL) {
+        int32_t own = 0;  // this member's rounds so far
         for (int32_t r = 0; r < rounds; ++r) {
             const int32_t kind = r % 3;
             if (!member_of(r)) continue;
@@ -445,6 +475,10 @@ __global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32
             const int32_t member = kind == 2 ? w : (w >> 1);
             rc = ccb_barrier<K, V>(ws + kind * CCB_STRIPES * CCB_LINE_WORDS, n, member, maxPoll, err);
             if (rc != CCB_OK) break;
+            if constexpr (kStamps) {
+                if (leader()) RoundStamps{stampLds, CCB_BREAKDOWN_MAX_ROUNDS}(own);
+                ++own;
+            }
             const int32_t first = kind == 2 ? 0 : kind * half;
             uint32_t s = 0;
             for (int32_t i = threadIdx.x; i < n; i += blockDim.x)
@@ -478,8 +512,18 @@ __global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32
                 return slots + ((size_t)(q % kRing) * nGrid + pos) * kSlot;
             }
         };
-        rc = witness_pipeline<K, V>(Grouped{ws, slots, nGrid, half, w, parity, pos, rounds}, rounds,
-                                    out, nGrid, w, seed, maxPoll, err);
+        const Grouped sched{ws, slots, nGrid, half, w, parity, pos, rounds};
+        if constexpr (kStamps)
+            rc = witness_pipeline<K, V>(sched, rounds, out, nGrid, w, seed, maxPoll, err,
+                                        RoundStamps{stampLds, CCB_BREAKDOWN_MAX_ROUNDS});
+        else
+            rc = witness_pipeline<K, V>(sched, rounds, out, nGrid, w, seed, maxPoll, err);
+    }
+    if constexpr (kStamps) {
+        __syncthreads();
+        const int32_t nStamp = rounds < CCB_BREAKDOWN_MAX_ROUNDS ? rounds : CCB_BREAKDOWN_MAX_ROUNDS;
+        for (int32_t i = threadIdx.x; i < nStamp; i += blockDim.x)
+            stamps[(size_t)i * nGrid + w] = stampLds[i];
     }
     if (wgStatus != nullptr && leader()) wgStatus[w] = rc == CCB_OK ? 1 : 3;
 }
@@ -1305,7 +1349,8 @@ const void* kernel_ptr(KernelId id, int32_t mode)
     case KernelId::BarrierOnly: return CCB_PICK_X(ccb_k_barrier_only, mode, false);
     case KernelId::BarrierStamps: return CCB_PICK_X(ccb_k_barrier_only, mode, true);
     case KernelId::SlotRounds: return CCB_PICK(ccb_k_slot_rounds, mode);
-    case KernelId::GroupedRounds: return CCB_PICK(ccb_k_grouped_rounds, mode);
+    case KernelId::GroupedRounds: return CCB_PICK_X(ccb_k_grouped_rounds, mode, false);
+    case KernelId::GroupedStamps: return CCB_PICK_X(ccb_k_grouped_rounds, mode, true);
     case KernelId::Stencil: return CCB_PICK(ccb_k_stencil, mode);
     }
     return nullptr;
@@ -1328,10 +1373,10 @@ hipError_t launch_slot_rounds(const LaunchShape& ls, int32_t* ws, uint32_t* slot
 }
 
 hipError_t launch_grouped_rounds(const LaunchShape& ls, int32_t* ws, uint32_t* slots,
-                                 uint32_t* out, int32_t* wgStatus, uint64_t seed, int32_t rounds,
-                                 uint32_t maxPoll)
+                                 uint32_t* out, int32_t* wgStatus, uint64_t* stamps, uint64_t seed,
+                                 int32_t rounds, uint32_t maxPoll)
 {
-    void* args[] = {&ws, &slots, &out, &wgStatus, &seed, &rounds, &maxPoll};
+    void* args[] = {&ws, &slots, &out, &wgStatus, &stamps, &seed, &rounds, &maxPoll};
     return coop(ls.fn, ls.nGrid, ls.threads, ls.lds, ls.stream, args);
 }
 
@@ -1370,8 +1415,9 @@ hipError_t launch_register_query(KernelId id, int32_t mode, int32_t* out, hipStr
         void* args[] = {&out, &none, &none, &none, &seed, &zero, &zero, &query};
         return hipLaunchKernel(fn, dim3(1), dim3(kWave), args, 0, s);
     }
-    case KernelId::GroupedRounds: {
-        void* args[] = {&out, &none, &none, &none, &seed, &zero, &query};
+    case KernelId::GroupedRounds:
+    case KernelId::GroupedStamps: {
+        void* args[] = {&out, &none, &none, &none, &none, &seed, &zero, &query};
         return hipLaunchKernel(fn, dim3(1), dim3(kWave), args, 0, s);
     }
     case KernelId::Stencil: {

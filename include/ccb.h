@@ -291,6 +291,21 @@ CCB_API ccbStatus ccb_run_grouped_rounds(int32_t* ws, uint32_t* slots, uint32_t*
                                          int32_t nGrid, int32_t threads, int32_t wgsPerCu,
                                          uint32_t maxPoll, int32_t mode, ccbStream stream);
 
+/* ccb_run_grouped_rounds (usedCores, wgStatus and maxPoll at their
+ * defaults) with a timeline, for per-round-kind timing (instrumentation, not
+ * on the pages): member w records, for each of its first
+ * CCB_BREAKDOWN_MAX_ROUNDS own rounds i (an even w's rounds are the A and mix
+ * rounds, an odd w's the B and mix rounds, in order), the device wall clock
+ * when it passed that round's barrier:
+ *   stamps  device, min(rounds, CCB_BREAKDOWN_MAX_ROUNDS) * nGrid uint64,
+ *           8-B aligned; stamps[i * nGrid + w], 0 past w's last round
+ * The stamps are kept in LDS and written out at the end.  Other arguments
+ * and errors as ccb_run_grouped_rounds (NULL_POINTER also for stamps). */
+CCB_API ccbStatus ccb_bench_grouped_timeline(int32_t* ws, uint32_t* slots, uint32_t* out,
+                                             uint64_t* stamps, uint64_t seed, int32_t rounds,
+                                             int32_t nGrid, int32_t threads, int32_t wgsPerCu,
+                                             int32_t mode, ccbStream stream);
+
 /* Persistent barrier-separated stencil.  Iteration t reads buffer t & 1 and
  * writes buffer (t + 1) & 1 (buffer 0 = bufA, 1 = bufB):
  *   y[i] = (x[i-1] + 2 x[i] + x[i+1]) >> 2,  x[-1] = x[0], x[n] = x[n-1],

@@ -316,6 +316,28 @@ def test_breakdown_stamps_are_ordered(ccb, wl, mode):
     assert (t[:, :, 2].min(axis=1) >= t[:, :, 0].max(axis=1)).all()
 
 
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_grouped_timeline_matches_oracle(ccb, wl, mode):
+    """ccb_bench_grouped_timeline computes what ccb_run_grouped_rounds does
+    (the oracle's outputs) and stamps each member's own rounds in order:
+    an even member's rounds are A and mix, an odd member's B and mix."""
+    n, rounds = 16, 60
+    _say(f"grouped timeline: {n} x 64, {rounds} rounds, mode={mode}")
+    ws = wl.workspace(3)
+    slots = torch.zeros(ccb.CCB_SLOT_ROWS * ccb.CCB_SLOT_WORDS * n, dtype=torch.int32, device="cuda")
+    out = torch.zeros((rounds, n), dtype=torch.int32, device="cuda")
+    stamps = torch.zeros(rounds * n, dtype=torch.int64, device="cuda")
+    assert ccb.ccb_bench_grouped_timeline(ws, slots, out, stamps, 4, rounds, n, 64, 0, mode) == 0
+    st, ctrs = ccb.ccb_syncall_status(ws, 3, None)
+    want_out, _, want_ctrs, rc = oracle.grouped_rounds(4, rounds, n)
+    assert st == 0 and rc == 0 and tuple(ctrs) == want_ctrs
+    assert np.array_equal(_u32(out), want_out)
+    t = stamps.cpu().numpy().reshape(rounds, n)
+    own = rounds // 3 * 2   # rounds divisible by 3: each member takes 2 of every 3
+    assert (t[:own] > 0).all() and (t[own:] == 0).all()
+    assert (np.diff(t[:own], axis=0) >= 0).all()
+
+
 def test_breakdown_rejects_bad_arguments(ccb, wl):
     ws = wl.workspace(1)
     stamps = torch.zeros(8 * 3, dtype=torch.int64, device="cuda")
