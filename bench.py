@@ -286,6 +286,39 @@ class Bench:
         self.extra["latency_roofline"] = roof
         log(f"barrier-only ns/barrier at 256 WGs: {lat}")
 
+    # ------------------------------------------------------------ fence placement
+    def fence_placement(self, n_grid=256):
+        """ccb_bench_fence_placement: the full-visibility barrier's release and
+        acquire placed six ways at n_grid workgroups x 256 threads; ns per
+        barrier (slope over 500 -> 2500 rounds) and the fraction of plain
+        reads after the barrier that returned a stale value (2000 rounds)."""
+        np, torch, ccb, stream = self.np, self.torch, self.ccb, self.stream
+        nbytes = ccb.ccb_bench_fence_placement_bytes(n_grid)
+        scratch = torch.zeros(nbytes // 4, dtype=torch.int32, device=self.dev)
+        stale = torch.zeros(n_grid, dtype=torch.int32, device=self.dev)
+        names = ["none", "per_workgroup_release_acquire", "per_workgroup_release_only",
+                 "per_workgroup_acquire_only", "per_xcd_release_per_workgroup_acquire",
+                 "per_xcd_release_workgroup_scope_invalidate"]
+        err_word = ccb.CCB_STRIPES * 32
+        out = {}
+        for v, name in enumerate(names):
+            res = {}
+            for r in (500, 2500):
+                def f(r=r, v=v):
+                    ccb.check(ccb.ccb_bench_fence_placement(scratch, nbytes, stale, r, n_grid, 256, v,
+                                                            stream), "fence placement")
+                f()
+                res[r] = min(self.timer(f) for _ in range(3))
+                assert int(scratch[err_word].item()) == 0
+            ccb.check(ccb.ccb_bench_fence_placement(scratch, nbytes, stale, 2000, n_grid, 256, v,
+                                                    stream), "fence placement")
+            torch.cuda.synchronize()
+            assert int(scratch[err_word].item()) == 0
+            out[name] = {"ns_per_barrier": round((res[2500] - res[500]) / 2000 * 1e6, 1),
+                         "stale_read_fraction": round(float(stale.sum().item()) / (2000 * n_grid), 4)}
+        self.extra["fence_placement_at_256"] = out
+        log(f"fence placement: {out}")
+
     # ------------------------------------------------------------ where a barrier's time goes
     def barrier_breakdown(self, floor, mode_name=None, n_grid=256, rounds=1024, skip=64):
         """Per-member, per-round wall-clock stamps of barrier-only rounds at
@@ -798,10 +831,12 @@ def main():
         b.latency(floor)
         b.barrier_breakdown(floor)
         b.barrier_breakdown(floor, "striped-full")
+        b.fence_placement()
         print(json.dumps({k: b.extra[k] for k in ("floor", "barrier_only_ns_at_256",
                                                    "barrier_only_ns_by_workgroups",
                                                    "tree_order_ns_by_workgroups",
-                                                   "latency_roofline", "barrier_breakdown")}),
+                                                   "latency_roofline", "barrier_breakdown",
+                                                   "fence_placement_at_256")}),
               flush=True)
         return
 
@@ -821,6 +856,7 @@ def main():
         b.latency(floor)
         b.barrier_breakdown(floor)
         b.barrier_breakdown(floor, "striped-full")
+        b.fence_placement()
         b.hip_grid_sync()
         b.gpu_sha["cfg4"] = b.grouped()
         gbs = b.copy_ceiling()

@@ -125,6 +125,10 @@ _f = {
     "ccb_bench_atomic_contended": _sig("ccb_bench_atomic_contended", _I32, _V, _V, _I32, _I32, _V),
     "ccb_bench_notify_pingpong": _sig("ccb_bench_notify_pingpong", _I32, _V, _V, _I32, _I32,
                                       _U32, _V, _V),
+    "ccb_bench_fence_placement_bytes": _sig("ccb_bench_fence_placement_bytes", ctypes.c_size_t,
+                                            _I32),
+    "ccb_bench_fence_placement": _sig("ccb_bench_fence_placement", _I32, _V, ctypes.c_size_t, _V,
+                                      _I32, _I32, _I32, _I32, _V),
     "ccb_bench_hip_grid_sync": _sig("ccb_bench_hip_grid_sync", _I32, _I32, _I32, _I32, _V, _V),
     "ccb_bench_copy": _sig("ccb_bench_copy", _I32, _V, _V, _I64, _V),
     "ccb_cnt_notify_create": _sig("ccb_cnt_notify_create", _I32, _V, _U64),
@@ -257,6 +261,16 @@ def ccb_bench_atomic_contended(line, ticks, iters, n_grid, stream=None) -> int:
 def ccb_bench_notify_pingpong(lines, ticks_out, iters, peer, max_poll, err, stream=None) -> int:
     return _f["ccb_bench_notify_pingpong"](_p(lines), _p(ticks_out), iters, peer, max_poll, _p(err),
                                            _s(stream))
+
+
+def ccb_bench_fence_placement_bytes(n_grid: int) -> int:
+    return int(_f["ccb_bench_fence_placement_bytes"](n_grid))
+
+
+def ccb_bench_fence_placement(scratch, scratch_bytes, stale, rounds, n_grid, threads, variant,
+                              stream=None) -> int:
+    return _f["ccb_bench_fence_placement"](_p(scratch), scratch_bytes, _p(stale), rounds, n_grid,
+                                           threads, variant, _s(stream))
 
 
 def ccb_bench_hip_grid_sync(rounds, n_grid, threads, done_out, stream=None) -> int:

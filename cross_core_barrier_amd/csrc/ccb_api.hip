@@ -652,6 +652,33 @@ CCB_API ccbStatus ccb_bench_notify_pingpong(int32_t* lines, uint64_t* ticksOut, 
                                                 err, (hipStream_t)stream));
 }
 
+CCB_API size_t ccb_bench_fence_placement_bytes(int32_t nGrid)
+{
+    if (nGrid < 1) return 0;
+    return (size_t)(CCB_STRIPES + 17 + nGrid) * CCB_LINE_BYTES;
+}
+
+CCB_API ccbStatus ccb_bench_fence_placement(int32_t* scratch, size_t scratchBytes, int32_t* stale,
+                                            int32_t rounds, int32_t nGrid, int32_t threads,
+                                            int32_t variant, ccbStream stream)
+{
+    if (scratch == nullptr || stale == nullptr) return CCB_ERR_NULL_POINTER;
+    DeviceInfo info;
+    if (rounds < 1 || nGrid < 1 || !valid_threads(threads) || variant < 0 || variant > 5 ||
+        !aligned(scratch, CCB_LINE_BYTES) || !aligned(stale, 4) ||
+        scratchBytes < ccb_bench_fence_placement_bytes(nGrid) ||
+        !counts_fit((int64_t)rounds + 1, nGrid, 0))
+        return CCB_ERR_INVALID_VALUE;
+    ccbStatus st = current_device(nullptr, &info);
+    if (st != CCB_OK) return st;
+    if (nGrid > info.numCUs) return CCB_ERR_NOT_CORESIDENT;  // one workgroup per CU at most
+    const int64_t words = (int64_t)ccb_bench_fence_placement_bytes(nGrid) / 4;
+    if ((st = from_hip(ccb::launch_fill_zero(scratch, words, (hipStream_t)stream))) != CCB_OK)
+        return st;
+    return from_hip(ccb::launch_fence_placement(scratch, stale, rounds, nGrid, threads, variant,
+                                                CCB_SOFT_MAX_POLL, (hipStream_t)stream));
+}
+
 CCB_API ccbStatus ccb_bench_hip_grid_sync(int32_t rounds, int32_t nGrid, int32_t threads,
                                           int32_t* doneOut, ccbStream stream)
 {

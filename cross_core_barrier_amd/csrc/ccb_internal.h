@@ -67,6 +67,8 @@ hipError_t launch_notify_pingpong(int32_t* lines, uint64_t* ticks, int32_t iters
 hipError_t launch_hip_grid_sync(int32_t rounds, int32_t nGrid, int32_t threads, int32_t* done,
                                 int numCUs, hipStream_t s);
 hipError_t launch_copy(int4* dst, const int4* src, int64_t n16, int nBlocks, hipStream_t s);
+hipError_t launch_fence_placement(int32_t* scratch, int32_t* stale, int32_t rounds, int32_t nGrid,
+                                  int32_t threads, int32_t variant, uint32_t maxPoll, hipStream_t s);
 
 }  // namespace ccb
 

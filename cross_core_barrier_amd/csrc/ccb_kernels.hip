@@ -1281,6 +1281,127 @@ __global__ void ccb_k_notify_pingpong(int32_t* lines, uint64_t* ticks, int32_t i
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Where the full-visibility barrier's cache maintenance can go: barrier-only
+// rounds on the striped counter with one plain store before each barrier and
+// one plain load after it, and the release (L2 write-back) and acquire
+// (invalidate) placed per variant:
+//   0  none (the ordering-only barrier)
+//   1  every workgroup: release before its arrival, acquire after its poll
+//      (CCB_VIS_FULL)
+//   2  every workgroup: release only
+//   3  every workgroup: acquire only
+//   4  one release per XCD: once all members have arrived, one leader per
+//      XCD writes its L2 back (and invalidates it) and raises that XCD's
+//      flag; every workgroup waits for the flags of all XCDs with members,
+//      then acquires
+//   5  as 4, but the workgroups' acquire is the workgroup-scope invalidate
+//      (`buffer_inv sc0`) instead of the agent-scope one
+// Leaders are found at the start: each member adds one to its XCD's count
+// (XCC_ID) and the first one in is the leader; one ordering-only barrier
+// later every member reads the counts (which XCDs have members).  In round
+// r member w stores r + 1 to its data line and afterwards loads member
+// (w + 1) mod N's; stale[w] counts the loads that returned less than r + 1.
+// scratch (int32 words, zeroed by the caller): stripes [0, 64 lines), the
+// error word at line 64, XCD flags at lines 65..72, XCD counts at lines
+// 73..80, then one data line per member.
+namespace {
+constexpr int kFpErrLine = CCB_STRIPES, kFpFlagLine = CCB_STRIPES + 1;
+constexpr int kFpRegLine = CCB_STRIPES + 9, kFpDataLine = CCB_STRIPES + 17;
+}  // namespace
+
+template <int kVariant>
+__global__ __launch_bounds__(1024) void ccb_k_fence_placement(int32_t* scratch, int32_t* stale,
+                                                               int32_t rounds, uint32_t maxPoll)
+{
+    constexpr int W = CCB_LINE_WORDS;
+    __shared__ int32_t result;
+    __shared__ int32_t shRank, shMask;
+    const int32_t n = gridDim.x, w = blockIdx.x;
+    const int lane = (int)__lane_id();
+    int32_t* const ws = scratch;
+    int32_t* const err = scratch + kFpErrLine * W;
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20) & 7u;  // XCC_ID
+    constexpr bool kLeaders = kVariant >= 4;
+    if constexpr (kLeaders) {
+        if (threadIdx.x == 0)
+            shRank = __hip_atomic_fetch_add(scratch + (kFpRegLine + xcc) * W, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+        if (ccb_barrier<CCB_STRIPES, CCB_VIS_ORDER>(ws, n, w, maxPoll, err) != CCB_OK) return;
+        if (threadIdx.x < kWave) {
+            const int32_t c = lane < 8 ? __hip_atomic_load(scratch + (kFpRegLine + lane) * W,
+                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                       : 0;
+            const uint64_t m = __ballot(c > 0);
+            if (threadIdx.x == 0) shMask = (int32_t)m;
+        }
+        __syncthreads();
+    }
+    const bool lead = kLeaders && shRank == 0;
+    const uint32_t mask = kLeaders ? (uint32_t)shMask : 0u;
+    int32_t* const mine = scratch + (kFpDataLine + w) * W;
+    const int32_t* const next = scratch + (kFpDataLine + (w + 1) % n) * W;
+    int32_t bad = 0;
+    for (int32_t r = 0; r < rounds; ++r) {
+        if (threadIdx.x == 0) *mine = r + 1;  // plain store
+        ccb_wait_memory();
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            int32_t before = 0, rc;
+            if constexpr (kVariant == 1 || kVariant == 2) {
+                if (threadIdx.x == 0) before = ccb_arrive<CCB_STRIPES, CCB_VIS_FULL>(ws, w);
+            } else {
+                if (threadIdx.x == 0) before = ccb_arrive<CCB_STRIPES, CCB_VIS_ORDER>(ws, w);
+            }
+            if constexpr (kVariant == 1 || kVariant == 3)
+                rc = ccb_await<CCB_STRIPES, CCB_VIS_FULL>(ws, n, w, before, maxPoll, err);
+            else
+                rc = ccb_await<CCB_STRIPES, CCB_VIS_ORDER>(ws, n, w, before, maxPoll, err);
+            if constexpr (kLeaders) {
+                // the second phase: every member's stores are in its XCD's L2
+                const int32_t epoch = r + 2;  // the registration used round 1
+                if (rc == CCB_OK && lead) {
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                    if (threadIdx.x == 0)
+                        __hip_atomic_store(scratch + (kFpFlagLine + xcc) * W, epoch, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
+                bool done = rc != CCB_OK || lane >= 8 || ((mask >> lane) & 1u) == 0;
+                uint32_t polls = 0;
+                const int32_t* flag = scratch + (kFpFlagLine + (lane < 8 ? lane : 0)) * W;
+                while (!__all(done)) {
+                    const int32_t v = __hip_atomic_load(const_cast<int32_t*>(flag), __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+                    done = done || v >= epoch;
+                    if (__all(done)) break;
+                    if (++polls >= maxPoll) {
+                        rc = CCB_ERR_DEADLOCK;
+                        if (lane == 0)
+                            __hip_atomic_store(err, rc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    if ((polls % CCB_ERR_CHECK_EVERY) == 0) {
+                        const int32_t e =
+                            __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (e != CCB_OK) {
+                            rc = e;
+                            break;
+                        }
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                if constexpr (kVariant == 4) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                if constexpr (kVariant == 5) asm volatile("buffer_inv sc0" ::: "memory");
+            }
+            if (threadIdx.x == 0) result = rc;
+        }
+        __syncthreads();
+        if (result != CCB_OK) break;
+        if (threadIdx.x == 0 && *next < r + 1) ++bad;  // plain load
+    }
+    if (threadIdx.x == 0) stale[w] = bad;
+}
+
 // HIP's own grid barrier (cooperative groups' grid sync), `rounds` times in a
 // row: the platform's stock answer to the same problem, timed beside ours.
 // Workgroup 0 writes `rounds` to *done once it has passed the last one.
@@ -1553,6 +1674,20 @@ hipError_t launch_hip_grid_sync(int32_t rounds, int32_t nGrid, int32_t threads, 
     if ((int64_t)perCU * numCUs < nGrid) return hipErrorCooperativeLaunchTooLarge;
     void* args[] = {&rounds, &done};
     return hipLaunchCooperativeKernel(fn, dim3(nGrid), dim3(threads), args, 0, s);
+}
+
+hipError_t launch_fence_placement(int32_t* scratch, int32_t* stale, int32_t rounds, int32_t nGrid,
+                                  int32_t threads, int32_t variant, uint32_t maxPoll, hipStream_t s)
+{
+    const void* fns[] = {
+        reinterpret_cast<const void*>(&ccb_k_fence_placement<0>),
+        reinterpret_cast<const void*>(&ccb_k_fence_placement<1>),
+        reinterpret_cast<const void*>(&ccb_k_fence_placement<2>),
+        reinterpret_cast<const void*>(&ccb_k_fence_placement<3>),
+        reinterpret_cast<const void*>(&ccb_k_fence_placement<4>),
+        reinterpret_cast<const void*>(&ccb_k_fence_placement<5>)};
+    void* args[] = {&scratch, &stale, &rounds, &maxPoll};
+    return hipLaunchCooperativeKernel(fns[variant], dim3(nGrid), dim3(threads), args, 0, s);
 }
 
 hipError_t launch_copy(int4* dst, const int4* src, int64_t n16, int nBlocks, hipStream_t s)

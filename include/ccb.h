@@ -415,6 +415,35 @@ CCB_API ccbStatus ccb_bench_notify_pingpong(int32_t* lines, uint64_t* ticksOut, 
                                            int32_t peer, uint32_t maxPoll, int32_t* err,
                                            ccbStream stream);
 
+/* Where a full-visibility barrier's cache maintenance can go (measurement,
+ * not on the pages).  nGrid workgroups (at most one per compute unit) run
+ * `rounds` barriers on the striped counter; before each, thread 0 of member w
+ * stores r + 1 to its data line with a plain store, and after it loads member
+ * (w + 1) mod nGrid's with a plain load.  `variant` places the agent-scope
+ * release (L2 write-back) and acquire (invalidate):
+ *   0  none (the ordering-only barrier)
+ *   1  every workgroup: release before its arrival, acquire after its poll
+ *      (what CCB_VISIBILITY_FULL does)
+ *   2  every workgroup: release only
+ *   3  every workgroup: acquire only
+ *   4  one release per XCD: once all members have arrived, one leader
+ *      workgroup per XCD (the first to register its XCC id at the start)
+ *      writes back its L2 and raises a flag; every workgroup waits for the
+ *      flags of the XCDs that hold members, then acquires
+ *   5  as 4, with a workgroup-scope invalidate (buffer_inv sc0) as each
+ *      workgroup's acquire
+ *   scratch       device, scratchBytes >= ccb_bench_fence_placement_bytes(nGrid),
+ *                 128-B aligned (zeroed here by a fill kernel)
+ *   stale         device, nGrid int32: per member, the loads that returned an
+ *                 older value than the round's
+ * The caller times launches (e.g. two round counts).  Every wait is bounded
+ * by CCB_SOFT_MAX_POLL.  Errors: NULL_POINTER, INVALID_VALUE,
+ * NOT_CORESIDENT (nGrid above the CU count). */
+CCB_API size_t ccb_bench_fence_placement_bytes(int32_t nGrid);
+CCB_API ccbStatus ccb_bench_fence_placement(int32_t* scratch, size_t scratchBytes, int32_t* stale,
+                                            int32_t rounds, int32_t nGrid, int32_t threads,
+                                            int32_t variant, ccbStream stream);
+
 /* HIP's cooperative-groups grid barrier (grid_group::sync) `rounds` times in
  * one cooperative launch of nGrid workgroups of `threads` threads (a
  * multiple of 64, at most 1024): the platform's stock grid barrier, for

@@ -139,3 +139,27 @@ def test_refused_launch_leaves_no_error(ccb):
     ccb.check(ccb.ccb_bench_hip_grid_sync(3, 8, 64, done), "grid sync after refusal")
     torch.cuda.synchronize()
     assert int(done.item()) == 3
+
+
+@pytest.mark.parametrize("variant", range(6))
+def test_fence_placement_completes(ccb, variant):
+    """Every placement runs its rounds without a bounded wait giving up; the
+    two that release and acquire at agent scope for every reader (every
+    workgroup, or one write-back per XCD plus every workgroup's acquire)
+    never return a stale value to a plain read after the barrier."""
+    n, rounds = 64, 300
+    _say(f"fence placement variant {variant}: {n} x 64, {rounds} rounds")
+    nbytes = ccb.ccb_bench_fence_placement_bytes(n)
+    scratch = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    stale = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    assert ccb.ccb_bench_fence_placement(scratch, nbytes, stale, rounds, n, 64, variant) == 0
+    torch.cuda.synchronize()
+    assert int(scratch[ccb.CCB_STRIPES * 32].item()) == 0          # error word
+    s = stale.cpu().numpy()
+    assert ((s >= 0) & (s <= rounds)).all()
+    if variant in (1, 4):
+        assert (s == 0).all()
+    assert ccb.ccb_bench_fence_placement(scratch, nbytes - 4, stale, rounds, n, 64, variant) == \
+        ccb.CCB_ERR_INVALID_VALUE
+    assert ccb.ccb_bench_fence_placement(scratch, nbytes, stale, rounds, n, 64, 6) == \
+        ccb.CCB_ERR_INVALID_VALUE
