@@ -512,7 +512,29 @@ class Bench:
         data = dend.max(axis=0) - first
         barrier = (rel.max(axis=0) - dend.max(axis=0))[:-1]
         skew = dend.max(axis=0) - dend.min(axis=0)
+        # Per-workgroup data phases (its release -> its data end): how much of
+        # the finish skew is systematic per workgroup (a static assignment
+        # could remove that part) and how much is per-iteration noise.
+        begin = np.concatenate([start[:, None], rel[:, :-1]], axis=1)
+        d = (dend - begin)[:, 2:]  # from the third iteration on
+        mu = d.mean(axis=1)
+        half = d.shape[1] // 2
+        dispatch_round = np.arange(G) * 4 // G  # four workgroups per CU, dealt in order
+        equalised = d * (mu.mean() / mu)[:, None]
+        skew_model = {
+            "per_workgroup_mean_us": {"min": round(float(mu.min()) / 1e3, 2),
+                                      "median": round(float(np.median(mu)) / 1e3, 2),
+                                      "max": round(float(mu.max()) / 1e3, 2)},
+            "split_half_correlation": round(float(np.corrcoef(d[:, :half].mean(1),
+                                                              d[:, half:].mean(1))[0, 1]), 3),
+            "within_workgroup_std_us": round(float(np.median(d.std(axis=1))) / 1e3, 2),
+            "by_dispatch_round_mean_us": [round(float(mu[dispatch_round == r].mean()) / 1e3, 2)
+                                          for r in range(4)],
+            "mean_of_iteration_max_us": round(float(d.max(axis=0).mean()) / 1e3, 2),
+            # every workgroup's work scaled by its own measured speed
+            "ideal_static_rebalance_max_us": round(float(equalised.max(axis=0).mean()) / 1e3, 2)}
         self.extra["stencil_phases"] = {
+            "skew_model": skew_model,
             "data_phase_us_mean": round(float(data.mean()) / 1e3, 2),
             "data_phase_GBs": round(STENCIL_BYTES_PER_ITER / float(data.mean()), 1),
             "data_phase_frac_of_peak": round(STENCIL_BYTES_PER_ITER / float(data.mean()) / HBM_PEAK_GBS, 4),
