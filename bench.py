@@ -283,6 +283,11 @@ class Bench:
             composed = floor["fetch_add_ns"] + other
             roof.update({"notify_one_way_ns": other, "composed_floor_ns": round(composed, 1),
                          "ratio_to_composed_floor": round(best / composed, 2)})
+        # the public device API's default, full visibility, beside it
+        full = lat["striped-full"]
+        roof["full_visibility"] = {"achieved_ns_per_barrier": full,
+                                   "ratio": round(full / floor["fetch_add_ns"], 2),
+                                   "ratio_to_ordering_only": round(full / best, 2)}
         self.extra["latency_roofline"] = roof
         log(f"barrier-only ns/barrier at 256 WGs: {lat}")
 

@@ -66,7 +66,32 @@ __attribute__((visibility("default"))) int ccb_capi_example(char* msg, int msgLe
                                  CCB_BARRIER_STRIPED | CCB_VISIBILITY_ORDER, consumer));
     int64_t arrivals = 0;
     CCB_TRY(ccb_syncall_status(ws, 1, &arrivals, consumer));
+    /* the same rounds on the two-level arrival tree */
+    int64_t treeArrivals = 0;
+    CCB_TRY(ccb_syncall_workspace_reset(ws, 1, consumer));
+    CCB_TRY(ccb_run_barrier_only(ws, NULL, NULL, 100, 8, 64, 0, 0, 0,
+                                 CCB_BARRIER_TREE | CCB_VISIBILITY_ORDER, consumer));
+    CCB_TRY(ccb_syncall_status(ws, 1, &treeArrivals, consumer));
     HIP_TRY(hipFree(ws));
+    if (treeArrivals != 800) {
+        snprintf(msg, (size_t)msgLen, "tree barrier: %lld arrivals, expected 800",
+                 (long long)treeArrivals);
+        return 1;
+    }
+
+    /* a wait nothing will satisfy, ended from the host */
+    ccbCntNotify h2;
+    CCB_TRY(ccb_cnt_notify_create(&h2, 0));
+    ccbCntWaitInfo never = {CCB_CNT_WAIT_BIGGER_OR_EQUAL, 1, 5 /* s */, 0, {0, 0, 0}};
+    CCB_TRY(ccb_cnt_notify_wait(h2, consumer, &never));
+    CCB_TRY(ccb_cnt_notify_abort(h2));
+    ccbStatus aborted = CCB_OK;
+    CCB_TRY(ccb_cnt_notify_query(h2, NULL, &aborted, consumer));
+    CCB_TRY(ccb_cnt_notify_destroy(h2));
+    if (aborted != CCB_ERR_CANCELLED) {
+        snprintf(msg, (size_t)msgLen, "abort: last wait %d, expected CANCELLED", (int)aborted);
+        return 1;
+    }
     HIP_TRY(hipStreamDestroy(producer));
     HIP_TRY(hipStreamDestroy(consumer));
     if (arrivals != 800) {
@@ -138,13 +163,32 @@ __attribute__((visibility("default"))) int ccb_capi_example(char* msg, int msgLe
             snprintf(msg, (size_t)msgLen, "stencil: element %d is %d", i, (int)hy[i]);
             return 1;
         }
+    /* the same stencil through the entry point that allocates nothing: no
+     * workspace, no halo; its outcome lands in a device word */
+    int32_t* dstatus = NULL;
+    HIP_TRY(hipMalloc((void**)&dstatus, sizeof(int32_t)));
+    HIP_TRY(hipMemcpy(da, hx, sizeof(hx), hipMemcpyHostToDevice));
+    CCB_TRY(ccb_run_stencil_noalloc(da, db, N, ITERS, dstatus, GRID, THREADS, 0, 0,
+                                    CCB_BARRIER_STRIPED | CCB_VISIBILITY_ORDER, NULL));
+    int32_t hstatus = -1;
+    HIP_TRY(hipMemcpy(&hstatus, dstatus, sizeof(hstatus),
+                      hipMemcpyDeviceToHost));
+    HIP_TRY(hipMemcpy(hy, db, sizeof(hy), hipMemcpyDeviceToHost));
+    for (int i = 0; i < N; ++i)
+        if (hy[i] != 777 || hstatus != CCB_OK) {
+            snprintf(msg, (size_t)msgLen, "stencil without allocation: element %d is %d, status %d",
+                     i, (int)hy[i], (int)hstatus);
+            return 1;
+        }
+    HIP_TRY(hipFree(dstatus));
     HIP_TRY(hipFree(da));
     HIP_TRY(hipFree(db));
     HIP_TRY(hipFree(dws));
     HIP_TRY(hipFree(dhalo));
 
     snprintf(msg, (size_t)msgLen,
-             "released and cleared (id %u); 800 arrivals; batch of %d released; stencil fixed point",
+             "released and cleared (id %u); 800 arrivals (stripes and tree); a wait aborted; "
+             "batch of %d released; stencil fixed point, also without allocation",
              id, NC);
     return 0;
 }
