@@ -280,14 +280,17 @@ ccbCntNotify encode_handle(uint32_t idx, uint32_t gen)
 struct CntRef {
     uint32_t idx;
     uint32_t* pair;         // device: count, then outcome
-    uint32_t* cancelHost;   // host view of the line's cancel token
-    const uint32_t* cancelDev;
+    const uint32_t* cancelDev;  // device view of the line's cancel token
+    uint32_t token;             // its value at the lookup
 };
 
 // Looks a handle up.  `kill` also marks the slot free, under the same lock
 // as the check, so that of two concurrent destroys of one handle only one
-// succeeds.
-ccbStatus resolve(ccbCntNotify h, CntRef* ref, bool kill = false)
+// succeeds.  `cancel` ends the waits enqueued so far on the line (they see
+// a new token); it too happens under the lock, before a destroyed line can
+// go back to the free list, so that a wait of the line's next owner never
+// carries the old token.
+ccbStatus resolve(ccbCntNotify h, CntRef* ref, bool kill = false, bool cancel = false)
 {
     const uintptr_t v = reinterpret_cast<uintptr_t>(h);
     if (v == 0) return CCB_ERR_INVALID_HANDLE;
@@ -301,6 +304,7 @@ ccbStatus resolve(ccbCntNotify h, CntRef* ref, bool kill = false)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hip_failed();
     if (dev != s.device) return CCB_ERR_INVALID_HANDLE;
+    if (cancel) __atomic_fetch_add(g_cnt_cancel[s.device] + idx, 1u, __ATOMIC_RELEASE);
     if (kill) {
         s.alive = false;
         g_cnt_free.push(idx);
@@ -308,14 +312,11 @@ ccbStatus resolve(ccbCntNotify h, CntRef* ref, bool kill = false)
     if (ref != nullptr) {
         ref->idx = idx;
         ref->pair = g_cnt_pool[s.device] + (size_t)idx * kLineWords + 2 * (s.gen % kGenPairs);
-        ref->cancelHost = g_cnt_cancel[s.device] + idx;
         ref->cancelDev = g_cnt_cancel_dev[s.device] + idx;
+        ref->token = __atomic_load_n(g_cnt_cancel[s.device] + idx, __ATOMIC_ACQUIRE);
     }
     return CCB_OK;
 }
-
-// Ends the waits enqueued so far on a line: they see a new token.
-void cancel_waits(const CntRef& ref) { __atomic_fetch_add(ref.cancelHost, 1u, __ATOMIC_RELEASE); }
 
 }  // namespace
 
@@ -782,9 +783,8 @@ CCB_API ccbStatus ccb_cnt_notify_wait(ccbCntNotify h, ccbStream stream, const cc
     st = current_device(nullptr, &dinfo);
     if (st != CCB_OK) return st;
     const uint64_t ticks = (uint64_t)info->timeout * (uint64_t)dinfo.wallClockKHz * 1000ull;
-    const uint32_t token = __atomic_load_n(ref.cancelHost, __ATOMIC_ACQUIRE);
     return from_hip(ccb::launch_cnt_wait(ref.pair, info->mode, info->value, info->isClear, ticks,
-                                         ref.cancelDev, token, (hipStream_t)stream));
+                                         ref.cancelDev, ref.token, (hipStream_t)stream));
 }
 
 CCB_API ccbStatus ccb_cnt_notify_reset(ccbCntNotify h, ccbStream stream)
@@ -807,20 +807,13 @@ CCB_API ccbStatus ccb_cnt_notify_get_id(ccbCntNotify h, uint32_t* id)
 
 CCB_API ccbStatus ccb_cnt_notify_abort(ccbCntNotify h)
 {
-    CntRef ref;
-    ccbStatus st = resolve(h, &ref);
-    if (st != CCB_OK) return st;
-    cancel_waits(ref);
-    return CCB_OK;
+    return resolve(h, nullptr, false, true);
 }
 
 CCB_API ccbStatus ccb_cnt_notify_destroy(ccbCntNotify h)
 {
-    CntRef ref;
-    ccbStatus st = resolve(h, &ref, true);
-    if (st != CCB_OK) return st;
-    cancel_waits(ref);  // a wait still queued for the handle ends instead of spinning
-    return CCB_OK;
+    // a wait still queued for the handle ends instead of spinning
+    return resolve(h, nullptr, true, true);
 }
 
 CCB_API ccbStatus ccb_cnt_notify_query(ccbCntNotify h, uint32_t* value, ccbStatus* lastWait,

@@ -420,6 +420,15 @@ __device__ __forceinline__ int32_t ccb_syncall_soft_mix(int32_t* ws, int32_t gro
                                                   ws + CCB_STRIPES * CCB_LINE_WORDS);
 }
 
+/* The two-level arrival tree (CCB_TREE_GROUPS group counters under one top
+ * counter, see ccb_tree), full visibility; same workspace layout. */
+__device__ __forceinline__ int32_t ccb_syncall_soft_tree(int32_t* ws, int32_t usedCores)
+{
+    const int32_t n = usedCores != 0 ? usedCores : (int32_t)(gridDim.x * gridDim.y * gridDim.z);
+    return ccb_barrier<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_FULL>(
+        ws, n, ccb_block_linear(), CCB_SOFT_MAX_POLL, ws + CCB_STRIPES * CCB_LINE_WORDS);
+}
+
 /* The pages' single-counter barrier exactly (one counter line, full
  * visibility); same workspace layout, only stripe 0 is used. */
 __device__ __forceinline__ int32_t ccb_syncall_soft_flat(int32_t* ws, int32_t usedCores)

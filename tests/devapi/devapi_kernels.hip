@@ -2,7 +2,8 @@
 // the way a caller's own kernel would use it: the flag-slot pattern of the
 // SYNCALL guide §6.1 (write own slot, barrier, read every member's slot)
 // over a 2-D grid, with ccb_syncall_soft, ccb_syncall_soft_ordered,
-// ccb_syncall_soft_flat, ccb_syncall_soft_bounded or ccb_syncall_soft_mix
+// ccb_syncall_soft_flat, ccb_syncall_soft_tree, ccb_syncall_soft_bounded or
+// ccb_syncall_soft_mix
 // (role groups of one leader and 1 or 2 companions; usedCores then counts
 // groups), or the split-phase pair ccb_arrive / ccb_await with the kernel's
 // own workgroup barriers and work between the two halves.  Test code only: the
@@ -78,7 +79,8 @@ __global__ __launch_bounds__(1024) void devapi_rounds(int32_t* ws, uint32_t* slo
             if (rc == CCB_OK && tid == 0 && r + 1 < rounds &&
                 nextWitness != devapi_witness(seed, (uint32_t)(r + 1), (uint32_t)w))
                 rc = CCB_ERR_INVALID_VALUE;  // the overlapped work went wrong
-        } else rc = ccb_syncall_soft_mix(ws, usedCores, ratio);
+        } else if (kVariant == 7) rc = ccb_syncall_soft_tree(ws, usedCores);
+        else rc = ccb_syncall_soft_mix(ws, usedCores, ratio);
         if (rc != CCB_OK) break;
         uint32_t s = 0;
         for (int32_t i = (int32_t)tid; i < n; i += (int32_t)blockDim.x)
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(1024) void devapi_rounds(int32_t* ws, uint32_t* slo
 
 }  // namespace
 
-// Launches variant 0..6 cooperatively on a gx x gy grid of `threads`
+// Launches variant 0..7 cooperatively on a gx x gy grid of `threads`
 // threads (a multiple of 64, at most 1024).  slots: 2 * gx * gy uint32;
 // out: rounds * gx * gy uint32; status: gx * gy int32.  Returns a hipError_t.
 extern "C" int devapi_run(int variant, int32_t* ws, uint32_t* slots, uint32_t* out, int32_t* status,
@@ -108,18 +110,18 @@ extern "C" int devapi_run(int variant, int32_t* ws, uint32_t* slots, uint32_t* o
     const bool mix = variant == 4 || variant == 5;
     const int32_t members = mix ? ccb_mix_participants(usedCores, variant == 4 ? 1 : 2, gx * gy)
                                 : usedCores;
-    if (variant < 0 || variant > 6 || threads < 64 || threads > 1024 || threads % 64 != 0 ||
+    if (variant < 0 || variant > 7 || threads < 64 || threads > 1024 || threads % 64 != 0 ||
         gx < 1 || gy < 1 || usedCores < 0 || members > gx * gy)
         return (int)hipErrorInvalidValue;
     // every buffer is written by the kernel: never launch with a missing one
     if (ws == nullptr || slots == nullptr || out == nullptr || status == nullptr)
         return (int)hipErrorInvalidValue;
     void* args[] = {&ws, &slots, &out, &status, &seed, &rounds, &usedCores, &maxPoll};
-    const void* const fns[7] = {
+    const void* const fns[8] = {
         reinterpret_cast<const void*>(&devapi_rounds<0>), reinterpret_cast<const void*>(&devapi_rounds<1>),
         reinterpret_cast<const void*>(&devapi_rounds<2>), reinterpret_cast<const void*>(&devapi_rounds<3>),
         reinterpret_cast<const void*>(&devapi_rounds<4>), reinterpret_cast<const void*>(&devapi_rounds<5>),
-        reinterpret_cast<const void*>(&devapi_rounds<6>)};
+        reinterpret_cast<const void*>(&devapi_rounds<6>), reinterpret_cast<const void*>(&devapi_rounds<7>)};
     const void* fn = fns[variant];
     return (int)hipLaunchCooperativeKernel(fn, dim3(gx, gy), dim3(threads), args, 0, stream);
 }
