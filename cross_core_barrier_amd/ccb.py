@@ -50,18 +50,25 @@ CCB_SLOT_WORDS = 4
 CCB_CNT_NOTIFY_POOL = 1024
 
 CCB_BARRIER_STRIPED, CCB_BARRIER_FLAT, CCB_BARRIER_TREE = 0, 1, 4
-CCB_VISIBILITY_ORDER, CCB_VISIBILITY_FULL = 0, 2
+CCB_VISIBILITY_ORDER, CCB_VISIBILITY_FULL, CCB_VISIBILITY_XCD = 0, 2, 8
 CCB_TREE_GROUPS = 8
 MODES = {
     "striped-order": CCB_BARRIER_STRIPED | CCB_VISIBILITY_ORDER,
     "striped-full": CCB_BARRIER_STRIPED | CCB_VISIBILITY_FULL,
+    "striped-xcd": CCB_BARRIER_STRIPED | CCB_VISIBILITY_XCD,
     "flat-order": CCB_BARRIER_FLAT | CCB_VISIBILITY_ORDER,
     "flat-full": CCB_BARRIER_FLAT | CCB_VISIBILITY_FULL,
+    "flat-xcd": CCB_BARRIER_FLAT | CCB_VISIBILITY_XCD,
     "tree-order": CCB_BARRIER_TREE | CCB_VISIBILITY_ORDER,
     "tree-full": CCB_BARRIER_TREE | CCB_VISIBILITY_FULL,
+    "tree-xcd": CCB_BARRIER_TREE | CCB_VISIBILITY_XCD,
 }
 # word of a one-barrier workspace that holds the tree's top counter
 CCB_TREE_TOP_WORD = (CCB_STRIPES - 1) * (CCB_LINE_BYTES // 4) + CCB_LINE_BYTES // 8
+# words of a barrier's workspace that the per-XCD write-back uses: members
+# registered per XCD, and the last round each XCD's leader wrote back
+CCB_XCD_COUNT_WORD = 1 * (CCB_LINE_BYTES // 4) + 8
+CCB_XCD_FLAG_WORD = 2 * (CCB_LINE_BYTES // 4) + 8
 
 CCB_CNT_RECORD_SET_VALUE, CCB_CNT_RECORD_ADD, CCB_CNT_RECORD_BIT_OR, CCB_CNT_RECORD_BIT_AND = 0, 1, 2, 4
 (CCB_CNT_WAIT_LESS, CCB_CNT_WAIT_EQUAL, CCB_CNT_WAIT_BIGGER, CCB_CNT_WAIT_BIGGER_OR_EQUAL,

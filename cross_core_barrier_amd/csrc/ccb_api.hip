@@ -92,15 +92,27 @@ inline bool valid_threads(int32_t threads)
 
 // Dynamic LDS that keeps at most wgsPerCu workgroups on one CU, and the check
 // that nGrid workgroups fit on the device at once (SYNCALL guide §6.3).
+// A mode is one counter layout (striped, flat or tree) ORed with one
+// visibility (order, full or per-XCD write-back).
 inline bool valid_mode(int32_t mode)
 {
-    return (mode >= 0 && mode <= 3) || mode == (CCB_BARRIER_TREE | CCB_VISIBILITY_ORDER) ||
-           mode == (CCB_BARRIER_TREE | CCB_VISIBILITY_FULL);
+    const int32_t layout = mode & (CCB_BARRIER_FLAT | CCB_BARRIER_TREE);
+    const int32_t vis = mode & ~(CCB_BARRIER_FLAT | CCB_BARRIER_TREE);
+    return mode >= 0 && layout != (CCB_BARRIER_FLAT | CCB_BARRIER_TREE) &&
+           (vis == CCB_VISIBILITY_ORDER || vis == CCB_VISIBILITY_FULL || vis == CCB_VISIBILITY_XCD);
+}
+
+// The barrier shares data through device-coherent accesses (no fences).
+inline bool order_only(int32_t mode)
+{
+    return (mode & (CCB_VISIBILITY_FULL | CCB_VISIBILITY_XCD)) == 0;
 }
 
 // Every valid mode, for the register query.
-constexpr int32_t kModes[] = {0, 1, 2, 3, CCB_BARRIER_TREE, CCB_BARRIER_TREE | CCB_VISIBILITY_FULL};
-constexpr int kModeSlots = 8;  // mode values 0..7 index the query table
+constexpr int32_t kModes[] = {0, 1, 2, 3, CCB_BARRIER_TREE, CCB_BARRIER_TREE | CCB_VISIBILITY_FULL,
+                              CCB_VISIBILITY_XCD, CCB_BARRIER_FLAT | CCB_VISIBILITY_XCD,
+                              CCB_BARRIER_TREE | CCB_VISIBILITY_XCD};
+constexpr int kModeSlots = 16;  // mode values 0..15 index the query table
 
 // Waves per SIMD that a persistent kernel's SGPR allocation allows.  The
 // occupancy API counts only the kernel's own SGPRs.  On MI355X each wave also
@@ -556,7 +568,7 @@ CCB_API ccbStatus ccb_run_stencil(int32_t* bufA, int32_t* bufB, int64_t n, int32
                                   ccbStream stream)
 {
     if (bufA == nullptr || bufB == nullptr || ws == nullptr) return CCB_ERR_NULL_POINTER;
-    const bool needHalo = valid_mode(mode) && (mode & CCB_VISIBILITY_FULL) == 0;
+    const bool needHalo = valid_mode(mode) && order_only(mode);
     if (needHalo && halo == nullptr) return CCB_ERR_NULL_POINTER;
     if (!stencil_args_ok(bufA, bufB, n, iters, nGrid, threads, wgsPerCu, mode) ||
         !aligned(ws, CCB_LINE_BYTES) || (halo != nullptr && !aligned(halo, 4)) ||
@@ -584,7 +596,7 @@ CCB_API ccbStatus ccb_run_stencil_noalloc(int32_t* bufA, int32_t* bufB, int64_t 
     // the scratch: the workspace of one barrier (padded to 256 B), then the
     // halo buffer, which only the ordering-only barrier uses
     const size_t wsBytes = (ccb_syncall_workspace_bytes(1) + 255) / 256 * 256;
-    const bool needHalo = (mode & CCB_VISIBILITY_FULL) == 0;
+    const bool needHalo = order_only(mode);
     const size_t haloBytes = needHalo ? ccb_stencil_halo_bytes(n, threads, nGrid) : 0;
     if (wsBytes + haloBytes > CCB_NOALLOC_SCRATCH_BYTES) return CCB_ERR_INVALID_VALUE;
     int dev = 0;

@@ -153,6 +153,7 @@ __global__ __launch_bounds__(1024) void ccb_k_barrier_only(int32_t* ws, uint32_t
     int32_t* err = ws + CCB_STRIPES * CCB_LINE_WORDS;
     int32_t rc = CCB_OK;
     int32_t done = 0;
+    ccb_xcd_team team = {};
     // Rounds follow each other with nothing in between, so the workgroup
     // barrier that releases round r also orders round r + 1's arrival: one
     // per round.  The result word alternates so that wave 0 can publish
@@ -163,12 +164,12 @@ __global__ __launch_bounds__(1024) void ccb_k_barrier_only(int32_t* ws, uint32_t
             int32_t e;
             if constexpr (kStamps) {
                 if (leader()) lds[3 * r] = wall_clock64();
-                if (leader()) before = ccb_arrive<K, V>(ws, w);
+                if (leader()) before = ccb_arrive<K, V>(ws, w, team);
                 e = ccb_await<K, V>(ws, nMembers, w, before, maxPoll, err,
-                                    StampHook{&lds[3 * r + 1], &lds[3 * r + 2]});
+                                    StampHook{&lds[3 * r + 1], &lds[3 * r + 2]}, team);
             } else {
-                if (leader()) before = ccb_arrive<K, V>(ws, w);
-                e = ccb_await<K, V>(ws, nMembers, w, before, maxPoll, err);
+                if (leader()) before = ccb_arrive<K, V>(ws, w, team);
+                e = ccb_await<K, V>(ws, nMembers, w, before, maxPoll, err, ccb_no_hook(), team);
             }
             if (leader()) result[r & 1] = e;
         }
@@ -393,11 +394,12 @@ __global__ __launch_bounds__(1024) void ccb_k_slot_rounds(int32_t* ws, uint32_t*
     }
     int32_t* err = ws + CCB_STRIPES * CCB_LINE_WORDS;
     int32_t rc = CCB_OK;
-    if constexpr (V == CCB_VIS_FULL) {
+    if constexpr (V != CCB_VIS_ORDER) {
+        ccb_xcd_team team = {};
         for (int32_t r = 0; r < rounds; ++r) {
             uint32_t* row = slots + (size_t)(r % kRing) * nGrid * kSlot;
             if (leader()) shared_store<V>(row + (size_t)w * kSlot, witness(seed, (uint32_t)r, (uint32_t)w));
-            rc = ccb_barrier<K, V>(ws, nMembers, w, maxPoll, err);
+            rc = ccb_barrier<K, V>(ws, nMembers, w, maxPoll, err, team);
             if (rc != CCB_OK) break;
             uint32_t s = 0;
             for (int32_t i = threadIdx.x; i < nMembers; i += blockDim.x)
@@ -464,7 +466,10 @@ __global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32
     int32_t* err = ws + 3 * CCB_STRIPES * CCB_LINE_WORDS;
     int32_t rc = CCB_OK;
     auto member_of = [&](int32_t r) { return (r % 3) == 2 || (r % 3) == parity; };
-    if constexpr (V == CCB_VIS_FULL) {
+    if constexpr (V != CCB_VIS_ORDER) {
+        // a member takes part in its own group's barrier and the mixed one;
+        // the two states stay in registers (an indexed array would not)
+        ccb_xcd_team tGroup = {}, tMix = {};
         int32_t own = 0;  // this member's rounds so far
         for (int32_t r = 0; r < rounds; ++r) {
             const int32_t kind = r % 3;
@@ -473,7 +478,12 @@ __global__ __launch_bounds__(1024) void ccb_k_grouped_rounds(int32_t* ws, uint32
             if (leader()) shared_store<V>(row + (size_t)pos * kSlot, witness(seed, (uint32_t)r, (uint32_t)w));
             const int32_t n = kind == 2 ? nGrid : half;
             const int32_t member = kind == 2 ? w : (w >> 1);
-            rc = ccb_barrier<K, V>(ws + kind * CCB_STRIPES * CCB_LINE_WORDS, n, member, maxPoll, err);
+            auto bar = [&](ccb_xcd_team& team) {
+                return ccb_barrier<K, V>(ws + kind * CCB_STRIPES * CCB_LINE_WORDS, n, member,
+                                         maxPoll, err, team);
+            };
+            if constexpr (V == CCB_VIS_XCD) rc = kind == 2 ? bar(tMix) : bar(tGroup);
+            else rc = bar(tGroup);  // stateless: one copy of the barrier
             if (rc != CCB_OK) break;
             if constexpr (kStamps) {
                 if (leader()) RoundStamps{stampLds, CCB_BREAKDOWN_MAX_ROUNDS}(own);
@@ -760,6 +770,7 @@ __global__ __launch_bounds__(1024) void ccb_k_stencil(int32_t* bufA, int32_t* bu
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int nWave = blockDim.x / kWave;
     int32_t* err = ws + CCB_STRIPES * CCB_LINE_WORDS;
+    ccb_xcd_team team = {};
     // timeline (optional): per workgroup, the start, then for every iteration
     // the end of its data phase and the moment it left the following barrier
     uint64_t* stamps = timeline != nullptr ? timeline + (size_t)g.w * (2 * (size_t)iters + 1) : nullptr;
@@ -769,7 +780,7 @@ __global__ __launch_bounds__(1024) void ccb_k_stencil(int32_t* bufA, int32_t* bu
         int32_t* y = (t & 1) ? bufA : bufB;
         const bool publish = V == CCB_VIS_ORDER && t + 1 < iters;
         const int pIn = (t - 1) & 1, pOut = t & 1;
-        if (V == CCB_VIS_FULL || t == 0) {
+        if (V != CCB_VIS_ORDER || t == 0) {
             stencil_sweep<HaloSrc::Direct>(g, x, y, nullptr, nullptr, halo, pIn,
                                            publish && staged ? outFirst : nullptr,
                                            publish && staged ? outLast : nullptr,
@@ -818,7 +829,7 @@ __global__ __launch_bounds__(1024) void ccb_k_stencil(int32_t* bufA, int32_t* bu
                     g.myChunks > 0 && (g.w + (g.myChunks - 1) * g.G) >= g.nFullChunks;
                 if (wave == 0 || wave == nWave - 1 || partial || !staged) ccb_wait_memory();
             }
-            if (ccb_barrier<K, V, false>(ws, (int32_t)g.G, (int32_t)g.w, maxPoll, err) != CCB_OK)
+            if (ccb_barrier<K, V, false>(ws, (int32_t)g.G, (int32_t)g.w, maxPoll, err, team) != CCB_OK)
                 break;
         }
         if (stamps != nullptr && threadIdx.x == 0) stamps[2 + 2 * t] = wall_clock64();
@@ -1105,7 +1116,7 @@ __global__ __launch_bounds__(256) void ccb_k_cnt_batch(const uint32_t* __restric
 __global__ void ccb_k_cnt_record(uint32_t* line, int32_t mode, uint32_t value)
 {
     if (!leader()) return;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    ccb_fence_release_agent();
     switch (mode) {
     case CCB_CNT_RECORD_SET_VALUE:
         __hip_atomic_exchange(line, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1171,7 +1182,7 @@ __global__ void ccb_k_cnt_wait(uint32_t* line, int32_t mode, uint32_t value, int
 __global__ void ccb_k_cnt_reset(uint32_t* line)
 {
     if (!leader()) return;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    ccb_fence_release_agent();
     __hip_atomic_store(line, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1207,14 +1218,14 @@ __global__ void ccb_k_atomic_chain(int32_t* line, uint64_t* ticks, int32_t iters
     const uint64_t t0 = wall_clock64();
     if (kind == 0) {
         for (int32_t i = 0; i < iters; ++i) {
-            if (fenced) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            if (fenced) ccb_fence_release_agent();
             v = __hip_atomic_fetch_add(line + (v & zero), 1, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
             if (fenced) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
     } else {
         for (int32_t i = 0; i < iters; ++i) {
-            if (fenced) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            if (fenced) ccb_fence_release_agent();
             v = __hip_atomic_load(line + (v & zero), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (fenced) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
@@ -1360,7 +1371,7 @@ __global__ __launch_bounds__(1024) void ccb_k_fence_placement(int32_t* scratch, 
                 // the second phase: every member's stores are in its XCD's L2
                 const int32_t epoch = r + 2;  // the registration used round 1
                 if (rc == CCB_OK && lead) {
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                    ccb_fence_release_agent();
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                     if (threadIdx.x == 0)
                         __hip_atomic_store(scratch + (kFpFlagLine + xcc) * W, epoch, __ATOMIC_RELAXED,
@@ -1438,31 +1449,45 @@ static hipError_t coop(const void* fn, int nGrid, int threads, size_t lds, hipSt
     return hipLaunchCooperativeKernel(fn, dim3(nGrid), dim3(threads), args, (unsigned)lds, s);
 }
 
-#define CCB_PICK_X(kernel, mode, x)                                                                  \
-    ((mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_ORDER)                                     \
-         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_ORDER, x>)                 \
-     : (mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_FULL)                                    \
-         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_FULL, x>)                  \
-     : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_ORDER)                                      \
-         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_ORDER, x>)                           \
-     : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_FULL)                                       \
-         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_FULL, x>)                            \
-     : (mode) == (CCB_BARRIER_TREE | CCB_VISIBILITY_ORDER)                                      \
-         ? reinterpret_cast<const void*>(&kernel<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_ORDER, x>)   \
-         : reinterpret_cast<const void*>(&kernel<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_FULL, x>))
+// Each mode's kernel instance (an invalid mode falls through to the last;
+// the entry points reject invalid modes first).
+#define CCB_PICK_X(kernel, mode, x)                                                            \
+    ((mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_ORDER)                                    \
+         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_ORDER, x>)               \
+     : (mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_FULL)                                   \
+         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_FULL, x>)                \
+     : (mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_XCD)                                    \
+         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_XCD, x>)                 \
+     : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_ORDER)                                     \
+         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_ORDER, x>)                         \
+     : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_FULL)                                      \
+         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_FULL, x>)                          \
+     : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_XCD)                                       \
+         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_XCD, x>)                           \
+     : (mode) == (CCB_BARRIER_TREE | CCB_VISIBILITY_ORDER)                                     \
+         ? reinterpret_cast<const void*>(&kernel<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_ORDER, x>) \
+     : (mode) == (CCB_BARRIER_TREE | CCB_VISIBILITY_FULL)                                      \
+         ? reinterpret_cast<const void*>(&kernel<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_FULL, x>)  \
+         : reinterpret_cast<const void*>(&kernel<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_XCD, x>))
 
-#define CCB_PICK(kernel, mode)                                                                  \
-    ((mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_ORDER)                                     \
-         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_ORDER>)                 \
-     : (mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_FULL)                                    \
-         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_FULL>)                  \
-     : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_ORDER)                                      \
-         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_ORDER>)                           \
-     : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_FULL)                                       \
-         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_FULL>)                            \
-     : (mode) == (CCB_BARRIER_TREE | CCB_VISIBILITY_ORDER)                                      \
-         ? reinterpret_cast<const void*>(&kernel<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_ORDER>)   \
-         : reinterpret_cast<const void*>(&kernel<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_FULL>))
+#define CCB_PICK(kernel, mode)                                                              \
+    ((mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_ORDER)                                 \
+         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_ORDER>)               \
+     : (mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_FULL)                                \
+         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_FULL>)                \
+     : (mode) == (CCB_BARRIER_STRIPED | CCB_VISIBILITY_XCD)                                 \
+         ? reinterpret_cast<const void*>(&kernel<CCB_STRIPES, CCB_VIS_XCD>)                 \
+     : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_ORDER)                                  \
+         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_ORDER>)                         \
+     : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_FULL)                                   \
+         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_FULL>)                          \
+     : (mode) == (CCB_BARRIER_FLAT | CCB_VISIBILITY_XCD)                                    \
+         ? reinterpret_cast<const void*>(&kernel<1, CCB_VIS_XCD>)                           \
+     : (mode) == (CCB_BARRIER_TREE | CCB_VISIBILITY_ORDER)                                  \
+         ? reinterpret_cast<const void*>(&kernel<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_ORDER>) \
+     : (mode) == (CCB_BARRIER_TREE | CCB_VISIBILITY_FULL)                                   \
+         ? reinterpret_cast<const void*>(&kernel<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_FULL>)  \
+         : reinterpret_cast<const void*>(&kernel<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_XCD>))
 
 const void* kernel_ptr(KernelId id, int32_t mode)
 {

@@ -91,13 +91,19 @@ enum {
  *                         device-coherent accesses
  *   CCB_VISIBILITY_FULL   agent-scope release and acquire fences around the
  *                         arrival and poll; the workloads share data through
- *                         plain accesses */
+ *                         plain accesses
+ *   CCB_VISIBILITY_XCD    what CCB_VISIBILITY_FULL guarantees, with one L2
+ *                         write-back per XCD per barrier (by a leader
+ *                         workgroup, after every member has arrived) instead
+ *                         of one per workgroup; each workgroup still runs
+ *                         its own acquire (see ccb_device.h) */
 enum {
     CCB_BARRIER_STRIPED = 0,
     CCB_BARRIER_FLAT = 1,
     CCB_BARRIER_TREE = 4,
     CCB_VISIBILITY_ORDER = 0,
-    CCB_VISIBILITY_FULL = 2
+    CCB_VISIBILITY_FULL = 2,
+    CCB_VISIBILITY_XCD = 8
 };
 
 /* Group counters of CCB_BARRIER_TREE: the MI355X's XCD count, so that with
@@ -147,6 +153,9 @@ CCB_API ccbStatus ccb_device_info(int32_t* numCUs, int32_t* ldsPerCU, int32_t* w
  *        barrier uses only its first stripe;
  *   line k*CCB_STRIPES: int32 error word at byte 0 (CCB_OK, or
  *        CCB_ERR_DEADLOCK once any member's poll hit its bound).
+ * With CCB_VISIBILITY_XCD a barrier also uses bytes 32..63 of its stripe
+ * lines 1 and 2: the members registered per XCD and each XCD's last
+ * written-back round (8 int32 each).
  * Every stripe must be zero (or a multiple of its participant count) when a
  * launch starts ([SYNCALL] §4.1); ccb_syncall_workspace_reset zeroes the
  * workspace.  A stripe stays valid while the number of arrivals on it since
@@ -176,8 +185,8 @@ CCB_API ccbStatus ccb_device_info(int32_t* numCUs, int32_t* ldsPerCU, int32_t* w
  * default CCB_SOFT_MAX_POLL); a member that exhausts it sets the error word
  * and leaves its round loop, and so does every member that then sees the
  * error word -- no launch traps or hangs.  `mode` picks the barrier variant
- * (CCB_BARRIER_* | CCB_VISIBILITY_*: 0, 1, 2, 3, 4 or 6); any other value is
- * INVALID_VALUE.  Read
+ * (CCB_BARRIER_* | CCB_VISIBILITY_*: 0, 1, 2, 3, 4, 6, 8, 9 or 12); any
+ * other value is INVALID_VALUE.  Read
  * the outcome with ccb_syncall_status after the stream has run the launch.
  * ======================================================================== */
 
@@ -320,7 +329,7 @@ CCB_API ccbStatus ccb_bench_grouped_timeline(int32_t* ws, uint32_t* slots, uint3
  *   ws          device, workspace of 1 barrier (zeroed)
  *   halo        device, haloBytes bytes of scratch (contents ignored), at
  *               least ccb_stencil_halo_bytes(n, threads, nGrid); may be NULL (and
- *               haloBytes 0) with CCB_VISIBILITY_FULL
+ *               haloBytes 0) with CCB_VISIBILITY_FULL or CCB_VISIBILITY_XCD
  *   timeline    device, nGrid * (2 * iters + 1) uint64 wall-clock stamps, or
  *               NULL: for workgroup w, [w*(2*iters+1)] = its start, then for
  *               each iteration t, [.. + 1 + 2t] = the end of its data phase and
@@ -358,8 +367,8 @@ CCB_API size_t ccb_stencil_halo_bytes(int64_t n, int32_t threads, int32_t nGrid)
  * aligned).  Arguments and results are those of ccb_run_stencil otherwise.
  * Limit: with CCB_VISIBILITY_ORDER, 8,448 + ccb_stencil_halo_bytes(n,
  * threads, nGrid) must fit in CCB_NOALLOC_SCRATCH_BYTES (n up to about
- * 2.6e8 elements at 256 threads per workgroup); CCB_VISIBILITY_FULL needs
- * only the workspace part.  Larger launches return CCB_ERR_INVALID_VALUE.
+ * 2.6e8 elements at 256 threads per workgroup); CCB_VISIBILITY_FULL and
+ * CCB_VISIBILITY_XCD need only the workspace part.  Larger launches return CCB_ERR_INVALID_VALUE.
  * Every call on one GPU shares that GPU's scratch: calls that overlap in
  * time on one GPU (on different streams, or from different host threads
  * without ordering) race on it and give wrong results; order them on one

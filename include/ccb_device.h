@@ -60,6 +60,19 @@
  *                  workgroup writes before the barrier and another reads
  *                  after it must go through ccb_store_coherent /
  *                  ccb_load_coherent (device-coherent accesses).
+ *   CCB_VIS_XCD    the guarantee of CCB_VIS_FULL with one L2 write-back per
+ *                  XCD instead of one per workgroup.  Every thread's stores
+ *                  complete before the arrival (so they sit in the L2 of the
+ *                  workgroup's XCD: the vector L1 is write-through), the
+ *                  round completes as under CCB_VIS_ORDER, then one leader
+ *                  workgroup per XCD writes that L2 back and raises the
+ *                  XCD's flag, and every member waits for the flags of all
+ *                  XCDs with members before its agent-scope acquire (the
+ *                  acquire is the only invalidate that reaches a CU's L1,
+ *                  so it stays per workgroup).  Saves N - 8 write-backs per
+ *                  barrier for the price of a second notification.  Needs
+ *                  a ccb_xcd_team per workspace, kept by the caller between
+ *                  barriers, and a workspace zeroed before the launch.
  *
  * Failure.  The poll is bounded ([SYNCALL] §5.2 bounds it at 10^6 polls and
  * asserts).  A GPU trap would kill the context, so instead the member that
@@ -87,7 +100,27 @@
 
 #define CCB_LINE_WORDS (CCB_LINE_BYTES / 4)
 
-enum ccbVisibility { CCB_VIS_FULL = 0, CCB_VIS_ORDER = 1 };
+enum ccbVisibility { CCB_VIS_FULL = 0, CCB_VIS_ORDER = 1, CCB_VIS_XCD = 2 };
+
+/* Words of a barrier's workspace used by CCB_VIS_XCD (reserved bytes of
+ * stripe lines 1 and 2): the members registered on XCD x, and the last
+ * round whose stores XCD x's leader has written back. */
+#define CCB_XCD_COUNT_WORD (1 * CCB_LINE_WORDS + 8)
+#define CCB_XCD_FLAG_WORD (2 * CCB_LINE_WORDS + 8)
+#define CCB_XCDS 8
+
+/* What a member of a CCB_VIS_XCD barrier knows about its XCD.  Zero it
+ * (ccb_xcd_team t = {}) before the first barrier on a workspace and pass the
+ * same object to every later barrier on that workspace: the first barrier
+ * registers the workgroup on its XCD (the first to register is the XCD's
+ * leader) and learns which XCDs have members.  Wave 0 keeps the live copy;
+ * the other waves' copies are not used. */
+struct ccb_xcd_team {
+    int32_t joined;  /* 0 until the first barrier has completed */
+    int32_t leader;  /* this workgroup writes its XCD's L2 back */
+    uint32_t xcc;    /* this workgroup's XCD (the XCC_ID register) */
+    uint32_t xcds;   /* bit x: XCD x has members */
+};
 
 /* Device-coherent accesses for data shared across a CCB_VIS_ORDER barrier. */
 __device__ __forceinline__ void ccb_store_coherent(int32_t* p, int32_t v)
@@ -109,6 +142,17 @@ __device__ __forceinline__ uint32_t ccb_load_coherent(const uint32_t* p)
 
 /* Wait until every memory operation this thread issued has completed. */
 __device__ __forceinline__ void ccb_wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+/* Agent-scope release fence whose L2 write-back has completed before the
+ * next memory access is issued.  LLVM's AMDGPU memory model implements the
+ * fence as `buffer_wbl2 sc1` then `s_waitcnt vmcnt(0)`, but the compiler
+ * drops that wait wherever it tracks no other vector memory access in
+ * flight (it does not count the write-back); the explicit wait keeps it. */
+__device__ __forceinline__ void ccb_fence_release_agent()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    ccb_wait_memory();
+}
 
 /* No work between the arrival and the poll. */
 struct ccb_no_overlap {
@@ -178,12 +222,32 @@ __device__ __forceinline__ int32_t ccb_arrive(int32_t* ctr, int32_t member)
 {
     static_assert((K >= 1 && K <= 64) || (K <= -1 && K >= -32),
                   "stripes are polled by one wave; tree groups sit below the top line");
+    static_assert(kVis != CCB_VIS_XCD, "CCB_VIS_XCD takes a ccb_xcd_team");
     constexpr int kLines = K > 0 ? K : -K;
     // release: the workgroup's earlier global stores become visible at agent
     // scope before the arrival can be observed
-    if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (kVis == CCB_VIS_FULL) ccb_fence_release_agent();
     return __hip_atomic_fetch_add(ctr + (member % kLines) * CCB_LINE_WORDS, 1, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
+}
+
+/* ccb_arrive for any visibility, with the XCD state of CCB_VIS_XCD (ignored
+ * otherwise).  Before its first arrival on the workspace the member
+ * registers on its XCD and waits for that to land, so that a round seen
+ * complete also has every member registered. */
+template <int K, ccbVisibility kVis>
+__device__ __forceinline__ int32_t ccb_arrive(int32_t* ctr, int32_t member, ccb_xcd_team& team)
+{
+    if constexpr (kVis == CCB_VIS_XCD) {
+        if (!team.joined) {
+            team.xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20) & (CCB_XCDS - 1);  // XCC_ID
+            team.leader = __hip_atomic_fetch_add(ctr + CCB_XCD_COUNT_WORD + team.xcc, 1,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            ccb_wait_memory();
+        }
+    }
+    return ccb_arrive<K, kVis == CCB_VIS_FULL ? CCB_VIS_FULL : CCB_VIS_ORDER>(ctr, member);
 }
 
 /* The poll of a two-level tree (K = ccb_tree(G)); see ccb_await. */
@@ -215,7 +279,10 @@ __device__ __forceinline__ int32_t ccb_await_tree(const int32_t* ctr, int32_t n,
         // With full visibility the group's released stores must reach the
         // pollers of the top counter through this member: acquire from the
         // group counter, release to the top.
-        if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+        if (kVis == CCB_VIS_FULL) {
+            ccb_fence_release_agent();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
         if (lane == 0)
             __hip_atomic_fetch_add(top, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -251,6 +318,7 @@ __device__ __forceinline__ int32_t ccb_await(const int32_t* ctr, int32_t n, int3
                                              int32_t before, uint32_t maxPoll, int32_t* err,
                                              Hook hook = Hook())
 {
+    static_assert(kVis != CCB_VIS_XCD, "CCB_VIS_XCD takes a ccb_xcd_team");
     if constexpr (K < 0) {
         return ccb_await_tree<-K, kVis>(ctr, n, member, before, maxPoll, err, hook);
     } else {
@@ -325,6 +393,77 @@ __device__ __forceinline__ int32_t ccb_await(const int32_t* ctr, int32_t n, int3
     }
 }
 
+/* ccb_await for any visibility, with the XCD state of CCB_VIS_XCD (ignored
+ * otherwise).  Under CCB_VIS_XCD, once the round is complete (as under
+ * CCB_VIS_ORDER; hook.released() marks that point): on the first barrier
+ * the XCDs with members are read from the registrations; the XCD's leader
+ * writes its L2 back (agent-scope release fence: every member of the XCD
+ * has arrived, so all their stores are in that L2) and stores the round in
+ * its XCD's flag; every member then polls the flags of the XCDs with
+ * members until each holds the round (bounded by maxPoll like the first
+ * poll, and watching the error word) and ends with the agent-scope acquire
+ * fence. */
+template <int K, ccbVisibility kVis, class Hook = ccb_no_hook>
+__device__ __forceinline__ int32_t ccb_await(const int32_t* ctr, int32_t n, int32_t member,
+                                             int32_t before, uint32_t maxPoll, int32_t* err,
+                                             Hook hook, ccb_xcd_team& team)
+{
+    if constexpr (kVis != CCB_VIS_XCD) {
+        return ccb_await<K, kVis>(ctr, n, member, before, maxPoll, err, hook);
+    } else {
+        int32_t rc = ccb_await<K, CCB_VIS_ORDER>(ctr, n, member, before, maxPoll, err, hook);
+        if (rc != CCB_OK) return rc;
+        const int lane = (int)__lane_id();
+        constexpr int kLines = K > 0 ? K : -K;
+        const int32_t b = __shfl(before, 0, 64);
+        const int32_t s = member % kLines;
+        const int32_t epoch = b / ((n - s + kLines - 1) / kLines) + 1;  // checked by the poll above
+        int32_t* const base = const_cast<int32_t*>(ctr);
+        if (!team.joined) {
+            // every member registered before it arrived and the round is
+            // complete, so every registration is in
+            team.xcc = __shfl(team.xcc, 0, 64);
+            team.leader = __shfl(team.leader, 0, 64);
+            const int32_t c =
+                lane < CCB_XCDS ? __hip_atomic_load(base + CCB_XCD_COUNT_WORD + lane, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT)
+                                : 0;
+            team.xcds = (uint32_t)__ballot(c > 0) & ((1u << CCB_XCDS) - 1);
+            team.joined = 1;
+        }
+        int32_t* const flags = base + CCB_XCD_FLAG_WORD;
+        if (team.leader) {
+            ccb_fence_release_agent();
+            if (lane == 0)
+                __hip_atomic_store(flags + team.xcc, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const bool watch = lane < CCB_XCDS && ((team.xcds >> lane) & 1u) != 0;
+        int32_t* const addr = flags + (watch ? lane : (int)team.xcc);
+        uint32_t polls = 0;
+        for (;;) {
+            const int32_t v = __hip_atomic_load(addr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (__all(!watch || v >= epoch)) break;
+            if (++polls >= maxPoll) {
+                if (lane == 0)
+                    __hip_atomic_store(err, (int32_t)CCB_ERR_DEADLOCK, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                rc = CCB_ERR_DEADLOCK;
+                break;
+            }
+            if ((polls % CCB_ERR_CHECK_EVERY) == 0) {
+                const int32_t e = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (e != CCB_OK) {
+                    rc = e;
+                    break;
+                }
+            }
+            if (CCB_POLL_SLEEP > 0) __builtin_amdgcn_s_sleep(CCB_POLL_SLEEP);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        return rc;
+    }
+}
+
 /* The barrier proper (both phases with the workgroup barriers around them).
  *   ctr      K stripe lines (stripe s: int32 at ctr[s * CCB_LINE_WORDS])
  *   n        participant count (> 0)
@@ -342,24 +481,36 @@ __device__ __forceinline__ int32_t ccb_await(const int32_t* ctr, int32_t n, int3
  * thread). */
 template <int K, ccbVisibility kVis, bool kPreWait = true, class Overlap = ccb_no_overlap>
 __device__ __forceinline__ int32_t ccb_barrier(int32_t* ctr, int32_t n, int32_t member,
-                                               uint32_t maxPoll, int32_t* err,
+                                               uint32_t maxPoll, int32_t* err, ccb_xcd_team& team,
                                                Overlap overlap = Overlap())
 {
     __shared__ int32_t ccb_result;
-    if (kVis == CCB_VIS_ORDER && kPreWait) ccb_wait_memory();  // this thread's accesses are done
+    // this thread's accesses are done (CCB_VIS_XCD: its stores are in the L2)
+    if ((kVis == CCB_VIS_ORDER && kPreWait) || kVis == CCB_VIS_XCD) ccb_wait_memory();
     __syncthreads();
     const uint32_t tid = threadIdx.x + blockDim.x * (threadIdx.y + blockDim.y * threadIdx.z);
     if (tid < 64) {  // wave 0
         int32_t before = 0;
         if (tid == 0) {
-            before = ccb_arrive<K, kVis>(ctr, member);
+            before = ccb_arrive<K, kVis>(ctr, member, team);
             overlap();
         }
-        const int32_t rc = ccb_await<K, kVis>(ctr, n, member, before, maxPoll, err);
+        const int32_t rc = ccb_await<K, kVis>(ctr, n, member, before, maxPoll, err, ccb_no_hook(), team);
         if (tid == 0) ccb_result = rc;
     }
     __syncthreads();
     return ccb_result;
+}
+
+/* The same for CCB_VIS_FULL and CCB_VIS_ORDER, which keep no state. */
+template <int K, ccbVisibility kVis, bool kPreWait = true, class Overlap = ccb_no_overlap>
+__device__ __forceinline__ int32_t ccb_barrier(int32_t* ctr, int32_t n, int32_t member,
+                                               uint32_t maxPoll, int32_t* err,
+                                               Overlap overlap = Overlap())
+{
+    static_assert(kVis != CCB_VIS_XCD, "CCB_VIS_XCD takes a ccb_xcd_team");
+    ccb_xcd_team unused = {};
+    return ccb_barrier<K, kVis, kPreWait, Overlap>(ctr, n, member, maxPoll, err, unused, overlap);
 }
 
 /* Linear index of this workgroup in the grid. */
@@ -427,6 +578,18 @@ __device__ __forceinline__ int32_t ccb_syncall_soft_tree(int32_t* ws, int32_t us
     const int32_t n = usedCores != 0 ? usedCores : (int32_t)(gridDim.x * gridDim.y * gridDim.z);
     return ccb_barrier<ccb_tree(CCB_TREE_GROUPS), CCB_VIS_FULL>(
         ws, n, ccb_block_linear(), CCB_SOFT_MAX_POLL, ws + CCB_STRIPES * CCB_LINE_WORDS);
+}
+
+/* ccb_syncall_soft with one L2 write-back per XCD (CCB_VIS_XCD): the same
+ * visibility as ccb_syncall_soft.  `team` is this workgroup's ccb_xcd_team
+ * for `ws`, zeroed before the first call and passed to every call on `ws`;
+ * the workspace must be zeroed before the launch. */
+__device__ __forceinline__ int32_t ccb_syncall_soft_xcd(int32_t* ws, int32_t usedCores,
+                                                        ccb_xcd_team& team)
+{
+    const int32_t n = usedCores != 0 ? usedCores : (int32_t)(gridDim.x * gridDim.y * gridDim.z);
+    return ccb_barrier<CCB_STRIPES, CCB_VIS_XCD>(ws, n, ccb_block_linear(), CCB_SOFT_MAX_POLL,
+                                                 ws + CCB_STRIPES * CCB_LINE_WORDS, team);
 }
 
 /* The pages' single-counter barrier exactly (one counter line, full

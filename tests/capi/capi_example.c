@@ -72,10 +72,16 @@ __attribute__((visibility("default"))) int ccb_capi_example(char* msg, int msgLe
     CCB_TRY(ccb_run_barrier_only(ws, NULL, NULL, 100, 8, 64, 0, 0, 0,
                                  CCB_BARRIER_TREE | CCB_VISIBILITY_ORDER, consumer));
     CCB_TRY(ccb_syncall_status(ws, 1, &treeArrivals, consumer));
+    /* and with full visibility through one L2 write-back per XCD */
+    int64_t xcdArrivals = 0;
+    CCB_TRY(ccb_syncall_workspace_reset(ws, 1, consumer));
+    CCB_TRY(ccb_run_barrier_only(ws, NULL, NULL, 100, 8, 64, 0, 0, 0,
+                                 CCB_BARRIER_STRIPED | CCB_VISIBILITY_XCD, consumer));
+    CCB_TRY(ccb_syncall_status(ws, 1, &xcdArrivals, consumer));
     HIP_TRY(hipFree(ws));
-    if (treeArrivals != 800) {
-        snprintf(msg, (size_t)msgLen, "tree barrier: %lld arrivals, expected 800",
-                 (long long)treeArrivals);
+    if (treeArrivals != 800 || xcdArrivals != 800) {
+        snprintf(msg, (size_t)msgLen, "tree / per-XCD barrier: %lld / %lld arrivals, expected 800",
+                 (long long)treeArrivals, (long long)xcdArrivals);
         return 1;
     }
 

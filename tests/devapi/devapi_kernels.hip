@@ -2,8 +2,8 @@
 // the way a caller's own kernel would use it: the flag-slot pattern of the
 // SYNCALL guide §6.1 (write own slot, barrier, read every member's slot)
 // over a 2-D grid, with ccb_syncall_soft, ccb_syncall_soft_ordered,
-// ccb_syncall_soft_flat, ccb_syncall_soft_tree, ccb_syncall_soft_bounded or
-// ccb_syncall_soft_mix
+// ccb_syncall_soft_flat, ccb_syncall_soft_tree, ccb_syncall_soft_xcd,
+// ccb_syncall_soft_bounded or ccb_syncall_soft_mix
 // (role groups of one leader and 1 or 2 companions; usedCores then counts
 // groups), or the split-phase pair ccb_arrive / ccb_await with the kernel's
 // own workgroup barriers and work between the two halves.  Test code only: the
@@ -44,6 +44,7 @@ __global__ __launch_bounds__(1024) void devapi_rounds(int32_t* ws, uint32_t* slo
         return;
     }
     int32_t rc = CCB_OK;
+    ccb_xcd_team team = {};  // variant 8: this workgroup's XCD state for ws
     for (int32_t r = 0; r < rounds; ++r) {
         uint32_t* row = slots + (size_t)(r & 1) * nGrid;  // two rows suffice for this order
         if (tid == 0) {
@@ -80,6 +81,7 @@ __global__ __launch_bounds__(1024) void devapi_rounds(int32_t* ws, uint32_t* slo
                 nextWitness != devapi_witness(seed, (uint32_t)(r + 1), (uint32_t)w))
                 rc = CCB_ERR_INVALID_VALUE;  // the overlapped work went wrong
         } else if (kVariant == 7) rc = ccb_syncall_soft_tree(ws, usedCores);
+        else if (kVariant == 8) rc = ccb_syncall_soft_xcd(ws, usedCores, team);
         else rc = ccb_syncall_soft_mix(ws, usedCores, ratio);
         if (rc != CCB_OK) break;
         uint32_t s = 0;
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(1024) void devapi_rounds(int32_t* ws, uint32_t* slo
 
 }  // namespace
 
-// Launches variant 0..7 cooperatively on a gx x gy grid of `threads`
+// Launches variant 0..8 cooperatively on a gx x gy grid of `threads`
 // threads (a multiple of 64, at most 1024).  slots: 2 * gx * gy uint32;
 // out: rounds * gx * gy uint32; status: gx * gy int32.  Returns a hipError_t.
 extern "C" int devapi_run(int variant, int32_t* ws, uint32_t* slots, uint32_t* out, int32_t* status,
@@ -110,18 +112,19 @@ extern "C" int devapi_run(int variant, int32_t* ws, uint32_t* slots, uint32_t* o
     const bool mix = variant == 4 || variant == 5;
     const int32_t members = mix ? ccb_mix_participants(usedCores, variant == 4 ? 1 : 2, gx * gy)
                                 : usedCores;
-    if (variant < 0 || variant > 7 || threads < 64 || threads > 1024 || threads % 64 != 0 ||
+    if (variant < 0 || variant > 8 || threads < 64 || threads > 1024 || threads % 64 != 0 ||
         gx < 1 || gy < 1 || usedCores < 0 || members > gx * gy)
         return (int)hipErrorInvalidValue;
     // every buffer is written by the kernel: never launch with a missing one
     if (ws == nullptr || slots == nullptr || out == nullptr || status == nullptr)
         return (int)hipErrorInvalidValue;
     void* args[] = {&ws, &slots, &out, &status, &seed, &rounds, &usedCores, &maxPoll};
-    const void* const fns[8] = {
+    const void* const fns[9] = {
         reinterpret_cast<const void*>(&devapi_rounds<0>), reinterpret_cast<const void*>(&devapi_rounds<1>),
         reinterpret_cast<const void*>(&devapi_rounds<2>), reinterpret_cast<const void*>(&devapi_rounds<3>),
         reinterpret_cast<const void*>(&devapi_rounds<4>), reinterpret_cast<const void*>(&devapi_rounds<5>),
-        reinterpret_cast<const void*>(&devapi_rounds<6>), reinterpret_cast<const void*>(&devapi_rounds<7>)};
+        reinterpret_cast<const void*>(&devapi_rounds<6>), reinterpret_cast<const void*>(&devapi_rounds<7>),
+        reinterpret_cast<const void*>(&devapi_rounds<8>)};
     const void* fn = fns[variant];
     return (int)hipLaunchCooperativeKernel(fn, dim3(gx, gy), dim3(threads), args, 0, stream);
 }

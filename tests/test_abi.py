@@ -97,11 +97,22 @@ def test_constants_match_pages(ccb):
                  "CCB_CNT_NOTIFY_POOL", "CCB_SOFT_MAX_POLL", "CCB_TREE_GROUPS",
                  "CCB_BREAKDOWN_MAX_ROUNDS"):
         assert defines.get(name) == getattr(ccb, name), name
-    assert len(enums) == 14
+    assert len(enums) == 15
     for name, val in enums.items():
         assert getattr(ccb, name) == val, name
     assert ccb.MODES == {"striped-order": 0, "flat-order": 1, "striped-full": 2, "flat-full": 3,
-                         "tree-order": 4, "tree-full": 6}
+                         "tree-order": 4, "tree-full": 6, "striped-xcd": 8, "flat-xcd": 9,
+                         "tree-xcd": 12}
+    # the per-XCD bookkeeping words of the device header, as the binding has them
+    dev = open(os.path.join(INCLUDE, "ccb_device.h")).read()
+    for name in ("CCB_XCD_COUNT_WORD", "CCB_XCD_FLAG_WORD"):
+        expr = re.search(r"#define %s \((.*)\)" % name, dev).group(1)
+        value = eval(expr.replace("CCB_LINE_WORDS", str(ccb.CCB_LINE_BYTES // 4)), {})
+        assert value == getattr(ccb, name), name
+    # both sit in reserved bytes of stripe lines, clear of word 0 and the tree's top
+    for word in (ccb.CCB_XCD_COUNT_WORD, ccb.CCB_XCD_FLAG_WORD):
+        assert word % 32 >= 1 and word % 32 + 8 <= 32 and word + 8 <= ccb.CCB_STRIPES * 32
+        assert not (word <= ccb.CCB_TREE_TOP_WORD < word + 8)
     assert ccb.ccb_syncall_workspace_bytes(1) == (ccb.CCB_STRIPES + 1) * 128
     assert ccb.ccb_syncall_workspace_bytes(3) == (3 * ccb.CCB_STRIPES + 1) * 128
     # 2^26 elements in chunks of 1024, 1024 workgroups: 64 chunks each
@@ -138,7 +149,11 @@ def test_validation_before_device_work(ccb):
     assert ccb.ccb_run_stencil(4096, 8192, 10, 1, 128, 512, 8, 1, 64) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_run_stencil(4096, 8192, 10, 1, 128, 512, 64, 1, 64,
                                timeline=4100) == ccb.CCB_ERR_INVALID_VALUE  # misaligned stamps
-    assert ccb.ccb_run_barrier_only(128, None, None, 1, 8, 64, mode=9) == ccb.CCB_ERR_INVALID_VALUE
+    # a mode is one layout (0 striped, 1 flat, 4 tree) ORed with one visibility
+    # (0 order, 2 full, 8 per-XCD write-back)
+    for bad in (5, 7, 10, 11, 13, 14, 15, 16, 18, -1):
+        assert ccb.ccb_run_barrier_only(128, None, None, 1, 8, 64, mode=bad) == \
+            ccb.CCB_ERR_INVALID_VALUE, bad
     # int32 stripes: (barriers + 1) * arrivals per stripe and barrier must stay below 2^31
     big = 2**31 // 4  # 256 members: 4 per stripe striped, 256 flat
     assert ccb.ccb_run_barrier_only(128, None, None, big, 256, 64) == ccb.CCB_ERR_INVALID_VALUE

@@ -24,8 +24,18 @@ grouped rounds, stencil; 64 stripes, one counter, and the two-level tree of
     (a non-returning atomic) comes right after an acquire-release sequence
     (`buffer_wbl2 sc1` then `buffer_inv sc1`), so the group's released
     stores reach the top counter's pollers through it;
-and for every kernel in the file: no write through the scalar data cache and
-no packed-FP32 arithmetic.
+  - per-XCD write-back: the registration on the XCD (a returning fetch-add
+    on the count words) is waited for before the first arrival; the XCD
+    flag is stored with an agent-scope store right after a release sequence
+    (the leader's L2 write-back), with no memory access in between; an
+    acquire follows the flag poll; and there is no write-back right before
+    an arrival (that is the per-workgroup placement this mode replaces);
+and for every kernel in the file: every L2 write-back is followed by an
+`s_waitcnt vmcnt(0)` before the next memory access (the compiler drops the
+memory model's wait where it tracks nothing else in flight, so the library
+waits explicitly; HIP's own grid sync, timed beside the barrier, is left as
+HIP compiles it), no write through the scalar data cache and no packed-FP32
+arithmetic.
 """
 
 import os
@@ -48,14 +58,28 @@ def asm(tmp_path_factory):
         return f.read()
 
 
+def _device_header():
+    with open(os.path.join(ROOT, "include", "ccb_device.h")) as f:
+        return f.read()
+
+
 @pytest.fixture(scope="module")
 def vis_codes():
-    """CCB_VIS_FULL / CCB_VIS_ORDER as the device header defines them."""
-    with open(os.path.join(ROOT, "include", "ccb_device.h")) as f:
-        text = f.read()
+    """CCB_VIS_FULL / CCB_VIS_ORDER / CCB_VIS_XCD as the device header defines them."""
+    text = _device_header()
     full = int(re.search(r"CCB_VIS_FULL\s*=\s*(\d+)", text).group(1))
     order = int(re.search(r"CCB_VIS_ORDER\s*=\s*(\d+)", text).group(1))
-    return {full: "full", order: "order"}
+    xcd = int(re.search(r"CCB_VIS_XCD\s*=\s*(\d+)", text).group(1))
+    return {full: "full", order: "order", xcd: "xcd"}
+
+
+def _registration_offset():
+    """Byte offset of the per-XCD count words from the workspace base: the
+    immediate offset of the registration fetch-add."""
+    text = _device_header()
+    line_words = 128 // 4
+    expr = re.search(r"#define CCB_XCD_COUNT_WORD \((.*)\)", text).group(1)
+    return 4 * eval(expr.replace("CCB_LINE_WORDS", str(line_words)), {})
 
 
 def _functions(asm_text):
@@ -90,8 +114,17 @@ def _is_mem(line):
     return _op(line).startswith(MEM_PREFIXES)
 
 
+def _registrations(ins):
+    """Per-XCD write-back: the returning fetch-adds on the XCD count words."""
+    off = f"offset:{_registration_offset()} "
+    return [i for i, l in enumerate(ins)
+            if _op(l) == "global_atomic_add" and " sc0" in l and off in l + " "]
+
+
 def _arrivals(ins):
-    return [i for i, l in enumerate(ins) if _op(l) == "global_atomic_add" and " sc0" in l]
+    reg = set(_registrations(ins))
+    return [i for i, l in enumerate(ins)
+            if _op(l) == "global_atomic_add" and " sc0" in l and i not in reg]
 
 
 def _top_arrivals(ins):
@@ -101,7 +134,7 @@ def _top_arrivals(ins):
 
 def test_every_persistent_kernel_present(asm, vis_codes):
     found = _persistent(asm, vis_codes)
-    want = {(k, s, v) for k in KINDS for s in (1, 64, -8) for v in ("full", "order")}
+    want = {(k, s, v) for k in KINDS for s in (1, 64, -8) for v in ("full", "order", "xcd")}
     assert set(found) == want
     for key, ins in found.items():
         assert _arrivals(ins), f"{key}: no returning fetch-add (the arrival)"
@@ -139,6 +172,77 @@ def _check_acquire(found):
         inv = [i for i, l in enumerate(ins) if l == "buffer_inv sc1"]
         if not polls or not inv or max(inv) < max(polls):
             bad.append(f"{key}: no agent-scope acquire after the poll")
+    return bad
+
+
+def _prev_mem(ins, i):
+    """Index of the last memory access before i (-1: none), and whether an
+    s_waitcnt vmcnt(0) lies between it and i."""
+    waited = False
+    j = i - 1
+    while j >= 0 and not _is_mem(ins[j]):
+        if _op(ins[j]) == "s_waitcnt" and "vmcnt(0)" in ins[j]:
+            waited = True
+        j -= 1
+    return j, waited
+
+
+def _check_xcd(found):
+    """Per-XCD write-back: registration waited for before the arrival; the
+    flag store right after the leader's release; an acquire after the flag
+    poll; no write-back right before an arrival."""
+    bad = []
+    for key, ins in found.items():
+        if key[2] != "xcd":
+            continue
+        regs = _registrations(ins)
+        if not regs:
+            bad.append(f"{key}: no registration on the XCD")
+        for a in _arrivals(ins):
+            j, waited = _prev_mem(ins, a)
+            if j >= 0 and ins[j] == "buffer_wbl2 sc1":
+                bad.append(f"{key}: a write-back right before the arrival")
+            if j in regs and not waited:
+                bad.append(f"{key}: the arrival does not wait for the registration")
+        flag_stores = []
+        for i, l in enumerate(ins):
+            if _op(l) == "buffer_wbl2":
+                k = i + 1
+                waited = False
+                while k < len(ins) and not _is_mem(ins[k]):
+                    if _op(ins[k]) == "s_waitcnt" and "vmcnt(0)" in ins[k]:
+                        waited = True
+                    k += 1
+                if k < len(ins) and _op(ins[k]).startswith("global_store") and " sc1" in ins[k] \
+                        and waited and l == "buffer_wbl2 sc1":
+                    flag_stores.append(k)
+        if not flag_stores:
+            bad.append(f"{key}: no agent-scope flag store right after a release")
+        polls = [i for i, l in enumerate(ins) if _op(l).startswith("global_load") and " sc1" in l]
+        inv = [i for i, l in enumerate(ins) if l == "buffer_inv sc1"]
+        if not polls or not inv or max(inv) < max(polls):
+            bad.append(f"{key}: no agent-scope acquire after the flag poll")
+    return bad
+
+
+def _check_writeback_waits(funcs):
+    """Every buffer_wbl2 is followed by s_waitcnt vmcnt(0) before the next
+    memory access."""
+    bad = []
+    for name, ins in funcs.items():
+        if "hip_grid_sync" in name:
+            continue  # HIP's cooperative-groups grid sync, not library code
+        for k, l in enumerate(ins):
+            if _op(l) != "buffer_wbl2":
+                continue
+            j = k + 1
+            waited = False
+            while j < len(ins) and not _is_mem(ins[j]):
+                if _op(ins[j]) == "s_waitcnt" and "vmcnt(0)" in ins[j]:
+                    waited = True
+                j += 1
+            if not waited:
+                bad.append(f"{name}: {ins[j] if j < len(ins) else None!r} right after a write-back")
     return bad
 
 
@@ -208,6 +312,14 @@ def test_full_visibility_release_before_arrival_acquire_after_poll(asm, vis_code
     assert _check_acquire(found) == []
 
 
+def test_every_writeback_is_waited_for(asm):
+    assert _check_writeback_waits(_functions(asm)) == []
+
+
+def test_xcd_registration_release_flag_acquire(asm, vis_codes):
+    assert _check_xcd(_persistent(asm, vis_codes)) == []
+
+
 def test_tree_full_top_arrival_after_acquire_release(asm, vis_codes):
     assert _check_tree_top(_persistent(asm, vis_codes)) == []
 
@@ -244,14 +356,29 @@ def test_first_poll_waits_for_the_arrivals_reply(asm, vis_codes):
 
 NEGATIVE = {
     "no_release": (
-        [('if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");', "")],
+        [("if (kVis == CCB_VIS_FULL) ccb_fence_release_agent();", "")],
         _check_release),
     "no_acquire": (
         [('if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");', "")],
         _check_acquire),
     "no_tree_acquire_release": (
-        [('if (kVis == CCB_VIS_FULL) __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");', "")],
+        [("if (kVis == CCB_VIS_FULL) {\n            ccb_fence_release_agent();\n"
+          "            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, \"agent\");\n        }", "")],
         _check_tree_top),
+    "writeback_wait_left_to_the_compiler": (
+        [('    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");\n    ccb_wait_memory();\n}',
+          '    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");\n}')],
+        None),
+    "no_xcd_leader_release": (
+        [("if (team.leader) {\n            ccb_fence_release_agent();", "if (team.leader) {")],
+        _check_xcd),
+    "no_xcd_acquire": (
+        [("            if (CCB_POLL_SLEEP > 0) __builtin_amdgcn_s_sleep(CCB_POLL_SLEEP);\n"
+          "        }\n"
+          "        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, \"agent\");",
+          "            if (CCB_POLL_SLEEP > 0) __builtin_amdgcn_s_sleep(CCB_POLL_SLEEP);\n"
+          "        }")],
+        _check_xcd),
     "poll_before_reply": (
         [("const int32_t b = __shfl(before, 0, 64);\n"
           "        __builtin_amdgcn_sched_barrier(0x44F);\n"
@@ -290,7 +417,11 @@ def test_negative_control_is_caught(name, tmp_path, vis_codes):
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     with open(out) as f:
-        found = _persistent(f.read(), vis_codes)
+        text = f.read()
+    if check is None:  # a check over every function
+        assert _check_writeback_waits(_functions(text)) != [], f"{name}: not noticed"
+        return
+    found = _persistent(text, vis_codes)
     assert check(found) != [], f"{name}: {check.__name__} does not notice"
 
 

@@ -36,8 +36,10 @@ def _u32(t):
     return t.cpu().numpy().view(np.uint32)
 
 
-MODES = [0, 1, 2, 3, 4, 6]  # striped / flat / tree x ordering-only / full fences
-MODE_IDS = ["striped-order", "flat-order", "striped-full", "flat-full", "tree-order", "tree-full"]
+# striped / flat / tree x ordering-only / full fences / per-XCD write-back
+MODES = [0, 1, 2, 3, 4, 6, 8, 9, 12]
+MODE_IDS = ["striped-order", "flat-order", "striped-full", "flat-full", "tree-order", "tree-full",
+            "striped-xcd", "flat-xcd", "tree-xcd"]
 _oracle_cache = {}
 
 
@@ -198,6 +200,31 @@ def test_barrier_only_counts_and_placement(wl, mode):
     key = set(zip(p[:, 1].tolist(), se.tolist(), sh.tolist(), cu.tolist()))
     print(f"distinct CUs used by 256 WGs: {len(key)}; XCDs: {sorted(set(p[:, 1].tolist()))}")
     assert len(set(p[:, 1].tolist())) == 8
+
+
+@pytest.mark.parametrize("mode", [8, 9, 12], ids=["striped-xcd", "flat-xcd", "tree-xcd"])
+@pytest.mark.parametrize("n_grid,used", [(256, 0), (5, 0), (64, 40)])
+def test_xcd_registration_and_flags(ccb, wl, n_grid, used, mode):
+    """Per-XCD write-back: every member registered once on the XCD it ran on
+    (the counts match the placement record), and the flag of each XCD with
+    members holds the last round, written by its leader after every round;
+    XCDs without members keep count and flag 0."""
+    rounds = 300
+    members = used or n_grid
+    _say(f"barrier_only xcd bookkeeping {n_grid}x64 used={used} rounds={rounds} mode={mode}")
+    ws = wl.workspace(1)
+    wg = torch.zeros(n_grid, dtype=torch.int32, device="cuda")
+    pl = torch.zeros(2 * n_grid, dtype=torch.int32, device="cuda")
+    assert ccb.ccb_run_barrier_only(ws, pl, wg, rounds, n_grid, 64, used, 0, 0, mode, None) == 0
+    st, ctrs = ccb.ccb_syncall_status(ws, 1, None)
+    assert st == 0 and ctrs == [rounds * members]
+    xcc = (pl.cpu().numpy().view(np.uint32).reshape(-1, 2)[:members, 1] & 7).astype(np.int64)
+    want_counts = np.bincount(xcc, minlength=8)
+    w = ws.cpu().numpy()
+    counts = w[ccb.CCB_XCD_COUNT_WORD:ccb.CCB_XCD_COUNT_WORD + 8]
+    flags = w[ccb.CCB_XCD_FLAG_WORD:ccb.CCB_XCD_FLAG_WORD + 8]
+    np.testing.assert_array_equal(counts, want_counts)
+    np.testing.assert_array_equal(flags, np.where(want_counts > 0, rounds, 0))
 
 
 @pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
@@ -457,7 +484,7 @@ def test_invalid_arguments(ccb, wl):
     assert ccb.ccb_run_barrier_only(ws, None, None, 1, 8, 65) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_run_barrier_only(ws, None, None, 1, 8, 64, 9) == ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_run_barrier_only(ws, None, None, 1, 8, 64, -1) == ccb.CCB_ERR_INVALID_VALUE
-    for bad in (5, 7, 8, -1):
+    for bad in (5, 7, 10, 13, 14, 16, -1):
         assert ccb.ccb_run_barrier_only(ws, None, None, 1, 8, 64, mode=bad) == \
             ccb.CCB_ERR_INVALID_VALUE
     assert ccb.ccb_run_barrier_only(ws.data_ptr() + 4, None, None, 1, 8, 64) == ccb.CCB_ERR_INVALID_VALUE

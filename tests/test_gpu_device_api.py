@@ -19,7 +19,7 @@ torch = pytest.importorskip("torch")
 
 LIB = os.path.join(os.path.dirname(__file__), "devapi", "libccb_devapi.so")
 VARIANTS = {0: "soft", 1: "soft_ordered", 2: "soft_flat", 3: "soft_bounded",
-            6: "split_phase", 7: "soft_tree"}  # 4, 5: mix 1:1, 1:2
+            6: "split_phase", 7: "soft_tree", 8: "soft_xcd"}  # 4, 5: mix 1:1, 1:2
 
 
 def _say(msg):
@@ -110,7 +110,7 @@ def test_device_api_bounded_reports_deadlock(devapi):
 def test_device_api_rejects_bad_launch(devapi):
     """Refused before anything is launched (the launcher also refuses null
     buffers, which every case below passes)."""
-    assert devapi.devapi_run(8, None, None, None, None, 0, 1, 1, 1, 64, 0, 0, None) != 0  # no variant 8
+    assert devapi.devapi_run(9, None, None, None, None, 0, 1, 1, 1, 64, 0, 0, None) != 0  # no variant 9
     assert devapi.devapi_run(6, None, None, None, None, 0, 1, 1, 1, 64, 0, 0, None) != 0  # null buffers
     assert devapi.devapi_run(5, None, None, None, None, 0, 1, 4, 1, 64, 2, 0, None) != 0  # 6 > 4
     assert devapi.devapi_run(0, None, None, None, None, 0, 1, 2, 1, 64, 3, 0, None) != 0
