@@ -32,9 +32,12 @@ def env():
     return ccb, workloads
 
 
-def test_graph_witness_rounds(env):
+@pytest.mark.parametrize("mode", [0, 8], ids=["striped-order", "striped-xcd"])
+def test_graph_witness_rounds(env, mode):
+    """Also with the per-XCD write-back, whose registration and flags live in
+    the workspace: the captured reset clears them before every replay."""
     ccb, wl = env
-    _say("graph: workspace reset + witness rounds 8x64, 100 rounds, 3 replays")
+    _say(f"graph: workspace reset + witness rounds 8x64, 100 rounds, 3 replays, mode={mode}")
     s = torch.cuda.Stream()
     ws = wl.workspace(1)
     slots = torch.zeros(ccb.CCB_SLOT_ROWS * ccb.CCB_SLOT_WORDS * 8, dtype=torch.int32, device="cuda")
@@ -42,7 +45,8 @@ def test_graph_witness_rounds(env):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         ccb.check(ccb.ccb_syncall_workspace_reset(ws, 1, s), "reset")
-        ccb.check(ccb.ccb_run_slot_rounds(ws, slots, out, None, 0, 100, 8, 64, 0, 0, 0, 0, s), "slot_rounds")
+        ccb.check(ccb.ccb_run_slot_rounds(ws, slots, out, None, 0, 100, 8, 64, 0, 0, 0, mode, s),
+                  "slot_rounds")
     want_out, _, want_ctr, rc = oracle.slot_rounds(0, 100, 8, 0)
     assert rc == 0
     for rep in range(3):

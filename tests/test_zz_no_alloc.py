@@ -15,8 +15,10 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-MODES = [0, 1, 2, 3, 4, 6]  # striped / flat / tree x ordering-only / full fences
-MODE_IDS = ["striped-order", "flat-order", "striped-full", "flat-full", "tree-order", "tree-full"]
+# striped / flat / tree x ordering-only / full fences / per-XCD write-back
+MODES = [0, 1, 2, 3, 4, 6, 8, 9, 12]
+MODE_IDS = ["striped-order", "flat-order", "striped-full", "flat-full", "tree-order", "tree-full",
+            "striped-xcd", "flat-xcd", "tree-xcd"]
 
 
 def _say(msg):
