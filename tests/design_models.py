@@ -203,3 +203,126 @@ def _set(t: tuple, i: int, v) -> tuple:
     lst = list(t)
     lst[i] = v
     return tuple(lst)
+
+
+# ---------------------------------------------------------------------------
+# Full visibility with one L2 write-back per XCD.
+#
+# Here the model also has caches, because that is what the protocol is about.
+# A member's WRITE lands in its XCD's L2 (every thread waits for its stores
+# before arriving; the vector L1 is write-through).  Memory changes only
+# when that XCD's leader writes the L2 back: every value the L2 holds for a
+# slot goes to memory.  A READ after the acquire sees the L2 of its own XCD
+# for a member of the same XCD, and memory for a member of another XCD (the
+# acquire invalidates the reader's copies of lines it does not own).
+#
+# Per member round the program is WRITE, ARRIVE, POLL (striped, as above),
+# then on the leader of each barrier's XCD (its first member there) LEAD
+# (write back, then store the round in the XCD's flag), then FPOLL (every
+# flag of an XCD with members of that barrier holds the round), then READ.
+#
+# Variants, each of which a check must catch:
+#   "early_writeback"  the leader writes back and raises its flag right
+#                      after its own arrival, before the round is complete
+#   "no_writeback"     the leader raises its flag without writing back
+#   "no_flag_poll"     members read right after the stripe poll
+#   "own_flag_only"    members wait for their own XCD's flag alone
+# ---------------------------------------------------------------------------
+LEAD, FPOLL = 14, 15
+
+
+def explore_xcd(rounds: Sequence[RoundSpec], n_participants: int, xcd_of: Sequence[int], *,
+                k: int = 1, ring_depth: int = 4, variant: str = "ok",
+                max_states: int = 5_000_000) -> Result:
+    n_bar = 1 + max(spec.counter for spec in rounds)
+    # leader of barrier b on XCD x: its first member there; XCDs with members
+    leaders, xcds = {}, {}
+    for spec in rounds:
+        for p in spec.members:
+            leaders.setdefault((spec.counter, xcd_of[p]), p)
+            xcds.setdefault(spec.counter, set()).add(xcd_of[p])
+    nx = 1 + max(xcd_of)
+    progs = []
+    for p in range(n_participants):
+        steps: List[Tuple[int, int]] = []
+        for r, spec in enumerate(rounds):
+            if p not in spec.members:
+                continue
+            lead = leaders[(spec.counter, xcd_of[p])] == p
+            steps += [(WRITE, r), (ARRIVE, r)]
+            if lead and variant == "early_writeback":
+                steps.append((LEAD, r))
+            steps.append((POLL, r))
+            if lead and variant != "early_writeback":
+                steps.append((LEAD, r))
+            if variant != "no_flag_poll":
+                steps.append((FPOLL, r))
+            steps.append((READ, r))
+        progs.append(steps)
+    n_slots = ring_depth * n_participants
+    res = Result()
+    # state = (pcs, counters, epochs, flags, l2 per XCD, memory)
+    start = ((0,) * n_participants, (0,) * (n_bar * k), (-1,) * n_participants,
+             (0,) * (n_bar * nx), ((-1,) * n_slots,) * nx, (-1,) * n_slots)
+    seen = set()
+    stack = [start]
+    while stack:
+        state = stack.pop()
+        if state in seen:
+            continue
+        seen.add(state)
+        if len(seen) > max_states:
+            raise RuntimeError("state space exceeds max_states")
+        pcs, ctrs, eps, flags, l2, mem = state
+        successors = []
+        all_done = True
+        for p in range(n_participants):
+            pc = pcs[p]
+            if pc >= len(progs[p]):
+                continue
+            all_done = False
+            kind, r = progs[p][pc]
+            spec = rounds[r]
+            b, n, x = spec.counter, spec.n, xcd_of[p]
+            nxt = _set(pcs, p, pc + 1)
+            slot = (r % ring_depth) * n_participants
+            if kind == WRITE:
+                successors.append((nxt, ctrs, eps, flags,
+                                   _set(l2, x, _set(l2[x], slot + p, r)), mem))
+            elif kind == ARRIVE:
+                s = spec.members.index(p) % k
+                ns = (n - s + k - 1) // k
+                before = ctrs[b * k + s]
+                successors.append((nxt, _set(ctrs, b * k + s, before + 1),
+                                   _set(eps, p, before // ns + 1), flags, l2, mem))
+            elif kind == POLL:
+                e = eps[p]
+                if all(ctrs[b * k + l] >= e * ((n - l + k - 1) // k) for l in range(min(n, k))):
+                    successors.append((nxt, ctrs, eps, flags, l2, mem))
+            elif kind == LEAD:
+                m = mem
+                if variant != "no_writeback":
+                    m = tuple(v if v >= 0 else mv for v, mv in zip(l2[x], mem))
+                successors.append((nxt, ctrs, eps, _set(flags, b * nx + x, eps[p]), l2, m))
+            elif kind == FPOLL:
+                watched = [x] if variant == "own_flag_only" else xcds[b]
+                if all(flags[b * nx + y] >= eps[p] for y in watched):
+                    successors.append((nxt, ctrs, eps, flags, l2, mem))
+            else:  # READ
+                for q in spec.members:
+                    got = l2[x][slot + q] if xcd_of[q] == x else mem[slot + q]
+                    if got != r:
+                        res.violations.append((r, p, q, got))
+                successors.append((nxt, ctrs, eps, flags, l2, mem))
+        if all_done:
+            res.final_counters.add(tuple(sum(ctrs[bb * k:(bb + 1) * k]) for bb in range(n_bar)))
+            res.complete_schedules_seen = True
+            continue
+        if not successors:
+            res.deadlock = True
+            if res.deadlock_state is None:
+                res.deadlock_state = state
+            continue
+        stack.extend(successors)
+    res.states = len(seen)
+    return res

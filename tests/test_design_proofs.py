@@ -1,9 +1,10 @@
 """Brute-force proofs of the kernels' barrier designs (CPU).
 
 The kernels split each counter into stripes (or, as the tree variant, into
-group counters under a top counter), and the ordering-only witness kernels
-pipeline their rounds two deep.  None of that is in the pages; each must
-compute exactly what the pages' single-counter barrier computes.  The model
+group counters under a top counter), the ordering-only witness kernels
+pipeline their rounds two deep, and full visibility can be placed as one L2
+write-back per XCD.  None of that is in the pages; each must compute
+exactly what the pages' single-counter barrier computes.  The model
 is tests/design_models.py, built on the oracle's round specifications; the
 first test checks that with one stripe and the plain program it explores
 exactly the oracle's own state space.
@@ -143,3 +144,35 @@ def test_lead_plus_lag_bound():
                 res = dm.explore(en.whole_grid(3, d + 2), 3, write_lead=a, read_lag=b,
                                  ring_depth=d)
                 assert (res.violations == []) == (d >= a + b), (a, b, d)
+
+
+# --- full visibility with one L2 write-back per XCD ----------------------------------
+
+@pytest.mark.parametrize("p,r,xcd_of,k", [(3, 3, (0, 1, 0), 1), (3, 3, (0, 1, 0), 2),
+                                          (4, 2, (0, 1, 0, 1), 2), (3, 2, (0, 0, 0), 1),
+                                          (4, 2, (0, 1, 2, 0), 1)])
+def test_xcd_writeback_whole_grid(p, r, xcd_of, k):
+    """Writes sit in the writer's XCD L2 until its leader writes back; every
+    read after the flag poll still sees every member's write of the round."""
+    res = dm.explore_xcd(en.whole_grid(p, r), p, xcd_of, k=k)
+    assert not res.deadlock and res.violations == []
+    assert res.final_counters == {(r * p,)}
+
+
+def test_xcd_writeback_grouped_and_partial():
+    res = dm.explore_xcd(en.grouped(4, 6), 4, (0, 1, 1, 0), ring_depth=4)
+    assert not res.deadlock and res.violations == [] and res.final_counters == {(4, 4, 8)}
+    res = dm.explore_xcd(en.whole_grid(4, 3, used_cores=3, n_members=3), 4, (0, 1, 1, 0), k=2)
+    assert not res.deadlock and res.violations == [] and res.final_counters == {(9,)}
+
+
+@pytest.mark.parametrize("variant", ["early_writeback", "no_writeback", "no_flag_poll",
+                                     "own_flag_only"])
+def test_xcd_writeback_negative_controls(variant):
+    """Each shortcut lets some read see a stale value."""
+    res = dm.explore_xcd(en.whole_grid(3, 3), 3, (0, 1, 0), variant=variant)
+    assert res.violations != []
+
+
+def test_xcd_writeback_shallow_ring():
+    assert dm.explore_xcd(en.whole_grid(3, 3), 3, (0, 1, 0), ring_depth=1).violations != []
