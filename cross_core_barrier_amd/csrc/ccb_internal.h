@@ -13,6 +13,9 @@ namespace ccb {
 // (non-temporal stores measured 4% slower, in both barrier variants).
 constexpr bool kStencilNT = false;
 constexpr bool kStencilNTLoad = true;
+// Stencil: full chunks are taken kStencilGroup at a time, all of the
+// group's loads issued before its first stores.
+constexpr int kStencilGroup = 2;
 constexpr int kCntUnroll = 1;      // ops per register set in the batch engine's two-set pipeline
 constexpr bool kCntNTLoad = true;   // non-temporal loads of the op stream (read once)
 

@@ -681,30 +681,34 @@ __device__ __forceinline__ void stencil_sweep(const StencilGeom& g, const int32_
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int nWave = blockDim.x / kWave;
     const int64_t fullMine = g.w < g.nFullChunks ? (g.nFullChunks - 1 - g.w) / g.G + 1 : 0;
-    for (int64_t k = 0; k < fullMine; ++k) {
-        const int64_t c = g.w + k * g.G;
-        // Rotate the wave priority chunk by chunk.  With equal priorities
-        // the oldest wave wins every issue arbitration, so of the workgroups
-        // sharing a CU the last-dispatched one finishes each iteration ~9 us
-        // behind the first, and the barrier waits for it.  Rotating makes
-        // the workgroups take turns (w * 4 / G is the dispatch round).
-        set_prio((int)((g.w * 4 / g.G + k) & 3));
-        const int64_t w0 = c * g.chunk + (int64_t)wave * 256;  // this wave's piece
-        const int4 v = load4<ccb::kStencilNTLoad>(x + w0 + 4 * lane);
+    // One full chunk in two halves: its loads, then the rest (so that a
+    // second chunk's loads can go out before this one's stores).
+    struct ChunkIn {
+        int4 v;
         int32_t lh, rh;
-        if (wave == 0) lh = chunk_left<S>(g, x, k, inLeft, halo, pIn);
-        else lh = x[w0 - 1];
-        if (wave == nWave - 1) rh = chunk_right<S>(g, x, k, inRight, halo, pIn);
-        else rh = x[w0 + 256];
-        int32_t left = lane_from_left(v.w);
-        int32_t right = lane_from_right(v.x);
-        if (lane == 0) left = lh;
-        if (lane == kWave - 1) right = rh;
+    };
+    auto load = [&](int64_t k) {
+        const int64_t c = g.w + k * g.G;
+        const int64_t w0 = c * g.chunk + (int64_t)wave * 256;  // this wave's piece
+        ChunkIn in;
+        in.v = load4<ccb::kStencilNTLoad>(x + w0 + 4 * lane);
+        if (wave == 0) in.lh = chunk_left<S>(g, x, k, inLeft, halo, pIn);
+        else in.lh = x[w0 - 1];
+        if (wave == nWave - 1) in.rh = chunk_right<S>(g, x, k, inRight, halo, pIn);
+        else in.rh = x[w0 + 256];
+        return in;
+    };
+    auto finish = [&](int64_t k, const ChunkIn& in) {
+        const int64_t w0 = (g.w + k * g.G) * g.chunk + (int64_t)wave * 256;
+        int32_t left = lane_from_left(in.v.w);
+        int32_t right = lane_from_right(in.v.x);
+        if (lane == 0) left = in.lh;
+        if (lane == kWave - 1) right = in.rh;
         int4 o;
-        o.x = st3(left, v.x, v.y);
-        o.y = st3(v.x, v.y, v.z);
-        o.z = st3(v.y, v.z, v.w);
-        o.w = st3(v.z, v.w, right);
+        o.x = st3(left, in.v.x, in.v.y);
+        o.y = st3(in.v.x, in.v.y, in.v.z);
+        o.z = st3(in.v.y, in.v.z, in.v.w);
+        o.w = st3(in.v.z, in.v.w, right);
         store4<ccb::kStencilNT>(y + w0 + 4 * lane, o);
         if (wave == 0 && lane == 0) {
             if (pubFirst != nullptr) pubFirst[k] = o.x;
@@ -714,6 +718,28 @@ __device__ __forceinline__ void stencil_sweep(const StencilGeom& g, const int32_
             if (pubLast != nullptr) pubLast[k] = o.w;
             if (pubHalo != nullptr) ccb_store_coherent(halo_entry(pubHalo, g, pOut, g.w, k, 1), o.w);
         }
+    };
+    // Rotate the wave priority chunk by chunk.  With equal priorities the
+    // oldest wave wins every issue arbitration, so of the workgroups sharing
+    // a CU the last-dispatched one finishes each iteration ~9 us behind the
+    // first, and the barrier waits for it.  Rotating makes the workgroups
+    // take turns (w * 4 / G is the dispatch round).
+    const int prio0 = (int)(g.w * 4 / g.G);
+    int64_t k = 0;
+    constexpr int kG = ccb::kStencilGroup;
+    if constexpr (kG > 1) {
+        for (; k + kG <= fullMine; k += kG) {
+            set_prio(prio0 + (int)(k / kG));
+            ChunkIn in[kG];
+#pragma unroll
+            for (int i = 0; i < kG; ++i) in[i] = load(k + i);
+#pragma unroll
+            for (int i = 0; i < kG; ++i) finish(k + i, in[i]);
+        }
+    }
+    for (; k < fullMine; ++k) {
+        set_prio(prio0 + (int)k);
+        finish(k, load(k));
     }
     set_prio(0);
     if (fullMine < g.myChunks) {
