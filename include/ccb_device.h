@@ -45,7 +45,8 @@
  *     bound reports DEADLOCK.  Size grids by min(API, 800 / (SGPRs + 16))
  *     waves per SIMD, or keep the kernel at 80 SGPRs or fewer.
  *
- * Visibility -- two strengths:
+ * Visibility -- two strengths; the full one in two placements (CCB_VIS_FULL,
+ * CCB_VIS_XCD):
  *   CCB_VIS_FULL   agent-scope release fence before the arrival and acquire
  *                  fence after the poll: plain global stores made before the
  *                  barrier are visible to plain loads after it on every XCD.
