@@ -90,8 +90,6 @@ inline bool valid_threads(int32_t threads)
     return threads >= 64 && threads <= 1024 && (threads % 64) == 0;
 }
 
-// Dynamic LDS that keeps at most wgsPerCu workgroups on one CU, and the check
-// that nGrid workgroups fit on the device at once (SYNCALL guide §6.3).
 // A mode is one counter layout (striped, flat or tree) ORed with one
 // visibility (order, full or per-XCD write-back).
 inline bool valid_mode(int32_t mode)
@@ -159,6 +157,8 @@ ccbStatus sgpr_waves(int dev, ccb::KernelId id, int32_t mode, int* waves)
     return CCB_OK;
 }
 
+// Dynamic LDS that keeps at most wgsPerCu workgroups on one CU, and the check
+// that nGrid workgroups fit on the device at once (SYNCALL guide §6.3).
 ccbStatus plan_persistent(ccb::KernelId id, int32_t mode, int32_t nGrid, int32_t threads,
                           int32_t wgsPerCu, hipStream_t stream, ccb::LaunchShape* ls)
 {
