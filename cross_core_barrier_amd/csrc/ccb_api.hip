@@ -184,11 +184,16 @@ ccbStatus plan_persistent(ccb::KernelId id, int32_t mode, int32_t nGrid, int32_t
     int perCU = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&perCU, fn, threads, lds) != hipSuccess)
         return hip_failed();
-    // the SGPR limit the occupancy API misses: 4 SIMDs per CU, threads / 64
-    // waves per workgroup spread over them
+    // the SGPR limit the occupancy API misses: `waves` per SIMD, 4 SIMDs per
+    // CU.  Workgroups of up to 4 waves, or a multiple of 4, spread evenly over
+    // the SIMDs.  Other shapes above 4 waves are counted as if each workgroup
+    // put ceil(waves / 4) of its waves on one SIMD: measured at their balanced
+    // counts, 5-wave workgroups at 6 per CU (8 waves per SIMD) and 6-wave
+    // workgroups at 4 per CU (6 per SIMD) did not all become resident.
     int waves = 0;
     if ((st = sgpr_waves(dev, id, mode, &waves)) != CCB_OK) return st;
-    const int bySgpr = 4 * waves / ((threads + 63) / 64);
+    const int wpg = (threads + 63) / 64;
+    const int bySgpr = (wpg <= 4 || wpg % 4 == 0) ? 4 * waves / wpg : waves / ((wpg + 3) / 4);
     if (bySgpr < perCU) perCU = bySgpr;
     if ((long)perCU * info.numCUs < nGrid) return CCB_ERR_NOT_CORESIDENT;
     ls->fn = fn;
