@@ -174,7 +174,10 @@ CCB_API ccbStatus ccb_device_info(int32_t* numCUs, int32_t* ldsPerCU, int32_t* w
  * `threads` threads cannot all be resident at once: the smaller of the
  * occupancy API's count and the count the kernel's SGPRs allow, at 800 SGPRs
  * per SIMD and 16 trap-handler SGPRs per wave beyond the kernel's own
- * allocation (which the API leaves out).  The first persistent launch on a
+ * allocation (which the API leaves out).  Workgroups of 5-7, 9-11 or 13-15
+ * waves are counted as if ceil(waves / 4) of their waves shared one SIMD
+ * (their waves do not spread evenly; 1-4 waves and multiples of 4 do).  The
+ * first persistent launch on a
  * device reads every kernel variant's allocation with one-workgroup query
  * launches on the default stream and waits for them (no allocation, no new
  * stream); make that first call outside stream capture.  After it, every

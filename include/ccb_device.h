@@ -43,7 +43,9 @@
  *     fits 7 waves per SIMD, not the 8 the API reports, and a grid sized by
  *     the API then waits for workgroups that never start until the poll
  *     bound reports DEADLOCK.  Size grids by min(API, 800 / (SGPRs + 16))
- *     waves per SIMD, or keep the kernel at 80 SGPRs or fewer.
+ *     waves per SIMD, or keep the kernel at 80 SGPRs or fewer.  A workgroup
+ *     of 5-7, 9-11 or 13-15 waves does not spread its waves evenly over the
+ *     4 SIMDs: count ceil(waves / 4) of them on one SIMD.
  *
  * Visibility -- two strengths; the full one in two placements (CCB_VIS_FULL,
  * CCB_VIS_XCD):
